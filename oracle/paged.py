@@ -1,0 +1,212 @@
+"""Paged quantized KV cache: byte layout, store and gather (CPU oracle).
+
+TEST INFRASTRUCTURE (see ``oracle/formats.py``).
+
+The pages do not describe paging. The PR #21954 analysis page ("code
+analysis", create_buffers) names separate data buffers (k_buffer, v_buffer)
+and separate block-scale buffers (k_scale_buffer, v_scale_buffer); the layout
+below keeps that split. Paging itself (fixed-size pages reached through a
+per-sequence page table, a slot = page * page_size + offset) is the reading
+adopted for the paged store the workloads name.
+
+Byte layout of one cache (all offsets in bytes; t = token index inside its
+page, t16 = t % 16, tile = t // 16, d = element index, b = d // 16):
+
+  every buffer is [num_pages][num_kv_heads][block], block = page_size * row
+  bytes, made of 16-token tiles laid one after the other.
+
+  GQA, FP8 (E4M3 / E5M2), row = D bytes, tile = 16 * D bytes:
+    K: 256 * (d // 16) + 16 * t16 + d % 16
+    V: 1024 * (d // 64) + 16 * (16 * (t16 // 4) + d % 16)
+       + 4 * ((d // 16) % 4) + t16 % 4
+  GQA, FP4 block-16 (E2M1 codes, 2 per byte, even d in the low nibble),
+  tile = 8 * D code bytes and D scale bytes:
+    K code byte:  256 * (d // 32) + 16 * t16 + (d % 32) // 2
+    V code byte:  1024 * (d // 128) + 16 * (16 * (t16 // 4) + (d % 128) // 8)
+                  + 4 * (t16 % 4) + (d % 8) // 2
+    K scale byte: 32 * (b // 2) + 2 * t16 + b % 2
+    V scale byte: 4 * ((D // 16) * (t16 // 4) + b) + t16 % 4
+  MLA, NVFP4 (one latent row of Dk elements per token, num_kv_heads = 1),
+  token-major: code byte t * Dk/2 + d // 2, E4M3 scale byte t * Dk/16 + b.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import quantize as Q
+from .formats import E2M1, E4M3, E5M2, decode
+
+TILE = 16
+
+
+@dataclass
+class CacheSpec:
+    dtype: str          # "e4m3" | "e5m2" | "mx16" | "nvfp4"
+    kind: str           # "gqa" | "mla"
+    num_kv_heads: int
+    head_dim: int       # GQA D; MLA Dk (latent + rope)
+    v_dim: int          # GQA D; MLA Dv (latent)
+    page_size: int
+    num_pages: int
+
+    def code_row_bytes(self) -> int:
+        return self.head_dim if self.dtype in ("e4m3", "e5m2") else self.head_dim // 2
+
+    def scale_row_bytes(self) -> int:
+        return 0 if self.dtype in ("e4m3", "e5m2") else self.head_dim // 16
+
+    def block_bytes(self) -> tuple[int, int]:
+        return (self.page_size * self.code_row_bytes(), self.page_size * self.scale_row_bytes())
+
+
+# ---------------------------- layout formulas -----------------------------
+def _tile_base(t, row_bytes):
+    return (t // TILE) * TILE * row_bytes
+
+
+def k_code_pos(spec: CacheSpec, t, d):
+    """(byte offset inside the page-head block, nibble) of K element (t, d)."""
+    t = np.asarray(t); d = np.asarray(d)
+    t16 = t % TILE
+    if spec.kind == "mla":
+        return t * (spec.head_dim // 2) + d // 2, d % 2
+    if spec.dtype in ("e4m3", "e5m2"):
+        return _tile_base(t, spec.head_dim) + 256 * (d // 16) + 16 * t16 + d % 16, np.zeros_like(d)
+    base = _tile_base(t, spec.head_dim // 2)
+    return base + 256 * (d // 32) + 16 * t16 + (d % 32) // 2, d % 2
+
+
+def v_code_pos(spec: CacheSpec, t, d):
+    t = np.asarray(t); d = np.asarray(d)
+    t16 = t % TILE
+    if spec.dtype in ("e4m3", "e5m2"):
+        off = (1024 * (d // 64) + 16 * (16 * (t16 // 4) + d % 16)
+               + 4 * ((d // 16) % 4) + t16 % 4)
+        return _tile_base(t, spec.head_dim) + off, np.zeros_like(d)
+    base = _tile_base(t, spec.head_dim // 2)
+    off = (1024 * (d // 128) + 16 * (16 * (t16 // 4) + (d % 128) // 8)
+           + 4 * (t16 % 4) + (d % 8) // 2)
+    return base + off, d % 2
+
+
+def k_scale_pos(spec: CacheSpec, t, b):
+    t = np.asarray(t); b = np.asarray(b)
+    if spec.kind == "mla":
+        return t * (spec.head_dim // 16) + b
+    return _tile_base(t, spec.head_dim // 16) + 32 * (b // 2) + 2 * (t % TILE) + b % 2
+
+
+def v_scale_pos(spec: CacheSpec, t, b):
+    t = np.asarray(t); b = np.asarray(b)
+    t16 = t % TILE
+    nb = spec.head_dim // 16
+    return _tile_base(t, nb) + 4 * (nb * (t16 // 4) + b) + t16 % 4
+
+
+# ------------------------------ cache model -------------------------------
+class OracleCache:
+    """Byte-exact model of the cache buffers: arrays [num_pages, Hkv, block]."""
+
+    def __init__(self, spec: CacheSpec, fill: int = 0):
+        self.spec = spec
+        cb, sb = spec.block_bytes()
+        shape_c = (spec.num_pages, spec.num_kv_heads, cb)
+        shape_s = (spec.num_pages, spec.num_kv_heads, sb)
+        self.k_codes = np.full(shape_c, fill, dtype=np.uint8)
+        self.v_codes = None if spec.kind == "mla" else np.full(shape_c, fill, dtype=np.uint8)
+        self.k_scales = np.full(shape_s, fill, dtype=np.uint8) if sb else None
+        self.v_scales = (np.full(shape_s, fill, dtype=np.uint8)
+                         if sb and spec.kind != "mla" else None)
+
+    # -- writing codes for rows (page[i], head, t[i], all d) --
+    def _put_codes(self, buf, pos_fn, page, head, t, codes):
+        """codes [N, D]; page, t [N]."""
+        d = np.arange(codes.shape[-1])[None, :]
+        byte, nib = pos_fn(self.spec, t[:, None], d)
+        byte = np.broadcast_to(byte, codes.shape)
+        nib = np.broadcast_to(nib, codes.shape)
+        pg = np.broadcast_to(page[:, None], codes.shape)
+        if self.spec.dtype in ("e4m3", "e5m2"):
+            buf[pg, head, byte] = codes
+            return
+        # two 4-bit codes per byte; both nibbles of a byte belong to the same
+        # token in every layout, so each byte is written whole
+        lo, hi = nib == 0, nib == 1
+        assert np.array_equal(byte[lo], byte[hi])
+        buf[pg[lo], head, byte[lo]] = (codes[lo] & 0xF) | ((codes[hi] & 0xF) << 4)
+
+    def _put_scales(self, buf, pos_fn, page, head, t, sc):
+        b = np.arange(sc.shape[-1])[None, :]
+        pos = np.broadcast_to(pos_fn(self.spec, t[:, None], b), sc.shape)
+        buf[np.broadcast_to(page[:, None], sc.shape), head, pos] = sc
+
+    def store(self, k, v, slots, k_scale=None, v_scale=None):
+        """Quantize and store tokens. k, v: float arrays [T, Hkv, D] (GQA) or
+        k [T, Dk] with v None (MLA). slots[i] = page * page_size + offset;
+        a negative slot skips the token. k_scale/v_scale: FP8 per-tensor
+        scales (None = 1.0); for NVFP4, k_scale is the global scale g."""
+        s = self.spec
+        slots = np.asarray(slots, dtype=np.int64)
+        keep = slots >= 0
+        k = np.asarray(k, dtype=np.float64)[keep]
+        if s.kind == "mla":
+            k = k.reshape(k.shape[0], 1, s.head_dim)
+        else:
+            v = np.asarray(v, dtype=np.float64)[keep]
+        page, t = slots[keep] // s.page_size, slots[keep] % s.page_size
+        assert np.all(page < s.num_pages)
+        for h in range(s.num_kv_heads):
+            if s.dtype in ("e4m3", "e5m2"):
+                fmt = E4M3 if s.dtype == "e4m3" else E5M2
+                kc = Q.quantize_fp8(k[:, h], 1.0 if k_scale is None else k_scale, fmt)
+                vc = Q.quantize_fp8(v[:, h], 1.0 if v_scale is None else v_scale, fmt)
+                self._put_codes(self.k_codes, k_code_pos, page, h, t, kc)
+                self._put_codes(self.v_codes, v_code_pos, page, h, t, vc)
+            elif s.dtype == "mx16":
+                kc, ks = Q.quantize_mx16(k[:, h])
+                vc, vs = Q.quantize_mx16(v[:, h])
+                self._put_codes(self.k_codes, k_code_pos, page, h, t, kc)
+                self._put_codes(self.v_codes, v_code_pos, page, h, t, vc)
+                self._put_scales(self.k_scales, k_scale_pos, page, h, t, ks)
+                self._put_scales(self.v_scales, v_scale_pos, page, h, t, vs)
+            elif s.dtype == "nvfp4":
+                kc, ks = Q.quantize_nvfp4(k[:, h], k_scale)
+                self._put_codes(self.k_codes, k_code_pos, page, h, t, kc)
+                self._put_scales(self.k_scales, k_scale_pos, page, h, t, ks)
+            else:
+                raise ValueError(s.dtype)
+
+    # -- reading back dequantized rows --
+    def _get_codes(self, buf, pos_fn, page, head, t, n):
+        d = np.arange(n)[None, :]
+        byte, nib = pos_fn(self.spec, t[:, None], d)
+        raw = buf[page[:, None], head, byte].astype(np.int64)
+        if self.spec.dtype in ("e4m3", "e5m2"):
+            return raw
+        return (raw >> (4 * nib)) & 0xF
+
+    def dequant(self, page, t, head=0, which="k", k_scale=None, v_scale=None):
+        """Dequantized float64 rows [N, dim] for tokens (page[i], t[i])."""
+        s = self.spec
+        page = np.atleast_1d(np.asarray(page, dtype=np.int64))
+        t = np.atleast_1d(np.asarray(t, dtype=np.int64))
+        n = s.head_dim
+        if which == "k":
+            codes = self._get_codes(self.k_codes, k_code_pos, page, head, t, n)
+        else:
+            if s.kind == "mla":
+                return self.dequant(page, t, head, "k", k_scale)[:, : s.v_dim]
+            codes = self._get_codes(self.v_codes, v_code_pos, page, head, t, n)
+        if s.dtype in ("e4m3", "e5m2"):
+            fmt = E4M3 if s.dtype == "e4m3" else E5M2
+            sc = k_scale if which == "k" else v_scale
+            return decode(codes, fmt) * float(np.float32(1.0 if sc is None else sc))
+        b = np.arange(n // 16)[None, :]
+        if s.dtype == "mx16":
+            sbuf, pfn = (self.k_scales, k_scale_pos) if which == "k" else (self.v_scales, v_scale_pos)
+            sc = sbuf[page[:, None], head, pfn(s, t[:, None], b)]
+            return Q.dequantize_mx16(codes, sc)
+        sc = self.k_scales[page[:, None], head, k_scale_pos(s, t[:, None], b)]
+        return Q.dequantize_nvfp4(codes, sc, k_scale)
