@@ -1,0 +1,228 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized paged KV decode hot path on one MI355X.
+
+One step = kvq_store of the new token(s) of every sequence + kvq_decode over
+the whole cache (split-context decode kernel and its combine), on seeded
+synthetic data already resident in HBM. Prints ONE JSON line.
+
+value = algorithmic KV bytes per step (codes + block scales of every cached
+token) / step time. Several copies of the cache are rotated so consecutive
+steps do not hit the 256 MB Infinity Cache.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn effective KV GB/s (% HBM peak), 8B-shape FP8 bs8 ctx20K"
+PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E, vendor figure
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def setup(w, dev, rotate):
+    import torch
+
+    import quantized_paged_kv_store_amd as K
+    from quantized_paged_kv_store_amd import inputs as I
+
+    lens = I.seq_lens(w)
+    table, npages = I.page_table(w, lens)
+    max_len = int(lens.max())
+    pre = np.maximum(lens - w.new_tokens, 0)
+    cache = K.kvq_alloc_pages(w.dtype, w.kind, w.kv_heads, w.head_dim, w.v_dim, w.page_size, npages,
+                              device=dev, fill=0)
+    # prefill, one sequence at a time (bounded host memory); scales first need the
+    # whole prefill, so K (and V) are staged on the device
+    n_pre = int(pre.sum())
+    row = (w.kv_heads, w.head_dim) if w.kind == "gqa" else (w.head_dim,)
+    kd = torch.empty((n_pre, *row), dtype=torch.bfloat16, device=dev)
+    vd = torch.empty((n_pre, *row), dtype=torch.bfloat16, device=dev) if w.kind == "gqa" else None
+    sd = torch.empty(n_pre, dtype=torch.int64, device=dev)
+    off = 0
+    for b in range(w.batch):
+        n = int(pre[b])
+        if n == 0:
+            continue
+        k, v = I.kv_rows(w, b, 0, n)
+        kd[off:off + n] = torch.from_numpy(k).view(torch.bfloat16).reshape(n, *row).to(dev)
+        if vd is not None:
+            vd[off:off + n] = torch.from_numpy(v).view(torch.bfloat16).to(dev)
+        sd[off:off + n] = torch.from_numpy(I.slots_for(table[b], np.arange(n), w.page_size)).to(dev)
+        off += n
+    ks = vs = None
+    if w.dtype in ("e4m3", "e5m2") and w.scale_mode == "amax":
+        ks = K.kvq_compute_scale(cache, kd, vd) if w.dist == "tiny" else K.kvq_compute_scale(cache, kd)
+        vs = ks if w.dist == "tiny" else K.kvq_compute_scale(cache, vd)
+    elif w.dtype == "nvfp4":
+        ks = K.kvq_compute_scale(cache, kd)
+    K.kvq_store(cache, kd, vd, sd, ks, vs)
+    torch.cuda.synchronize(dev)
+    del kd, vd, sd
+    caches = [cache] + [K.Cache(cache.desc, cache.memory.clone()) for _ in range(rotate - 1)]
+    # the new tokens stored by every step
+    kn, vn, sn = [], [], []
+    for b in range(w.batch):
+        k, v = I.kv_rows(w, b, int(pre[b]), int(lens[b]))
+        kn.append(k)
+        if v is not None:
+            vn.append(v)
+        sn.append(I.slots_for(table[b], np.arange(int(pre[b]), int(lens[b])), w.page_size))
+    new_k = torch.from_numpy(np.concatenate(kn)).view(torch.bfloat16).to(dev)
+    new_v = torch.from_numpy(np.concatenate(vn)).view(torch.bfloat16).to(dev) if vn else None
+    new_s = torch.from_numpy(np.concatenate(sn)).to(dev)
+    q = torch.from_numpy(I.queries(w)).view(torch.bfloat16).to(dev)
+    table_d = torch.from_numpy(table).to(dev)
+    lens_d = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    out = torch.empty((w.batch, w.q_heads, w.v_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.batch, w.q_heads), dtype=torch.float32, device=dev)
+    need = K.kvq_decode_workspace_bytes(cache, w.batch, w.q_heads, max_len)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+    return dict(caches=caches, new=(new_k, new_v, new_s), q=q, table=table_d, lens=lens_d, lens_h=lens,
+                max_len=max_len, ks=ks, vs=vs, out=out, lse=lse, ws=ws, sm=I.sm_scale(w),
+                bpt=K.kvq_bytes_per_token(cache.desc))
+
+
+def run_loop(st, steps, do_store, do_decode, offset=0):
+    import quantized_paged_kv_store_amd as K
+    caches = st["caches"]
+    for i in range(steps):
+        c = caches[(i + offset) % len(caches)]
+        if do_store:
+            K.kvq_store(c, *st["new"], st["ks"], st["vs"])
+        if do_decode:
+            K.kvq_decode(c, st["q"], st["table"], st["lens"], st["max_len"], st["sm"], st["ks"], st["vs"],
+                         out=st["out"], lse=st["lse"], workspace=st["ws"])
+
+
+def timed(st, steps, do_store, do_decode):
+    import torch
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    run_loop(st, steps, do_store, do_decode)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps     # ms per iteration
+
+
+def cpu_baseline(w, seconds_hint=20.0):
+    """The float64 oracle, untuned, on a bounded sample of the same workload."""
+    from oracle.attention import decode_attention
+    from oracle.formats import E4M3, E5M2
+    from oracle import quantize as Q
+    from oracle.paged import CacheSpec, OracleCache
+    from quantized_paged_kv_store_amd import inputs as I
+
+    lens = I.seq_lens(w)
+    b = 0
+    L = int(lens[b])
+    P = w.page_size
+    npg = (L + P - 1) // P
+    table = np.full((w.batch, max(1, (w.max_len + P - 1) // P)), -1, np.int32)
+    table[b, :npg] = np.arange(npg)
+    k, v = I.kv_rows(w, b, 0, L)
+    kf = I.bf16_to_f32(k)
+    vf = None if v is None else I.bf16_to_f32(v)
+    ks = vs = None
+    if w.dtype in ("e4m3", "e5m2") and w.scale_mode == "amax":
+        fmt = E4M3 if w.dtype == "e4m3" else E5M2
+        ks, vs = Q.fp8_scale(np.abs(kf).max(), fmt), Q.fp8_scale(np.abs(vf).max(), fmt)
+    elif w.dtype == "nvfp4":
+        ks = Q.nvfp4_global_scale(np.abs(kf).max())
+    oc = OracleCache(CacheSpec(w.dtype, w.kind, w.kv_heads, w.head_dim, w.v_dim, P, npg))
+    t0 = time.perf_counter()
+    oc.store(kf, vf, I.slots_for(table[b], np.arange(L), P), k_scale=ks, v_scale=vs)
+    t_codec = time.perf_counter() - t0
+    q = I.bf16_to_f32(I.queries(w)).astype(np.float64)
+    t0 = time.perf_counter()
+    decode_attention(oc, q, table, lens, I.sm_scale(w), ks, vs, batch_ids=[b])
+    t_dec = time.perf_counter() - t0
+    rows = 2 * w.kv_heads if w.kind == "gqa" else 1
+    bits = 8.0 if w.dtype in ("e4m3", "e5m2") else 4.5
+    nbytes = L * rows * w.head_dim * bits / 8
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    return {"value": round(nbytes / t_dec / 1e9, 4), "unit": "GB/s", "cores": int(blas),
+            "host_cores_available": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"sequence {b} of {w.batch} ({L} tokens, all {w.kv_heads} KV heads): float64 oracle "
+                      f"dequant + attention {t_dec:.2f} s; its quantize-and-store of the same tokens "
+                      f"{t_codec:.2f} s (not in value)",
+            "decode_s": round(t_dec, 3), "codec_s": round(t_codec, 3)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3_8b")
+    ap.add_argument("--rotate", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the decode path shards across (sequence, KV head) with no "
+              f"exchange, so a multi-GPU figure is N independent copies of this one; got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from quantized_paged_kv_store_amd import inputs as I
+
+    w = I.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    st = setup(w, dev, args.rotate)
+    log(f"setup {time.time() - t0:.1f} s")
+    run_loop(st, args.warmup, True, True)
+    torch.cuda.synchronize()
+    ms_step = timed(st, args.steps, True, True)
+    ms_dec = timed(st, args.steps, False, True)
+    ms_store = timed(st, args.steps, True, False)
+    kv_bytes = float(st["lens_h"].astype(np.int64).sum()) * st["bpt"]
+    value = kv_bytes / (ms_step * 1e-3) / 1e9
+    dec_gbps = kv_bytes / (ms_dec * 1e-3) / 1e9
+    log(f"step {ms_step * 1e3:.1f} us, decode {ms_dec * 1e3:.1f} us, store {ms_store * 1e3:.1f} us, "
+        f"{value:.0f} GB/s per step, {dec_gbps:.0f} GB/s decode")
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {w.q_heads} q heads / {w.kv_heads} kv heads, head_dim {w.head_dim}, "
+                        f"batch {w.batch}, context {w.max_len}, page {w.page_size}, {w.dtype} KV "
+                        f"({w.scale_mode} scales); step = store {w.new_tokens} new token(s)/sequence + decode",
+            "global_batch": w.batch, "seq_len": w.max_len, "kv_dtype": w.dtype,
+            "compute": "KV codes dequantized in registers to bf16 (QK) / f16 (PV) MFMA operands, f32 accumulate",
+            "cache_copies_rotated": args.rotate,
+        },
+        "pct_hbm_peak": round(100 * value / PEAK_HBM_GBPS, 2),
+        "decode_only_GBps": round(dec_gbps, 2), "decode_ms": round(ms_dec, 5), "store_ms": round(ms_store, 5),
+        "context_tokens_per_s": round(float(st["lens_h"].sum()) / (ms_step * 1e-3), 1),
+        "decode_tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "kernel": "kvq_decode (decode + combine launches), algorithmic KV bytes / HIP-event time",
+                     "algorithmic_bytes_per_launch": kv_bytes},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

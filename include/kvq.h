@@ -1,0 +1,198 @@
+/*
+ * kvq.h - quantized paged KV cache for decode attention on MI355X (gfx950).
+ *
+ * C ABI of libkvq.so. Every argument is a plain pointer or integer: host
+ * pointers are marked [host], device (HBM) pointers [dev]. The library never
+ * allocates device memory; every device buffer belongs to the caller and
+ * must stay alive until the work queued on `stream` has finished. `stream`
+ * is a hipStream_t passed as void* (NULL = the default stream). All device
+ * work is enqueued asynchronously on that stream; no entry point synchronizes
+ * the host or allocates, so store/decode may be recorded in a HIP graph.
+ *
+ * Errors: every entry point returns KVQ_OK (0) or a negative kvq_status.
+ * Argument errors are detected on the host BEFORE anything is enqueued, so a
+ * failed call has no device side effect. Values that live in device memory
+ * (slot ids, sequence lengths, page ids) are not read by the host; kernels
+ * skip slots outside the cache and treat page ids outside [0, num_pages) as
+ * pages with no tokens, so bad device data gives wrong numbers, never an
+ * out-of-bounds access.
+ *
+ * Sources (the pages this library implements):
+ *  [P1] SGLang "Quantized KV Cache" documentation page: the KV formats
+ *       (FP8 E4M3/E5M2, FP4 E2M1 with 8-bit block exponents over 16
+ *       elements, NVFP4), per-tensor scales defaulting to 1.0, and the
+ *       requirement that dequantization be fused into the attention kernel.
+ *  [P2] "KV cache quantization mechanism and traps": bytes per token and the
+ *       K-channel / V-token outlier structure; scales fixed at prefill are
+ *       reused for appended tokens.
+ *  [P3] vLLM "Quantized KV Cache" page: per-tensor k/v scales, calibration.
+ *  [P4] Analysis of SGLang PR #21954 (NVFP4 KV cache): create_buffers /
+ *       quantize_and_store, separate data and block-scale buffers, the
+ *       two-level FP32 global + E4M3 per-16-block NVFP4 scaling, E2M1_MAX.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* KV code format ([P1] "Supported formats"; [P4] strategy classes). */
+typedef enum kvq_dtype {
+  KVQ_FP8_E4M3 = 1, /* OCP E4M3FN, max 448, one fp32 scale per tensor      */
+  KVQ_FP8_E5M2 = 2, /* OCP E5M2, max 57344, one fp32 scale per tensor      */
+  KVQ_FP4_MX16 = 3, /* E2M1 + one E8M0 (2^(c-127)) scale per 16 elements   */
+  KVQ_NVFP4 = 4     /* E2M1 + one E4M3 scale per 16 elements + fp32 global */
+} kvq_dtype;
+
+typedef enum kvq_kind {
+  KVQ_GQA = 0, /* K and V rows per KV head; G = Hq / Hkv query heads share one */
+  KVQ_MLA = 1  /* one latent row per token shared by every query head;
+                  K = the whole row (head_dim), V = its first v_dim elements   */
+} kvq_kind;
+
+typedef enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_ARG = -1,         /* null pointer, negative size, inconsistent shape */
+  KVQ_ERR_UNSUPPORTED = -2, /* valid but not implemented (dtype x kind x dims) */
+  KVQ_ERR_SIZE = -3,        /* caller buffer (cache memory, workspace) too small */
+  KVQ_ERR_HIP = -4          /* a HIP launch reported an error */
+} kvq_status;
+
+/* Shape of one layer's cache. */
+typedef struct kvq_cache_desc {
+  int32_t dtype;        /* kvq_dtype */
+  int32_t kind;         /* kvq_kind */
+  int32_t num_kv_heads; /* GQA: Hkv >= 1; MLA: must be 1 */
+  int32_t head_dim;     /* GQA: D; MLA: latent + rope dims (Dk) */
+  int32_t v_dim;        /* GQA: must equal head_dim; MLA: latent dims (Dv) */
+  int32_t page_size;    /* tokens per page, a multiple of 16 */
+  int64_t num_pages;    /* physical pages in the pool, >= 1 */
+} kvq_cache_desc;
+
+/* Supported combinations (others return KVQ_ERR_UNSUPPORTED):
+ *   GQA x {E4M3, E5M2}: head_dim in {64, 128}
+ *   GQA x FP4_MX16:     head_dim == 128
+ *   MLA x NVFP4:        head_dim == 576, v_dim == 512
+ *   decode, GQA:        G = Hq / Hkv in [1, 16]
+ *   decode, MLA:        Hq a multiple of 16, at most 128                     */
+
+/* Byte offsets (from the start of the caller's cache memory) and sizes of the
+ * buffers inside one cache. Absent buffers have size 0. Each buffer is
+ * [num_pages][num_kv_heads][page block]; the page block is page_size tokens
+ * in 16-token tiles. Element (t, d) of a page (t16 = t % 16, tile = t / 16,
+ * b = d / 16; offsets inside the block):
+ *   GQA FP8, tile = 16*D bytes, offset tile*16*D +
+ *     K: 256*(d/16) + 16*t16 + d%16
+ *     V: 1024*(d/64) + 16*(16*(t16/4) + d%16) + 4*((d/16)%4) + t16%4
+ *   GQA FP4_MX16 (two E2M1 codes per byte, even d in the low nibble),
+ *   code tile = 8*D bytes, scale tile = D bytes:
+ *     K code:  256*(d/32) + 16*t16 + (d%32)/2
+ *     V code:  1024*(d/128) + 16*(16*(t16/4) + (d%128)/8) + 4*(t16%4) + (d%8)/2
+ *     K scale: 32*(b/2) + 2*t16 + b%2             (E8M0 code)
+ *     V scale: 4*((D/16)*(t16/4) + b) + t16%4     (E8M0 code)
+ *   MLA NVFP4 (token-major): code t*Dk/2 + d/2, scale t*Dk/16 + b (E4M3 code).
+ * The K layouts put the 16 tokens of a tile at consecutive 16-byte lanes and
+ * the V layouts put 4 consecutive tokens of one element in one dword, so each
+ * wave of the decode kernel reads a tile with fully coalesced 16-byte loads
+ * straight into matrix-core operand order.                                 */
+typedef struct kvq_layout {
+  size_t k_codes_offset, k_codes_bytes;
+  size_t v_codes_offset, v_codes_bytes;
+  size_t k_scales_offset, k_scales_bytes;
+  size_t v_scales_offset, v_scales_bytes;
+  size_t scratch_offset, scratch_bytes; /* used by kvq_compute_scale */
+  size_t total_bytes;
+} kvq_layout;
+
+typedef struct kvq_cache kvq_cache; /* opaque host handle */
+
+/* Human-readable text of a kvq_status. Never NULL. */
+const char* kvq_status_string(int status);
+
+/* Storage bytes per cached token of one layer, K+V codes plus per-block
+ * scales ([P2] bytes-per-token formula; [P1] "Memory savings": the FP4
+ * block-scale overhead, 4 + 8/16 bits per element). [host] out. */
+int kvq_bytes_per_token(const kvq_cache_desc* desc, double* bytes_out);
+
+/* create_buffers analogue ([P4]): lay out the data and block-scale buffers of
+ * one cache inside ONE caller-owned device allocation.
+ *   Query:  dev_mem == NULL -> *bytes_needed = size to allocate, *out untouched.
+ *   Bind:   dev_mem != NULL (256-byte aligned), dev_bytes >= bytes_needed ->
+ *           *out = new host handle pointing into dev_mem.
+ * Nothing is written to dev_mem (initial contents are the caller's). The
+ * handle is freed with kvq_free_handle; it does not own dev_mem.
+ * Errors: KVQ_ERR_ARG (null desc/out, bad shape), KVQ_ERR_UNSUPPORTED,
+ * KVQ_ERR_SIZE (dev_bytes too small). */
+int kvq_alloc_pages(const kvq_cache_desc* desc, void* dev_mem, size_t dev_bytes,
+                    size_t* bytes_needed, kvq_cache** out);
+
+/* Offsets of the buffers of a bound cache (see kvq_layout). [host] out. */
+int kvq_cache_layout(const kvq_cache* cache, kvq_layout* out);
+
+/* Frees the host handle only (never the device memory). NULL is ignored. */
+void kvq_free_handle(kvq_cache* cache);
+
+/* Per-tensor scale from the tensor's absolute maximum ([P1] "Scaling
+ * factors"; [P3] calibration: a scale estimated once, then kept fixed):
+ *   FP8 caches:  *scale_out = amax / 448 (E4M3) or amax / 57344 (E5M2)
+ *   NVFP4 cache: *scale_out = amax / (6 * 448)   (the global scale g)
+ *   amax == 0 gives 1.0. amax is taken jointly over x0[0..n0) and
+ *   x1[0..n1) (x1 may be NULL with n1 == 0); division is IEEE binary32.
+ * x0, x1: [dev] BF16. scale_out: [dev] one float. Uses the cache's scratch
+ * buffer: concurrent calls on one cache race.
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED (FP4_MX16 has no tensor scale). */
+int kvq_compute_scale(const kvq_cache* cache, const void* x0, int64_t n0, const void* x1,
+                      int64_t n1, float* scale_out, void* stream);
+
+/* quantize_and_store ([P4]): quantize num_tokens new tokens and write codes
+ * and block scales at their slots.
+ *   k, v: [dev] BF16, GQA [num_tokens][num_kv_heads][head_dim] each;
+ *         MLA: k = latent rows [num_tokens][head_dim], v must be NULL.
+ *   slot_mapping: [dev] int64 [num_tokens], slot = page * page_size + offset;
+ *         a negative slot or one >= num_pages*page_size skips the token.
+ *   k_scale, v_scale: [dev] fp32 scalars. FP8: per-tensor scales, NULL = 1.0
+ *         ([P1]: default when no scale is given); code = RNE_sat(x / scale).
+ *         NVFP4: k_scale = global scale g (required), v_scale unused.
+ *         FP4_MX16: both unused (block exponents are computed here from each
+ *         16-element block's amax: e = floor(log2 amax) - 2).
+ * Inputs must be finite. Two tokens mapped to one slot race.
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_HIP. num_tokens == 0 is a no-op. */
+int kvq_store(const kvq_cache* cache, const void* k, const void* v,
+              const int64_t* slot_mapping, int32_t num_tokens, const float* k_scale,
+              const float* v_scale, void* stream);
+
+/* Bytes of device workspace kvq_decode needs for this batch shape. */
+size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t num_q_heads,
+                                  int32_t max_seq_len);
+
+/* Paged decode attention with dequantization fused into the kernel ([P1]
+ * performance warning: unfused dequantization is very slow) and an online
+ * softmax. For every sequence b and query head h (kv head = h / G):
+ *   out[b][h][:] = sum_t softmax_t(sm_scale * q[b][h] . K^[t]) V^[t]
+ *   lse[b][h]    = log sum_t exp(sm_scale * q[b][h] . K^[t])
+ * over tokens t < seq_lens[b], token t at page page_table[b*stride + t/P],
+ * offset t%P. K^, V^ are the dequantized codes times their scales.
+ *   q:          [dev] BF16 [batch][num_q_heads][head_dim]
+ *   page_table: [dev] int32, row stride page_table_stride (>= ceil(max_seq_len/P))
+ *   seq_lens:   [dev] int32 [batch], each in [0, max_seq_len]
+ *   max_seq_len [host]: upper bound used to size the launch
+ *   k_scale, v_scale: [dev] fp32 (FP8: per-tensor scales, NULL = 1.0;
+ *               NVFP4: k_scale = global scale g, required; MX16: unused)
+ *   out:        [dev] fp32 [batch][num_q_heads][v_dim]
+ *   lse:        [dev] fp32 [batch][num_q_heads] (natural log) or NULL
+ *   workspace:  [dev] >= kvq_decode_workspace_bytes(...), 256-byte aligned
+ * A sequence of length 0 gets out = 0 and lse = -inf.
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_SIZE, KVQ_ERR_HIP. */
+int kvq_decode(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,
+               const int32_t* page_table, int32_t page_table_stride, const int32_t* seq_lens,
+               int32_t max_seq_len, float sm_scale, const float* k_scale, const float* v_scale,
+               float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

@@ -1,0 +1,8 @@
+"""Quantized paged KV store and decode attention for MI355X (gfx950).
+
+The compute path is libkvq.so (HIP kernels behind the C ABI in include/kvq.h);
+``kvq`` is its ctypes binding and ``inputs`` the seeded synthetic input
+generator shared by tests and the benchmark.
+"""
+from .kvq import (Cache, KVQError, kvq_alloc_pages, kvq_bytes_per_token, kvq_compute_scale,  # noqa: F401
+                  kvq_decode, kvq_decode_workspace_bytes, kvq_store, library, make_desc)

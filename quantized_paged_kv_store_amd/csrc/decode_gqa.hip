@@ -1,0 +1,394 @@
+// Paged GQA decode attention over a quantized KV cache, gfx950.
+//
+// The pages require dequantization to happen inside the attention kernel
+// (SGLang "Quantized KV Cache" page, performance warning in the
+// introduction); here it happens in registers, between the 16-byte HBM loads
+// and the matrix-core operands, and nothing dequantized is ever written back.
+//
+// Work split: one workgroup (4 waves) per (sequence b, KV head, split of the
+// context); each wave takes pairs of 16-token tiles round-robin and keeps its
+// own online-softmax state; the 4 waves merge through LDS and write one
+// partial (normalized output + log2-sum-exp) per split, which
+// combine.hip reduces (or the final output directly when there is one split).
+//
+// Per tile pair (32 tokens) a wave runs, with G <= 16 query heads as the MFMA
+// N dimension (columns >= G hold zeros and are never written):
+//   S^T[t][h]   = K^[t][:] . Q^T[:][h]      v_mfma_f32_16x16x32_bf16, 2*D/32 of them
+//                 (K^ = code value; FP8 -> BF16 and E2M1*2^e -> BF16 are exact)
+//   p = 2^(s*log2e*scale - m + 15)          online softmax in fp32, the 2^15
+//                 keeps fp16 P far from its subnormal range
+//   O^T[d][h]  += V^T[d][t] . P^T[t][h]     FP8: fp16 MFMA (E4M3/E5M2 exact in fp16)
+//                                          FP4: bf16 MFMA, P split hi + lo (E2M1*2^e
+//                                          is exact only in bf16)
+// The QK accumulator layout (lane = head column, 4 tokens per lane) is
+// exactly the PV B-operand layout once the 32 tokens of a pair are ordered
+// [tile A: 4g..4g+3, tile B: 4g..4g+3] along K, so scores never leave the lane.
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kPBias = 15.0f;  // p carries a factor 2^15
+
+// raw per-lane bytes of one 16-token tile
+template <int FMT, int D>
+struct Tile {
+  static constexpr int NK = (FMT == KVQ_FP4_MX16) ? 1 : D / 64;  // uint4 loads per lane for K and for V
+  uint4 k[NK];
+  uint4 v[NK];
+  uint32_t ks;  // FP4: K E8M0 codes of blocks (2g, 2g+1) for token lane%16
+  uint32_t vs;  // FP4: V E8M0 codes of tokens 4g..4g+3, block (lane%16)/2
+};
+
+template <int FMT, int D>
+__device__ __forceinline__ void load_tile(Tile<FMT, D>& t, const uint8_t* __restrict__ kb,
+                                          const uint8_t* __restrict__ vb, const uint8_t* __restrict__ ksb,
+                                          const uint8_t* __restrict__ vsb, int lane) {
+#pragma unroll
+  for (int i = 0; i < Tile<FMT, D>::NK; ++i) {
+    t.k[i] = *reinterpret_cast<const uint4*>(kb + 1024 * i + 16 * lane);
+    t.v[i] = *reinterpret_cast<const uint4*>(vb + 1024 * i + 16 * lane);
+  }
+  if (FMT == KVQ_FP4_MX16) {
+    t.ks = *reinterpret_cast<const uint16_t*>(ksb + 2 * lane);
+    t.vs = *reinterpret_cast<const uint32_t*>(vsb + 4 * (8 * (lane >> 4) + ((lane & 15) >> 1)));
+  }
+}
+
+template <int FMT, int D>
+__device__ __forceinline__ void zero_tile(Tile<FMT, D>& t) {
+#pragma unroll
+  for (int i = 0; i < Tile<FMT, D>::NK; ++i) {
+    t.k[i] = make_uint4(0, 0, 0, 0);
+    t.v[i] = make_uint4(0, 0, 0, 0);
+  }
+  t.ks = 0x7f7fu;
+  t.vs = 0x7f7f7f7fu;
+}
+
+// Zero the V codes (and neutralize scales) of this lane's tokens 4g+tt with
+// tt >= nvalid, so that padding bytes (possibly NaN codes) cannot reach the
+// PV product. tokens: nvalid in [0, 4].
+template <int FMT, int D>
+__device__ __forceinline__ void mask_tile_v(Tile<FMT, D>& t, int nvalid) {
+  if (FMT == KVQ_FP4_MX16) {
+    uint32_t w[4] = {t.v[0].x, t.v[0].y, t.v[0].z, t.v[0].w};
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+      if (tt >= nvalid) w[tt] = 0;
+    t.v[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    const uint32_t keep = nvalid >= 4 ? 0xffffffffu : ((1u << (8 * nvalid)) - 1u);
+    t.vs = (t.vs & keep) | (0x7f7f7f7fu & ~keep);
+  } else {
+    const uint32_t keep = nvalid >= 4 ? 0xffffffffu : ((1u << (8 * nvalid)) - 1u);
+#pragma unroll
+    for (int i = 0; i < Tile<FMT, D>::NK; ++i) {
+      t.v[i].x &= keep;
+      t.v[i].y &= keep;
+      t.v[i].z &= keep;
+      t.v[i].w &= keep;
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t u4_get(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+// S^T tile (16 tokens x 16 heads), lane holds tokens 4g..4g+3 of head lane%16.
+template <int FMT, int D>
+__device__ __forceinline__ f32x4 qk_tile(const Tile<FMT, D>& t, const bf16x8* qf) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (FMT == KVQ_FP4_MX16) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t w = u4_get(t.k[0], c);
+      const float sc = e8m0_to_f32((t.ks >> (8 * (c >> 1))) & 0xffu);
+      u32x4 a = {fp4x2_to_bf16x2_scaled<0>(w, sc), fp4x2_to_bf16x2_scaled<1>(w, sc),
+                 fp4x2_to_bf16x2_scaled<2>(w, sc), fp4x2_to_bf16x2_scaled<3>(w, sc)};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qf[c], acc, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      const uint4& kk = t.k[c >> 1];
+      const uint32_t w0 = (c & 1) ? kk.z : kk.x;
+      const uint32_t w1 = (c & 1) ? kk.w : kk.y;
+      u32x4 a = {fp8x2_to_bf16x2<FMT, false>(w0), fp8x2_to_bf16x2<FMT, true>(w0),
+                 fp8x2_to_bf16x2<FMT, false>(w1), fp8x2_to_bf16x2<FMT, true>(w1)};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qf[c], acc, 0, 0, 0);
+    }
+  }
+  return acc;
+}
+
+// O^T += V^T P^T over the 32 tokens of a tile pair.
+template <int FMT, int D>
+__device__ __forceinline__ void pv_pair(const Tile<FMT, D>& ta, const Tile<FMT, D>& tb, const float* p,
+                                        f32x4* o) {
+  if (FMT == KVQ_FP4_MX16) {
+    // P in bf16 as hi + lo (16 significant bits)
+    u32x4 phi, plo;
+    float r[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const __bf16 h = (__bf16)p[i];
+      r[i] = p[i] - (float)h;
+    }
+    phi = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+    plo = u32x4{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]), pack_bf16x2(r[6], r[7])};
+    const bf16x8 bh = __builtin_bit_cast(bf16x8, phi);
+    const bf16x8 bl = __builtin_bit_cast(bf16x8, plo);
+    // X[page][tt][k]: token 4g+tt, elements d = 8c+2k (lo) and 8c+2k+1 (hi)
+    uint32_t xa[4][4], xb[4][4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      const uint32_t wa = u4_get(ta.v[0], tt), wb = u4_get(tb.v[0], tt);
+      const float sa = e8m0_to_f32((ta.vs >> (8 * tt)) & 0xffu);
+      const float sb = e8m0_to_f32((tb.vs >> (8 * tt)) & 0xffu);
+      xa[tt][0] = fp4x2_to_bf16x2_scaled<0>(wa, sa);
+      xa[tt][1] = fp4x2_to_bf16x2_scaled<1>(wa, sa);
+      xa[tt][2] = fp4x2_to_bf16x2_scaled<2>(wa, sa);
+      xa[tt][3] = fp4x2_to_bf16x2_scaled<3>(wa, sa);
+      xb[tt][0] = fp4x2_to_bf16x2_scaled<0>(wb, sb);
+      xb[tt][1] = fp4x2_to_bf16x2_scaled<1>(wb, sb);
+      xb[tt][2] = fp4x2_to_bf16x2_scaled<2>(wb, sb);
+      xb[tt][3] = fp4x2_to_bf16x2_scaled<3>(wb, sb);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      u32x4 lo = {lo_halves(xa[0][k], xa[1][k]), lo_halves(xa[2][k], xa[3][k]), lo_halves(xb[0][k], xb[1][k]),
+                  lo_halves(xb[2][k], xb[3][k])};
+      u32x4 hi = {hi_halves(xa[0][k], xa[1][k]), hi_halves(xa[2][k], xa[3][k]), hi_halves(xb[0][k], xb[1][k]),
+                  hi_halves(xb[2][k], xb[3][k])};
+      const bf16x8 al = __builtin_bit_cast(bf16x8, lo), ah = __builtin_bit_cast(bf16x8, hi);
+      o[2 * k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, o[2 * k], 0, 0, 0);
+      o[2 * k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bl, o[2 * k], 0, 0, 0);
+      o[2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, o[2 * k + 1], 0, 0, 0);
+      o[2 * k + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, o[2 * k + 1], 0, 0, 0);
+    }
+  } else {
+    u32x4 pp = {pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]), pack_f16x2(p[4], p[5]), pack_f16x2(p[6], p[7])};
+    const f16x8 pb = __builtin_bit_cast(f16x8, pp);
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+      const uint32_t wa = u4_get(ta.v[j >> 2], j & 3);
+      const uint32_t wb = u4_get(tb.v[j >> 2], j & 3);
+      u32x4 a = {fp8x2_to_f16x2<FMT, false>(wa), fp8x2_to_f16x2<FMT, true>(wa), fp8x2_to_f16x2<FMT, false>(wb),
+                 fp8x2_to_f16x2<FMT, true>(wb)};
+      o[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), pb, o[j], 0, 0, 0);
+    }
+  }
+}
+
+// element index d of accumulator (tile j, row r) for a lane in group g
+template <int FMT>
+__device__ __forceinline__ int out_dim(int j, int g, int r) {
+  return (FMT == KVQ_FP4_MX16) ? 8 * (4 * g + r) + j : 16 * j + 4 * g + r;
+}
+
+template <int FMT, int D>
+__global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs a) {
+  constexpr int NJ = D / 16;                       // output accumulator tiles
+  constexpr int NC = (FMT == KVQ_FP4_MX16) ? 4 : D / 32;  // QK MFMAs per tile
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, hc = lane & 15;
+  const int L = min(max(a.seq_lens[b], 0), a.max_len);  // device data is clamped, never trusted
+  const int ntiles = (L + kTile - 1) / kTile;
+  const int t_begin = split * a.tiles_per_split;
+  const int t_end = min(t_begin + a.tiles_per_split, ntiles);
+  if (a.num_splits > 1 && t_begin >= t_end) return;  // combine never reads this split
+
+  const int G = a.group;
+  const int tpp = a.page_size / kTile;
+  const int64_t tile_code_bytes = (FMT == KVQ_FP4_MX16) ? 8 * D : 16 * D;
+  const int64_t tile_scale_bytes = (FMT == KVQ_FP4_MX16) ? D : 0;
+  const int64_t head_code = (int64_t)kvh * a.code_block_bytes;
+  const int64_t head_scale = (int64_t)kvh * a.scale_block_bytes;
+  const int64_t page_code = (int64_t)a.hkv * a.code_block_bytes;
+  const int64_t page_scale = (int64_t)a.hkv * a.scale_block_bytes;
+  const int32_t* pt = a.page_table + (int64_t)b * a.page_table_stride;
+
+  const float kscale = a.k_scale ? a.k_scale[0] : 1.0f;
+  const float vscale = a.v_scale ? a.v_scale[0] : 1.0f;
+  const float s_log2 = a.sm_scale_log2 * kscale;
+
+  // Q^T operand fragments for head hc (zero beyond the group)
+  bf16x8 qf[NC];
+  {
+    const bool hv = hc < G;
+    const uint16_t* qrow = a.q + ((int64_t)b * a.hq + (int64_t)kvh * G + (hv ? hc : 0)) * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int d0 = (FMT == KVQ_FP4_MX16) ? 32 * g + 8 * c : 64 * (c >> 1) + 16 * g + 8 * (c & 1);
+      uint4 w = *reinterpret_cast<const uint4*>(qrow + d0);
+      if (!hv) w = make_uint4(0, 0, 0, 0);
+      qf[c] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  f32x4 o[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf, l_run = 0.f;
+
+  const int npairs = (t_end - t_begin + 1) >> 1;
+
+  auto tile_ptrs = [&](int tile, bool& ok, const uint8_t*& kb, const uint8_t*& vb, const uint8_t*& ksb,
+                       const uint8_t*& vsb) {
+    const int page = pt[tile / tpp];
+    const int sub = tile - (tile / tpp) * tpp;
+    ok = (unsigned)page < (unsigned)a.num_pages;
+    const int64_t pg = ok ? page : 0;
+    kb = a.k_codes + pg * page_code + head_code + sub * tile_code_bytes;
+    vb = a.v_codes + pg * page_code + head_code + sub * tile_code_bytes;
+    ksb = a.k_scales + pg * page_scale + head_scale + sub * tile_scale_bytes;
+    vsb = a.v_scales + pg * page_scale + head_scale + sub * tile_scale_bytes;
+  };
+
+  Tile<FMT, D> cur[2], nxt[2];
+  bool okc[2] = {false, false}, okn[2] = {false, false};
+
+  auto load_pair = [&](int pr, Tile<FMT, D>* tl, bool* ok) {
+    const int tA = t_begin + 2 * pr;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int tile = tA + s;
+      const uint8_t *kb, *vb, *ksb, *vsb;
+      bool pok = false;
+      if (tile < t_end) tile_ptrs(tile, pok, kb, vb, ksb, vsb);
+      ok[s] = pok;
+      if (pok)
+        load_tile<FMT, D>(tl[s], kb, vb, ksb, vsb, lane);
+      else
+        zero_tile<FMT, D>(tl[s]);
+    }
+  };
+
+  int pr = wave;
+  if (pr < npairs) load_pair(pr, cur, okc);
+  for (; pr < npairs; pr += kWaves) {
+    const int nx = pr + kWaves;
+    if (nx < npairs) load_pair(nx, nxt, okn);
+
+    const int tA = t_begin + 2 * pr;
+    float s[8];
+    {
+      const f32x4 sa = qk_tile<FMT, D>(cur[0], qf);
+      const f32x4 sb = qk_tile<FMT, D>(cur[1], qf);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        s[i] = sa[i] * s_log2;
+        s[4 + i] = sb[i] * s_log2;
+      }
+    }
+    // tokens of this pair past the sequence end, in a missing second tile or
+    // in a page outside the pool are masked
+    const bool tail = (tA + 2) * kTile > L || !okc[0] || !okc[1];
+    if (tail) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int tok0 = (tA + half) * kTile + 4 * g;
+        const int nvalid = okc[half] ? max(0, min(4, L - tok0)) : 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i >= nvalid) s[4 * half + i] = kNegInf;
+        mask_tile_v<FMT, D>(cur[half], nvalid);
+      }
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
+    mx = fmaxf(mx, shfl_xor_f32(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float mb = (m_new == kNegInf) ? 0.f : m_new - kPBias;
+    const float alpha = (m_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    float p[8], psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = __builtin_amdgcn_exp2f(s[i] - mb);
+      psum += p[i];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) o[j] *= alpha;
+    pv_pair<FMT, D>(cur[0], cur[1], p, o);
+
+    cur[0] = nxt[0];
+    cur[1] = nxt[1];
+    okc[0] = okn[0];
+    okc[1] = okn[1];
+  }
+
+  // ---- merge the 4 waves of this workgroup through LDS ----
+  l_run += shfl_xor_f32(l_run, 16);
+  l_run += shfl_xor_f32(l_run, 32);
+  __shared__ float sm_o[kWaves][16][D + 1];
+  __shared__ float sm_m[kWaves][16], sm_l[kWaves][16];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm_o[wave][hc][out_dim<FMT>(j, g, r)] = o[j][r];
+  if (g == 0) {
+    sm_m[wave][hc] = m_run;
+    sm_l[wave][hc] = l_run;
+  }
+  __syncthreads();
+
+  const bool direct = a.num_splits == 1;
+  for (int idx = tid; idx < G * D; idx += 256) {
+    const int h = idx / D, d = idx - h * D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
+    float osum = 0.f, lsum = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = sm_m[w][h];
+        if (mw != kNegInf) {
+          const float f = __builtin_amdgcn_exp2f(mw - M);
+          osum += f * sm_o[w][h][d];
+          lsum += f * sm_l[w][h];
+        }
+      }
+    }
+    const float ov = lsum > 0.f ? (osum / lsum) * vscale : 0.f;
+    const float lse2 = lsum > 0.f ? M + __log2f(lsum) - kPBias : kNegInf;
+    const int64_t hq = (int64_t)b * a.hq + (int64_t)kvh * G + h;
+    if (direct) {
+      a.out[hq * D + d] = ov;
+      if (d == 0 && a.lse) a.lse[hq] = lse2 * 0.6931471805599453f;
+    } else {
+      a.ws_o[(hq * a.num_splits + split) * D + d] = ov;
+      if (d == 0) a.ws_lse[hq * a.num_splits + split] = lse2;
+    }
+  }
+}
+
+}  // namespace
+}  // namespace kvq
+
+using namespace kvq;
+
+hipError_t kvq_launch_decode_gqa(const kvq_cache* c, const GqaDecodeArgs& a, hipStream_t s) {
+  const dim3 grid(a.num_splits, a.hkv, a.batch);
+  const int dt = c->desc.dtype, D = c->desc.head_dim;
+  if (dt == KVQ_FP8_E4M3 && D == 128)
+    decode_gqa_kernel<KVQ_FP8_E4M3, 128><<<grid, 256, 0, s>>>(a);
+  else if (dt == KVQ_FP8_E4M3 && D == 64)
+    decode_gqa_kernel<KVQ_FP8_E4M3, 64><<<grid, 256, 0, s>>>(a);
+  else if (dt == KVQ_FP8_E5M2 && D == 128)
+    decode_gqa_kernel<KVQ_FP8_E5M2, 128><<<grid, 256, 0, s>>>(a);
+  else if (dt == KVQ_FP8_E5M2 && D == 64)
+    decode_gqa_kernel<KVQ_FP8_E5M2, 64><<<grid, 256, 0, s>>>(a);
+  else if (dt == KVQ_FP4_MX16 && D == 128)
+    decode_gqa_kernel<KVQ_FP4_MX16, 128><<<grid, 256, 0, s>>>(a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}

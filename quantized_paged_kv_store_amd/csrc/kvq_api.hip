@@ -1,0 +1,272 @@
+// C ABI of libkvq: argument validation, cache layout, split planning and
+// kernel launches. Every check happens before anything is enqueued.
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "kvq_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr size_t kScratchBytes = kvq::kAmaxBlocks * sizeof(unsigned);
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool is_fp8(int dt) { return dt == KVQ_FP8_E4M3 || dt == KVQ_FP8_E5M2; }
+
+// KVQ_OK, or the reason this descriptor cannot be used.
+int check_desc(const kvq_cache_desc* d) {
+  if (!d) return KVQ_ERR_ARG;
+  if (d->dtype < KVQ_FP8_E4M3 || d->dtype > KVQ_NVFP4) return KVQ_ERR_ARG;
+  if (d->kind != KVQ_GQA && d->kind != KVQ_MLA) return KVQ_ERR_ARG;
+  if (d->num_kv_heads < 1 || d->head_dim < 16 || d->v_dim < 1 || d->page_size < 1 || d->num_pages < 1)
+    return KVQ_ERR_ARG;
+  if (d->page_size % kvq::kTile) return KVQ_ERR_ARG;
+  if (d->head_dim % 16) return KVQ_ERR_ARG;
+  if (d->kind == KVQ_GQA) {
+    if (d->v_dim != d->head_dim) return KVQ_ERR_ARG;
+    if (is_fp8(d->dtype)) return (d->head_dim == 64 || d->head_dim == 128) ? KVQ_OK : KVQ_ERR_UNSUPPORTED;
+    if (d->dtype == KVQ_FP4_MX16) return d->head_dim == 128 ? KVQ_OK : KVQ_ERR_UNSUPPORTED;
+    return KVQ_ERR_UNSUPPORTED;
+  }
+  if (d->num_kv_heads != 1 || d->v_dim > d->head_dim || d->v_dim % 16) return KVQ_ERR_ARG;
+  if (d->dtype != KVQ_NVFP4) return KVQ_ERR_UNSUPPORTED;
+  return (d->head_dim == 576 && d->v_dim == 512) ? KVQ_OK : KVQ_ERR_UNSUPPORTED;
+}
+
+void compute_layout(const kvq_cache_desc* d, kvq_layout* L, int64_t* code_block, int64_t* scale_block) {
+  const int64_t row_code = is_fp8(d->dtype) ? d->head_dim : d->head_dim / 2;
+  const int64_t row_scale = is_fp8(d->dtype) ? 0 : d->head_dim / 16;
+  *code_block = row_code * d->page_size;
+  *scale_block = row_scale * d->page_size;
+  const size_t per_code = (size_t)d->num_pages * d->num_kv_heads * (size_t)*code_block;
+  const size_t per_scale = (size_t)d->num_pages * d->num_kv_heads * (size_t)*scale_block;
+  const bool has_v = d->kind == KVQ_GQA;
+  memset(L, 0, sizeof(*L));
+  size_t off = 0;
+  L->k_codes_offset = off;
+  L->k_codes_bytes = per_code;
+  off = align_up(off + per_code);
+  L->v_codes_offset = off;
+  L->v_codes_bytes = has_v ? per_code : 0;
+  off = align_up(off + L->v_codes_bytes);
+  L->k_scales_offset = off;
+  L->k_scales_bytes = per_scale;
+  off = align_up(off + per_scale);
+  L->v_scales_offset = off;
+  L->v_scales_bytes = has_v ? per_scale : 0;
+  off = align_up(off + L->v_scales_bytes);
+  L->scratch_offset = off;
+  L->scratch_bytes = kScratchBytes;
+  off = align_up(off + kScratchBytes);
+  L->total_bytes = off;
+}
+
+struct SplitPlan {
+  int tiles_per_split;
+  int num_splits;
+};
+
+// Context split: enough workgroups to fill 256 CUs several times over, each
+// split an even number of 16-token tiles (waves consume tile pairs), at most
+// 128 splits per sequence.
+SplitPlan plan_gqa(int batch, int hkv, int max_len) {
+  const int ntiles = (max_len + kvq::kTile - 1) / kvq::kTile;
+  const int64_t units = (int64_t)batch * hkv;
+  int64_t target = 1536;
+  if (const char* e = getenv("KVQ_DECODE_TARGET_WGS")) {
+    const long v = strtol(e, nullptr, 10);
+    if (v >= 1 && v <= (1 << 20)) target = v;
+  }
+  int64_t tps = units > 0 ? (ntiles * units + target - 1) / target : ntiles;
+  if (tps < 16) tps = 16;  // 2 tile pairs per wave at least
+  tps = (tps + 1) & ~(int64_t)1;
+  int64_t ns = ntiles > 0 ? (ntiles + tps - 1) / tps : 1;
+  if (ns > 128) {
+    ns = 128;
+    tps = (ntiles + ns - 1) / ns;
+    tps = (tps + 1) & ~(int64_t)1;
+    ns = (ntiles + tps - 1) / tps;
+  }
+  if (ns < 1) ns = 1;
+  return {(int)tps, (int)ns};
+}
+
+size_t workspace_for(const SplitPlan& p, int batch, int hq, int dv) {
+  if (p.num_splits <= 1) return 0;
+  const size_t parts = (size_t)batch * hq * p.num_splits;
+  return align_up(parts * dv * sizeof(float)) + align_up(parts * sizeof(float));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_status_string(int status) {
+  switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_ARG: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported format or shape";
+    case KVQ_ERR_SIZE: return "buffer too small";
+    case KVQ_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int kvq_bytes_per_token(const kvq_cache_desc* d, double* bytes_out) {
+  if (!bytes_out) return KVQ_ERR_ARG;
+  const int st = check_desc(d);
+  if (st == KVQ_ERR_ARG) return st;
+  const double bits = is_fp8(d->dtype) ? 8.0 : 4.0 + 8.0 / 16.0;
+  const double rows = d->kind == KVQ_GQA ? 2.0 * d->num_kv_heads : 1.0;
+  *bytes_out = rows * d->head_dim * bits / 8.0;
+  return KVQ_OK;
+}
+
+int kvq_alloc_pages(const kvq_cache_desc* d, void* dev_mem, size_t dev_bytes, size_t* bytes_needed,
+                    kvq_cache** out) {
+  const int st = check_desc(d);
+  if (st != KVQ_OK) return st;
+  kvq_layout L;
+  int64_t cb, sb;
+  compute_layout(d, &L, &cb, &sb);
+  if (bytes_needed) *bytes_needed = L.total_bytes;
+  if (!dev_mem) return bytes_needed ? KVQ_OK : KVQ_ERR_ARG;
+  if (!out) return KVQ_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(dev_mem) % kAlign) return KVQ_ERR_ARG;
+  if (dev_bytes < L.total_bytes) return KVQ_ERR_SIZE;
+  kvq_cache* c = new (std::nothrow) kvq_cache;
+  if (!c) return KVQ_ERR_ARG;
+  c->desc = *d;
+  c->layout = L;
+  c->base = static_cast<uint8_t*>(dev_mem);
+  c->code_block_bytes = cb;
+  c->scale_block_bytes = sb;
+  *out = c;
+  return KVQ_OK;
+}
+
+int kvq_cache_layout(const kvq_cache* c, kvq_layout* out) {
+  if (!c || !out) return KVQ_ERR_ARG;
+  *out = c->layout;
+  return KVQ_OK;
+}
+
+void kvq_free_handle(kvq_cache* c) { delete c; }
+
+int kvq_compute_scale(const kvq_cache* c, const void* x0, int64_t n0, const void* x1, int64_t n1, float* scale_out,
+                      void* stream) {
+  if (!c || !scale_out || n0 < 0 || n1 < 0) return KVQ_ERR_ARG;
+  if ((n0 > 0 && !x0) || (n1 > 0 && !x1)) return KVQ_ERR_ARG;
+  float div;
+  switch (c->desc.dtype) {
+    case KVQ_FP8_E4M3: div = 448.0f; break;
+    case KVQ_FP8_E5M2: div = 57344.0f; break;
+    case KVQ_NVFP4: div = 6.0f * 448.0f; break;
+    default: return KVQ_ERR_UNSUPPORTED;
+  }
+  unsigned* scratch = reinterpret_cast<unsigned*>(c->base + c->layout.scratch_offset);
+  const hipError_t e = kvq_launch_amax(static_cast<const uint16_t*>(x0), n0, static_cast<const uint16_t*>(x1), n1,
+                                       scratch, div, scale_out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+int kvq_store(const kvq_cache* c, const void* k, const void* v, const int64_t* slots, int32_t n, const float* k_scale,
+              const float* v_scale, void* stream) {
+  if (!c || n < 0) return KVQ_ERR_ARG;
+  if (n == 0) return KVQ_OK;
+  if (!k || !slots || !aligned16(k)) return KVQ_ERR_ARG;
+  if (c->desc.kind == KVQ_GQA) {
+    if (!v || !aligned16(v)) return KVQ_ERR_ARG;
+  } else {
+    if (v) return KVQ_ERR_ARG;
+    if (!k_scale) return KVQ_ERR_ARG;  // NVFP4 needs its global scale
+  }
+  const hipError_t e = kvq_launch_store(c, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), slots, n,
+                                        k_scale, v_scale, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_cache* c, int32_t batch, int32_t hq, int32_t max_len) {
+  if (!c || batch < 0 || hq < 1 || max_len < 0) return 0;
+  if (c->desc.kind == KVQ_GQA) return workspace_for(plan_gqa(batch, c->desc.num_kv_heads, max_len), batch, hq, c->desc.v_dim);
+  return 0;
+}
+
+int kvq_decode(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, const int32_t* page_table,
+               int32_t page_table_stride, const int32_t* seq_lens, int32_t max_len, float sm_scale,
+               const float* k_scale, const float* v_scale, float* out, float* lse, void* ws, size_t ws_bytes,
+               void* stream) {
+  if (!c || batch < 0 || hq < 1 || max_len < 0) return KVQ_ERR_ARG;
+  if (batch == 0) return KVQ_OK;
+  if (!q || !page_table || !seq_lens || !out || !aligned16(q)) return KVQ_ERR_ARG;
+  const kvq_cache_desc& d = c->desc;
+  const int P = d.page_size;
+  if (page_table_stride < (max_len + P - 1) / P || page_table_stride < 1) return KVQ_ERR_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (d.kind == KVQ_GQA) {
+    if (hq % d.num_kv_heads) return KVQ_ERR_ARG;
+    const int G = hq / d.num_kv_heads;
+    if (G > 16) return KVQ_ERR_UNSUPPORTED;
+    const SplitPlan plan = plan_gqa(batch, d.num_kv_heads, max_len);
+    const size_t need = workspace_for(plan, batch, hq, d.v_dim);
+    if (need && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % kAlign)) return KVQ_ERR_SIZE;
+    GqaDecodeArgs a;
+    memset(&a, 0, sizeof(a));
+    a.k_codes = c->base + c->layout.k_codes_offset;
+    a.v_codes = c->base + c->layout.v_codes_offset;
+    a.k_scales = c->base + c->layout.k_scales_offset;
+    a.v_scales = c->base + c->layout.v_scales_offset;
+    a.code_block_bytes = c->code_block_bytes;
+    a.scale_block_bytes = c->scale_block_bytes;
+    a.num_pages = d.num_pages;
+    a.q = static_cast<const uint16_t*>(q);
+    a.page_table = page_table;
+    a.page_table_stride = page_table_stride;
+    a.seq_lens = seq_lens;
+    const bool fp8 = is_fp8(d.dtype);
+    a.k_scale = fp8 ? k_scale : nullptr;
+    a.v_scale = fp8 ? v_scale : nullptr;
+    a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+    a.batch = batch;
+    a.hq = hq;
+    a.hkv = d.num_kv_heads;
+    a.group = G;
+    a.page_size = P;
+    a.max_len = max_len;
+    a.tiles_per_split = plan.tiles_per_split;
+    a.num_splits = plan.num_splits;
+    const size_t parts = (size_t)batch * hq * plan.num_splits;
+    a.ws_o = need ? static_cast<float*>(ws) : nullptr;
+    a.ws_lse = need ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align_up(parts * d.v_dim * sizeof(float)))
+                    : nullptr;
+    a.out = out;
+    a.lse = lse;
+    hipError_t e = kvq_launch_decode_gqa(c, a, s);
+    if (e != hipSuccess) return KVQ_ERR_HIP;
+    if (plan.num_splits > 1) {
+      CombineArgs cb;
+      cb.ws_o = a.ws_o;
+      cb.ws_lse = a.ws_lse;
+      cb.seq_lens = seq_lens;
+      cb.out = out;
+      cb.lse = lse;
+      cb.batch = batch;
+      cb.hq = hq;
+      cb.dv = d.v_dim;
+      cb.num_splits = plan.num_splits;
+      cb.tokens_per_split = plan.tiles_per_split * kvq::kTile;
+      cb.max_len = max_len;
+      e = kvq_launch_combine(cb, s);
+      if (e != hipSuccess) return KVQ_ERR_HIP;
+    }
+    return KVQ_OK;
+  }
+  return KVQ_ERR_UNSUPPORTED;  // MLA decode: see decode_mla.hip
+}
+
+}  // extern "C"

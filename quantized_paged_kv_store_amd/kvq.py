@@ -1,0 +1,203 @@
+"""Thin ctypes binding over libkvq.so (include/kvq.h).
+
+Argument marshalling only: torch tensors are used for device memory and the
+current HIP stream; every step of store / decode runs in the library's HIP
+kernels. There is no fallback: if libkvq.so is missing or a call fails, an
+exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, byref, c_char_p, c_double, c_float, c_int32, c_int64, c_size_t, c_void_p
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
+
+DTYPES = {"e4m3": 1, "e5m2": 2, "mx16": 3, "nvfp4": 4}
+KINDS = {"gqa": 0, "mla": 1}
+STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_ARG", -2: "KVQ_ERR_UNSUPPORTED", -3: "KVQ_ERR_SIZE", -4: "KVQ_ERR_HIP"}
+
+
+class KVQError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({_lib().kvq_status_string(status).decode()})")
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("dtype", c_int32), ("kind", c_int32), ("num_kv_heads", c_int32), ("head_dim", c_int32),
+                ("v_dim", c_int32), ("page_size", c_int32), ("num_pages", c_int64)]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [(n, c_size_t) for n in (
+        "k_codes_offset", "k_codes_bytes", "v_codes_offset", "v_codes_bytes",
+        "k_scales_offset", "k_scales_bytes", "v_scales_offset", "v_scales_bytes",
+        "scratch_offset", "scratch_bytes", "total_bytes")]
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built (run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        L.kvq_status_string.argtypes = [c_int32]
+        L.kvq_status_string.restype = c_char_p
+        L.kvq_bytes_per_token.argtypes = [POINTER(CacheDesc), POINTER(c_double)]
+        L.kvq_bytes_per_token.restype = c_int32
+        L.kvq_alloc_pages.argtypes = [POINTER(CacheDesc), c_void_p, c_size_t, POINTER(c_size_t), POINTER(c_void_p)]
+        L.kvq_alloc_pages.restype = c_int32
+        L.kvq_cache_layout.argtypes = [c_void_p, POINTER(Layout)]
+        L.kvq_cache_layout.restype = c_int32
+        L.kvq_free_handle.argtypes = [c_void_p]
+        L.kvq_free_handle.restype = None
+        L.kvq_compute_scale.argtypes = [c_void_p, c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_void_p]
+        L.kvq_compute_scale.restype = c_int32
+        L.kvq_store.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p]
+        L.kvq_store.restype = c_int32
+        L.kvq_decode_workspace_bytes.argtypes = [c_void_p, c_int32, c_int32, c_int32]
+        L.kvq_decode_workspace_bytes.restype = c_size_t
+        L.kvq_decode.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_int32,
+                                 c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.kvq_decode.restype = c_int32
+        _LIB = L
+    return _LIB
+
+
+def library():
+    """The loaded ctypes library (raises if libkvq.so is not built)."""
+    return _lib()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise KVQError(status, what)
+
+
+def _ptr(t):
+    return None if t is None else c_void_p(t.data_ptr())
+
+
+def _stream(device) -> c_void_p:
+    return c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def make_desc(dtype: str, kind: str, num_kv_heads: int, head_dim: int, v_dim: int, page_size: int,
+              num_pages: int) -> CacheDesc:
+    return CacheDesc(DTYPES[dtype], KINDS[kind], num_kv_heads, head_dim, v_dim, page_size, num_pages)
+
+
+def kvq_bytes_per_token(desc: CacheDesc) -> float:
+    out = c_double()
+    _check(_lib().kvq_bytes_per_token(byref(desc), byref(out)), "kvq_bytes_per_token")
+    return out.value
+
+
+class Cache:
+    """One layer's quantized cache bound into a caller-owned uint8 device tensor."""
+
+    def __init__(self, desc: CacheDesc, memory: torch.Tensor):
+        self.desc = desc
+        self.memory = memory
+        h = c_void_p()
+        need = c_size_t()
+        _check(_lib().kvq_alloc_pages(byref(desc), c_void_p(memory.data_ptr()), memory.numel(), byref(need),
+                                      byref(h)), "kvq_alloc_pages")
+        self.handle = h
+        lay = Layout()
+        _check(_lib().kvq_cache_layout(h, byref(lay)), "kvq_cache_layout")
+        self.layout = lay
+
+    def view(self, name: str) -> torch.Tensor:
+        """uint8 view of one buffer: k_codes, v_codes, k_scales, v_scales."""
+        off = getattr(self.layout, name + "_offset")
+        n = getattr(self.layout, name + "_bytes")
+        return self.memory[off:off + n]
+
+    @property
+    def device(self):
+        return self.memory.device
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and _LIB is not None:
+            _LIB.kvq_free_handle(h)
+            self.handle = None
+
+
+def kvq_alloc_pages(dtype: str, kind: str, num_kv_heads: int, head_dim: int, v_dim: int, page_size: int,
+                    num_pages: int, device="cuda", fill: int | None = None) -> Cache:
+    desc = make_desc(dtype, kind, num_kv_heads, head_dim, v_dim, page_size, num_pages)
+    need = c_size_t()
+    _check(_lib().kvq_alloc_pages(byref(desc), None, 0, byref(need), None), "kvq_alloc_pages(query)")
+    mem = torch.empty(need.value, dtype=torch.uint8, device=device)
+    if fill is not None:
+        mem.fill_(fill)
+    return Cache(desc, mem)
+
+
+def _dev_f32(x, device):
+    if x is None:
+        return None
+    if not isinstance(x, torch.Tensor):
+        x = torch.tensor([float(x)], dtype=torch.float32, device=device)
+    assert x.dtype == torch.float32 and x.device == device and x.numel() >= 1
+    return x
+
+
+def kvq_compute_scale(cache: Cache, x0: torch.Tensor, x1: torch.Tensor | None = None,
+                      out: torch.Tensor | None = None) -> torch.Tensor:
+    dev = cache.device
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=dev)
+    for x in (x0, x1):
+        if x is not None:
+            assert x.dtype == torch.bfloat16 and x.is_contiguous() and x.device == dev
+    _check(_lib().kvq_compute_scale(cache.handle, _ptr(x0), x0.numel(), _ptr(x1), 0 if x1 is None else x1.numel(),
+                                    _ptr(out), _stream(dev)), "kvq_compute_scale")
+    return out
+
+
+def kvq_store(cache: Cache, k: torch.Tensor, v: torch.Tensor | None, slot_mapping: torch.Tensor,
+              k_scale=None, v_scale=None) -> None:
+    dev = cache.device
+    assert k.dtype == torch.bfloat16 and k.is_contiguous() and k.device == dev
+    if v is not None:
+        assert v.dtype == torch.bfloat16 and v.is_contiguous() and v.device == dev
+    assert slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous() and slot_mapping.device == dev
+    ks, vs = _dev_f32(k_scale, dev), _dev_f32(v_scale, dev)
+    _check(_lib().kvq_store(cache.handle, _ptr(k), _ptr(v), _ptr(slot_mapping), slot_mapping.numel(), _ptr(ks),
+                            _ptr(vs), _stream(dev)), "kvq_store")
+
+
+def kvq_decode_workspace_bytes(cache: Cache, batch: int, num_q_heads: int, max_seq_len: int) -> int:
+    return int(_lib().kvq_decode_workspace_bytes(cache.handle, batch, num_q_heads, max_seq_len))
+
+
+def kvq_decode(cache: Cache, q: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+               sm_scale: float, k_scale=None, v_scale=None, out=None, lse=None, workspace=None):
+    """Returns (out fp32 [B, Hq, Dv], lse fp32 [B, Hq])."""
+    dev = cache.device
+    B, Hq, _ = q.shape
+    assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.device == dev
+    assert page_table.dtype == torch.int32 and page_table.is_contiguous() and page_table.dim() == 2
+    assert seq_lens.dtype == torch.int32 and seq_lens.numel() == B
+    if out is None:
+        out = torch.empty((B, Hq, cache.desc.v_dim), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    need = kvq_decode_workspace_bytes(cache, B, Hq, max_seq_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ks, vs = _dev_f32(k_scale, dev), _dev_f32(v_scale, dev)
+    _check(_lib().kvq_decode(cache.handle, _ptr(q), B, Hq, _ptr(page_table), page_table.shape[1], _ptr(seq_lens),
+                             max_seq_len, float(sm_scale), _ptr(ks), _ptr(vs), _ptr(out), _ptr(lse),
+                             _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(dev)),
+           "kvq_decode")
+    return out, lse

@@ -1,0 +1,202 @@
+"""Case builder shared by the GPU parity tests (not a test module).
+
+A Case draws one workload's seeded BF16 inputs, runs the HIP path through the
+C ABI (scale calibration, prefill store, append store, decode) and, for a
+chosen subset of sequences, replays the same inputs through the CPU oracle.
+Both sides only share the generated inputs.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+
+import numpy as np
+import torch
+
+import quantized_paged_kv_store_amd as K
+from oracle import quantize as Q
+from oracle.attention import decode_attention, softmax_attention
+from oracle.formats import E4M3, E5M2
+from oracle.paged import CacheSpec, OracleCache
+from quantized_paged_kv_store_amd import inputs as I
+
+# padding bytes of never-written slots: NaN codes for FP8 and E8M0 scales
+FILL = {"e4m3": 0x7F, "e5m2": 0x7F, "mx16": 0xFF, "nvfp4": 0xFF}
+TOL_MAX_ABS = 4e-3
+TOL_REL_L2 = 1e-3
+_THREADS = min(16, os.cpu_count() or 4)
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    n = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / n) if n > 0 else float(np.linalg.norm(a - b))
+
+
+def assert_close(got, want, what=""):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    mab = float(np.max(np.abs(got - want))) if got.size else 0.0
+    r = rel_l2(got, want)
+    assert mab <= TOL_MAX_ABS and r <= TOL_REL_L2, f"{what}: max-abs {mab:.3e} rel-L2 {r:.3e}"
+    return mab, r
+
+
+class Case:
+    def __init__(self, w: I.Workload, device="cuda", identity=False, spare_pages=0, lens=None):
+        self.w = w
+        self.dev = torch.device(device)
+        self.lens = I.seq_lens(w) if lens is None else np.asarray(lens, np.int32)
+        self.table, self.npages = I.page_table(w, self.lens, spare_pages, identity)
+        self.max_len = int(max(int(self.lens.max()), 1))
+        self.prefill = np.maximum(self.lens - w.new_tokens, 0)
+        self._rows = {}
+
+    # ------------------------------------------------------------ inputs --
+    def rows(self, b, t0, t1):
+        return I.kv_rows(self.w, b, t0, t1)
+
+    def _gather(self, ranges):
+        """BF16 rows for [(b, t0, t1)] concatenated (threaded generation)."""
+        if not ranges:
+            return None, None, np.zeros(0, np.int64)
+        with cf.ThreadPoolExecutor(_THREADS) as ex:
+            parts = list(ex.map(lambda r: self.rows(*r), ranges))
+        k = np.concatenate([p[0] for p in parts])
+        v = None if self.w.kind == "mla" else np.concatenate([p[1] for p in parts])
+        slots = np.concatenate([I.slots_for(self.table[b], np.arange(t0, t1), self.w.page_size)
+                                for b, t0, t1 in ranges])
+        return k, v, slots
+
+    def _to_dev(self, a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(self.dev)
+
+    def _bf16(self, a):
+        return self._to_dev(a).view(torch.bfloat16)
+
+    # ------------------------------------------------------------ HIP path --
+    def run_gpu(self, decode=True):
+        w = self.w
+        self.cache = K.kvq_alloc_pages(w.dtype, w.kind, w.kv_heads, w.head_dim, w.v_dim, w.page_size,
+                                       self.npages, device=self.dev, fill=FILL[w.dtype])
+        pre = [(b, 0, int(self.prefill[b])) for b in range(w.batch) if self.prefill[b] > 0]
+        new = [(b, int(self.prefill[b]), int(self.lens[b])) for b in range(w.batch) if self.lens[b] > self.prefill[b]]
+        kp, vp, sp = self._gather(pre)
+        self.k_scale = self.v_scale = None
+        if kp is not None and len(kp):
+            kd, sd = self._bf16(kp), self._to_dev(sp)
+            vd = None if vp is None else self._bf16(vp)
+            if w.dtype in ("e4m3", "e5m2") and w.scale_mode == "amax":
+                if w.dist == "tiny":   # one scale for K and V jointly
+                    self.k_scale = K.kvq_compute_scale(self.cache, kd, vd)
+                    self.v_scale = self.k_scale
+                else:
+                    self.k_scale = K.kvq_compute_scale(self.cache, kd)
+                    self.v_scale = K.kvq_compute_scale(self.cache, vd)
+            elif w.dtype == "nvfp4":
+                self.k_scale = K.kvq_compute_scale(self.cache, kd)
+            K.kvq_store(self.cache, kd, vd, sd, self.k_scale, self.v_scale)
+            del kd, vd, sd
+        elif w.dtype == "nvfp4":
+            self.k_scale = torch.ones(1, dtype=torch.float32, device=self.dev)
+        self.host_amax = None
+        if kp is not None and len(kp):
+            ak = float(np.abs(I.bf16_to_f32(kp)).max())
+            av = None if vp is None else float(np.abs(I.bf16_to_f32(vp)).max())
+            self.host_amax = (ak, av)
+        del kp, vp
+        kn, vn, sn = self._gather(new)
+        self.new_inputs = (kn, vn, sn)
+        if kn is not None and len(kn):
+            self.new_dev = (self._bf16(kn), None if vn is None else self._bf16(vn), self._to_dev(sn))
+            K.kvq_store(self.cache, *self.new_dev, self.k_scale, self.v_scale)
+        self.q = I.queries(w)
+        self.q_dev = self._bf16(self.q)
+        self.table_dev = self._to_dev(self.table)
+        self.lens_dev = self._to_dev(self.lens.astype(np.int32))
+        if decode:
+            self.out, self.lse = K.kvq_decode(self.cache, self.q_dev, self.table_dev, self.lens_dev, self.max_len,
+                                              I.sm_scale(w), self.k_scale, self.v_scale)
+        torch.cuda.synchronize(self.dev)
+        return self
+
+    def gpu_scales(self):
+        f = lambda t: None if t is None else np.float32(t.cpu().numpy()[0])
+        return f(self.k_scale), f(self.v_scale)
+
+    # -------------------------------------------------------------- oracle --
+    def oracle_scales(self):
+        w = self.w
+        if self.host_amax is None:
+            return (np.float32(1.0) if w.dtype == "nvfp4" else None), None
+        ak, av = self.host_amax
+        if w.dtype in ("e4m3", "e5m2") and w.scale_mode == "amax":
+            fmt = E4M3 if w.dtype == "e4m3" else E5M2
+            if w.dist == "tiny":
+                s = Q.fp8_scale(max(ak, av), fmt)
+                return s, s
+            return Q.fp8_scale(ak, fmt), Q.fp8_scale(av, fmt)
+        if w.dtype == "nvfp4":
+            return Q.nvfp4_global_scale(ak), None
+        return None, None
+
+    def oracle(self, batch_ids):
+        """Oracle cache over the pages of `batch_ids` only (compacted ids)."""
+        w = self.w
+        P = w.page_size
+        pages = []
+        for b in batch_ids:
+            n = (int(self.lens[b]) + P - 1) // P
+            pages.extend(int(p) for p in self.table[b, :n])
+        remap = {p: i for i, p in enumerate(pages)}
+        otable = np.full_like(self.table, -1)
+        for b in batch_ids:
+            n = (int(self.lens[b]) + P - 1) // P
+            otable[b, :n] = [remap[int(p)] for p in self.table[b, :n]]
+        spec = CacheSpec(w.dtype, w.kind, w.kv_heads, w.head_dim, w.v_dim, P, max(len(pages), 1))
+        oc = OracleCache(spec, fill=FILL[w.dtype])
+        ks, vs = self.oracle_scales()
+        for b in batch_ids:
+            L = int(self.lens[b])
+            k, v = self.rows(b, 0, L)
+            slots = I.slots_for(otable[b], np.arange(L), P)
+            kf = I.bf16_to_f32(k)
+            vf = None if v is None else I.bf16_to_f32(v)
+            oc.store(kf, vf, slots, k_scale=ks, v_scale=vs)
+        return oc, otable, np.array(pages, np.int64), (ks, vs)
+
+    def oracle_decode(self, batch_ids):
+        oc, otable, pages, (ks, vs) = self.oracle(batch_ids)
+        qf = I.bf16_to_f32(self.q).astype(np.float64)
+        out, lse = decode_attention(oc, qf, otable, self.lens, I.sm_scale(self.w), ks, vs, batch_ids=batch_ids)
+        return out, lse, oc, pages
+
+    def unquantized(self, b):
+        """Attention on the raw BF16 K/V of sequence b (information only)."""
+        w = self.w
+        L = int(self.lens[b])
+        k, v = self.rows(b, 0, L)
+        kf = I.bf16_to_f32(k).astype(np.float64)
+        qf = I.bf16_to_f32(self.q[b]).astype(np.float64)
+        if w.kind == "mla":
+            o, _ = softmax_attention(qf, kf, kf[:, :w.v_dim], I.sm_scale(w))
+            return o
+        vf = I.bf16_to_f32(v).astype(np.float64)
+        G = w.group
+        outs = []
+        for h in range(w.kv_heads):
+            o, _ = softmax_attention(qf[h * G:(h + 1) * G], kf[:, h], vf[:, h], I.sm_scale(w))
+            outs.append(o)
+        return np.concatenate(outs)
+
+    # ----------------------------------------------------- byte compare --
+    def gpu_pages(self, name, pages):
+        """GPU bytes of buffer `name` for physical pages, shaped [n, Hkv, block]."""
+        buf = self.cache.view(name)
+        blk = buf.numel() // (self.npages * self.w.kv_heads)
+        t = buf.view(self.npages, self.w.kv_heads, blk)
+        idx = torch.from_numpy(np.asarray(pages, np.int64)).to(self.dev)
+        return t.index_select(0, idx).cpu().numpy()

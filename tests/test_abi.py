@@ -1,0 +1,169 @@
+"""C-ABI checks that need no GPU: libkvq.so loads, exports every function
+include/kvq.h declares, and every host-side validation path returns its
+status before anything is enqueued (only such paths are exercised here)."""
+import ctypes
+import os
+import re
+from ctypes import byref, c_double, c_size_t, c_void_p
+
+import pytest
+
+import quantized_paged_kv_store_amd as K
+from oracle import accounting as A
+from quantized_paged_kv_store_amd.kvq import CacheDesc, Layout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, ARG, UNSUP, SIZE = 0, -1, -2, -3
+FAKE_DEV = 0x7f0000000000  # never dereferenced by the host code under test
+
+
+def _lib():
+    if not os.path.exists(K.kvq.LIB_PATH):
+        pytest.skip("libkvq.so not built")
+    return K.library()
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(kvq_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_function():
+    lib = _lib()
+    names = _declared()
+    assert set(names) >= {"kvq_alloc_pages", "kvq_store", "kvq_decode", "kvq_compute_scale",
+                          "kvq_bytes_per_token", "kvq_status_string", "kvq_cache_layout",
+                          "kvq_free_handle", "kvq_decode_workspace_bytes"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = _lib()
+    for st in (OK, ARG, UNSUP, SIZE, -4, 12345):
+        assert lib.kvq_status_string(st)
+
+
+def _desc(dtype="e4m3", kind="gqa", hkv=8, d=128, dv=None, p=16, n=64):
+    return K.make_desc(dtype, kind, hkv, d, d if dv is None else dv, p, n)
+
+
+def test_bytes_per_token_matches_accounting():
+    lib = _lib()
+    out = c_double()
+    for dtype in ("e4m3", "e5m2", "mx16"):
+        assert lib.kvq_bytes_per_token(byref(_desc(dtype)), byref(out)) == OK
+        assert out.value == A.kv_bytes_per_token(1, 8, 128, dtype)
+    assert lib.kvq_bytes_per_token(byref(_desc("nvfp4", "mla", 1, 576, 512, 64)), byref(out)) == OK
+    assert out.value == 324.0
+    # 3.56x / 1.78x token capacity of FP4 block-16 vs BF16 / FP8
+    fp8 = K.kvq_bytes_per_token(_desc("e4m3"))
+    fp4 = K.kvq_bytes_per_token(_desc("mx16"))
+    assert round(2 * fp8 / fp4, 2) == 3.56 and round(fp8 / fp4, 2) == 1.78
+
+
+def test_alloc_query_bind_and_layout():
+    lib = _lib()
+    d = _desc("mx16", hkv=4, n=100)
+    need = c_size_t()
+    assert lib.kvq_alloc_pages(byref(d), None, 0, byref(need), None) == OK
+    h = c_void_p()
+    assert lib.kvq_alloc_pages(byref(d), c_void_p(FAKE_DEV), need.value, byref(need), byref(h)) == OK
+    lay = Layout()
+    assert lib.kvq_cache_layout(h, byref(lay)) == OK
+    assert lay.k_codes_bytes == lay.v_codes_bytes == 100 * 4 * 16 * 64
+    assert lay.k_scales_bytes == lay.v_scales_bytes == 100 * 4 * 16 * 8
+    assert lay.scratch_bytes >= 4096 and lay.total_bytes == need.value
+    offs = [lay.k_codes_offset, lay.v_codes_offset, lay.k_scales_offset, lay.v_scales_offset, lay.scratch_offset]
+    assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
+    lib.kvq_free_handle(h)
+    lib.kvq_free_handle(None)
+
+
+@pytest.mark.parametrize("desc,status", [
+    (dict(dtype="e4m3", d=96), UNSUP),
+    (dict(dtype="mx16", d=64), UNSUP),
+    (dict(dtype="nvfp4", kind="gqa"), UNSUP),
+    (dict(dtype="e4m3", kind="mla", hkv=1, d=576, dv=512), UNSUP),
+    (dict(dtype="nvfp4", kind="mla", hkv=2, d=576, dv=512), ARG),
+    (dict(p=8), ARG),
+    (dict(n=0), ARG),
+    (dict(dv=64), ARG),
+    (dict(d=100), ARG),
+])
+def test_alloc_rejects_bad_descriptors(desc, status):
+    lib = _lib()
+    need = c_size_t()
+    assert lib.kvq_alloc_pages(byref(_desc(**desc)), None, 0, byref(need), None) == status
+
+
+def test_alloc_size_and_alignment_errors():
+    lib = _lib()
+    d = _desc()
+    need = c_size_t()
+    h = c_void_p()
+    assert lib.kvq_alloc_pages(byref(d), None, 0, byref(need), None) == OK
+    assert lib.kvq_alloc_pages(byref(d), c_void_p(FAKE_DEV), need.value - 1, byref(need), byref(h)) == SIZE
+    assert lib.kvq_alloc_pages(byref(d), c_void_p(FAKE_DEV + 16), need.value, byref(need), byref(h)) == ARG
+    assert lib.kvq_alloc_pages(byref(d), c_void_p(FAKE_DEV), need.value, byref(need), None) == ARG
+    assert lib.kvq_alloc_pages(None, None, 0, byref(need), None) == ARG
+
+
+@pytest.fixture
+def handles():
+    lib = _lib()
+    out = {}
+    for name, d in (("fp8", _desc("e4m3", hkv=2)), ("mx", _desc("mx16", hkv=2)),
+                    ("mla", _desc("nvfp4", "mla", 1, 576, 512, 64))):
+        need = c_size_t()
+        h = c_void_p()
+        assert lib.kvq_alloc_pages(byref(d), None, 0, byref(need), None) == OK
+        assert lib.kvq_alloc_pages(byref(d), c_void_p(FAKE_DEV), need.value, byref(need), byref(h)) == OK
+        out[name] = h
+    yield lib, out
+    for h in out.values():
+        lib.kvq_free_handle(h)
+
+
+def test_store_argument_errors(handles):
+    lib, h = handles
+    P = c_void_p(FAKE_DEV)
+    assert lib.kvq_store(h["fp8"], P, P, P, 0, None, None, None) == OK          # no-op
+    assert lib.kvq_store(h["fp8"], None, P, P, 4, None, None, None) == ARG
+    assert lib.kvq_store(h["fp8"], P, None, P, 4, None, None, None) == ARG
+    assert lib.kvq_store(h["fp8"], P, P, None, 4, None, None, None) == ARG
+    assert lib.kvq_store(h["fp8"], c_void_p(FAKE_DEV + 2), P, P, 4, None, None, None) == ARG
+    assert lib.kvq_store(h["fp8"], P, P, P, -1, None, None, None) == ARG
+    assert lib.kvq_store(h["mla"], P, P, P, 4, P, None, None) == ARG            # MLA has no V input
+    assert lib.kvq_store(h["mla"], P, None, P, 4, None, None, None) == ARG      # NVFP4 needs g
+    assert lib.kvq_store(None, P, P, P, 4, None, None, None) == ARG
+
+
+def test_compute_scale_argument_errors(handles):
+    lib, h = handles
+    P = c_void_p(FAKE_DEV)
+    assert lib.kvq_compute_scale(h["mx"], P, 10, None, 0, P, None) == UNSUP
+    assert lib.kvq_compute_scale(h["fp8"], None, 10, None, 0, P, None) == ARG
+    assert lib.kvq_compute_scale(h["fp8"], P, 10, None, 5, P, None) == ARG
+    assert lib.kvq_compute_scale(h["fp8"], P, 10, None, 0, None, None) == ARG
+    assert lib.kvq_compute_scale(h["fp8"], P, -1, None, 0, P, None) == ARG
+
+
+def test_decode_argument_errors(handles):
+    lib, h = handles
+    P = c_void_p(FAKE_DEV)
+    args = lambda hq, stride, max_len, ws, wsb, batch=4: (
+        h["fp8"], P, batch, hq, P, stride, P, max_len, 0.1, None, None, P, None, ws, wsb, None)
+    assert lib.kvq_decode(*args(8, 4, 64, None, 0, batch=0)) == OK               # empty batch
+    assert lib.kvq_decode(*args(7, 4, 64, None, 0)) == ARG                        # Hq % Hkv
+    assert lib.kvq_decode(*args(34, 4, 64, None, 0)) == UNSUP                     # G = 17 > 16
+    assert lib.kvq_decode(*args(8, 3, 64, None, 0)) == ARG                        # stride < ceil(64/16)
+    need = lib.kvq_decode_workspace_bytes(h["fp8"], 4, 8, 200000)
+    assert need > 0                                                               # long context -> splits
+    assert lib.kvq_decode(*args(8, 12500, 200000, None, 0)) == SIZE
+    assert lib.kvq_decode(*args(8, 12500, 200000, P, need - 1)) == SIZE
+    assert lib.kvq_decode(*args(8, 12500, 200000, c_void_p(FAKE_DEV + 16), need)) == SIZE
+    bad = list(args(8, 4, 64, None, 0))
+    bad[1] = None
+    assert lib.kvq_decode(*bad) == ARG
