@@ -3,7 +3,11 @@
 
 One step = kvq_store of the new token(s) of every sequence + kvq_decode over
 the whole cache (split-context decode kernel and its combine), on seeded
-synthetic data already resident in HBM. Prints ONE JSON line.
+synthetic data already resident in HBM, launched eagerly on torch's current
+stream (--graph replays the same launches from captured HIP graphs instead:
+the library's calls allocate nothing and never synchronize; on this machine a
+graph replay costs more than the eager launches it replaces). Prints ONE JSON
+line.
 
 value = algorithmic KV bytes per step (codes + block scales of every cached
 token) / step time. Several copies of the cache are rotated so consecutive
@@ -106,12 +110,30 @@ def run_loop(st, steps, do_store, do_decode, offset=0):
                          out=st["out"], lse=st["lse"], workspace=st["ws"])
 
 
-def timed(st, steps, do_store, do_decode):
+def capture(st, do_store, do_decode):
+    """One HIP graph per rotated cache copy holding the step's launches (the
+    library neither allocates nor synchronizes, so the calls are capturable)."""
+    import torch
+    graphs = []
+    for r in range(len(st["caches"])):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run_loop(st, 1, do_store, do_decode, offset=r)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    return graphs
+
+
+def timed(st, steps, do_store, do_decode, graphs=None):
     import torch
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
-    run_loop(st, steps, do_store, do_decode)
+    if graphs:
+        for i in range(steps):
+            graphs[i % len(graphs)].replay()
+    else:
+        run_loop(st, steps, do_store, do_decode)
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps     # ms per iteration
@@ -173,6 +195,7 @@ def main():
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true", help="replay captured HIP graphs instead of eager launches")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the decode path shards across (sequence, KV head) with no "
@@ -190,9 +213,16 @@ def main():
     log(f"setup {time.time() - t0:.1f} s")
     run_loop(st, args.warmup, True, True)
     torch.cuda.synchronize()
-    ms_step = timed(st, args.steps, True, True)
-    ms_dec = timed(st, args.steps, False, True)
-    ms_store = timed(st, args.steps, True, False)
+    use_graph = args.graph
+    g_step = capture(st, True, True) if use_graph else None
+    g_dec = capture(st, False, True) if use_graph else None
+    g_store = capture(st, True, False) if use_graph else None
+    if use_graph:
+        for i in range(args.warmup):
+            g_step[i % len(g_step)].replay()
+    ms_step = timed(st, args.steps, True, True, g_step)
+    ms_dec = timed(st, args.steps, False, True, g_dec)
+    ms_store = timed(st, args.steps, True, False, g_store)
     kv_bytes = float(st["lens_h"].astype(np.int64).sum()) * st["bpt"]
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     dec_gbps = kv_bytes / (ms_dec * 1e-3) / 1e9
@@ -209,6 +239,7 @@ def main():
             "global_batch": w.batch, "seq_len": w.max_len, "kv_dtype": w.dtype,
             "compute": "KV codes dequantized in registers to bf16 (QK) / f16 (PV) MFMA operands, f32 accumulate",
             "cache_copies_rotated": args.rotate,
+            "launch": "HIP graph replay per step" if use_graph else "eager launches",
         },
         "pct_hbm_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "decode_only_GBps": round(dec_gbps, 2), "decode_ms": round(ms_dec, 5), "store_ms": round(ms_store, 5),

@@ -77,7 +77,7 @@ typedef struct kvq_cache_desc {
  *   GQA x {E4M3, E5M2}: head_dim in {64, 128}
  *   GQA x FP4_MX16:     head_dim == 128
  *   MLA x NVFP4:        head_dim == 576, v_dim == 512
- *   decode, GQA:        G = Hq / Hkv in [1, 16]
+ *   decode, GQA:        G = Hq / Hkv in [1, 16], max_seq_len <= 2,097,152
  *   decode, MLA:        Hq a multiple of 16, at most 128                     */
 
 /* Byte offsets (from the start of the caller's cache memory) and sizes of the
@@ -185,6 +185,9 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t
  *   out:        [dev] fp32 [batch][num_q_heads][v_dim]
  *   lse:        [dev] fp32 [batch][num_q_heads] (natural log) or NULL
  *   workspace:  [dev] >= kvq_decode_workspace_bytes(...), 256-byte aligned
+ *               (partial results of the context splits); may be NULL when
+ *               kvq_decode_workspace_bytes returns 0. Calls that share one
+ *               workspace must not overlap on the device.
  * A sequence of length 0 gets out = 0 and lse = -inf.
  * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_SIZE, KVQ_ERR_HIP. */
 int kvq_decode(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,

@@ -11,6 +11,7 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr size_t kScratchBytes = kvq::kAmaxBlocks * sizeof(unsigned);
+constexpr int kMaxDecodeLen = 128 * 1024 * kvq::kTile;  // 128 splits x 1024 tiles
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -71,11 +72,11 @@ struct SplitPlan {
 
 // Context split: enough workgroups to fill 256 CUs several times over, each
 // split an even number of 16-token tiles (waves consume tile pairs), at most
-// 128 splits per sequence.
+// 1024 tiles per split and 128 splits per sequence (so max_len <= 2M tokens).
 SplitPlan plan_gqa(int batch, int hkv, int max_len) {
   const int ntiles = (max_len + kvq::kTile - 1) / kvq::kTile;
   const int64_t units = (int64_t)batch * hkv;
-  int64_t target = 1536;
+  int64_t target = 512;
   if (const char* e = getenv("KVQ_DECODE_TARGET_WGS")) {
     const long v = strtol(e, nullptr, 10);
     if (v >= 1 && v <= (1 << 20)) target = v;
@@ -83,6 +84,7 @@ SplitPlan plan_gqa(int batch, int hkv, int max_len) {
   int64_t tps = units > 0 ? (ntiles * units + target - 1) / target : ntiles;
   if (tps < 16) tps = 16;  // 2 tile pairs per wave at least
   tps = (tps + 1) & ~(int64_t)1;
+  if (tps > 1024) tps = 1024;  // the kernel stages one split's page ids in LDS
   int64_t ns = ntiles > 0 ? (ntiles + tps - 1) / tps : 1;
   if (ns > 128) {
     ns = 128;
@@ -94,10 +96,18 @@ SplitPlan plan_gqa(int batch, int hkv, int max_len) {
   return {(int)tps, (int)ns};
 }
 
-size_t workspace_for(const SplitPlan& p, int batch, int hq, int dv) {
-  if (p.num_splits <= 1) return 0;
+// Workspace: [partial outputs fp32 B*Hq*S*Dv] [partial LSEs fp32 B*Hq*S].
+struct WsLayout {
+  size_t o, lse, total;
+};
+WsLayout workspace_for(const SplitPlan& p, int batch, int hq, int dv) {
+  WsLayout w = {0, 0, 0};
+  if (p.num_splits <= 1) return w;
   const size_t parts = (size_t)batch * hq * p.num_splits;
-  return align_up(parts * dv * sizeof(float)) + align_up(parts * sizeof(float));
+  w.o = 0;
+  w.lse = align_up(parts * dv * sizeof(float));
+  w.total = w.lse + align_up(parts * sizeof(float));
+  return w;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
@@ -193,7 +203,8 @@ int kvq_store(const kvq_cache* c, const void* k, const void* v, const int64_t* s
 
 size_t kvq_decode_workspace_bytes(const kvq_cache* c, int32_t batch, int32_t hq, int32_t max_len) {
   if (!c || batch < 0 || hq < 1 || max_len < 0) return 0;
-  if (c->desc.kind == KVQ_GQA) return workspace_for(plan_gqa(batch, c->desc.num_kv_heads, max_len), batch, hq, c->desc.v_dim);
+  if (c->desc.kind == KVQ_GQA)
+    return workspace_for(plan_gqa(batch, c->desc.num_kv_heads, max_len), batch, hq, c->desc.v_dim).total;
   return 0;
 }
 
@@ -208,12 +219,14 @@ int kvq_decode(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, con
   const int P = d.page_size;
   if (page_table_stride < (max_len + P - 1) / P || page_table_stride < 1) return KVQ_ERR_ARG;
   const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (max_len > kMaxDecodeLen) return KVQ_ERR_UNSUPPORTED;
   if (d.kind == KVQ_GQA) {
     if (hq % d.num_kv_heads) return KVQ_ERR_ARG;
     const int G = hq / d.num_kv_heads;
     if (G > 16) return KVQ_ERR_UNSUPPORTED;
     const SplitPlan plan = plan_gqa(batch, d.num_kv_heads, max_len);
-    const size_t need = workspace_for(plan, batch, hq, d.v_dim);
+    const WsLayout wl = workspace_for(plan, batch, hq, d.v_dim);
+    const size_t need = wl.total;
     if (need && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % kAlign)) return KVQ_ERR_SIZE;
     GqaDecodeArgs a;
     memset(&a, 0, sizeof(a));
@@ -240,10 +253,9 @@ int kvq_decode(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, con
     a.max_len = max_len;
     a.tiles_per_split = plan.tiles_per_split;
     a.num_splits = plan.num_splits;
-    const size_t parts = (size_t)batch * hq * plan.num_splits;
-    a.ws_o = need ? static_cast<float*>(ws) : nullptr;
-    a.ws_lse = need ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + align_up(parts * d.v_dim * sizeof(float)))
-                    : nullptr;
+    uint8_t* wsb = static_cast<uint8_t*>(ws);
+    a.ws_o = need ? reinterpret_cast<float*>(wsb + wl.o) : nullptr;
+    a.ws_lse = need ? reinterpret_cast<float*>(wsb + wl.lse) : nullptr;
     a.out = out;
     a.lse = lse;
     hipError_t e = kvq_launch_decode_gqa(c, a, s);

@@ -194,7 +194,7 @@ def kvq_decode(cache: Cache, q: torch.Tensor, page_table: torch.Tensor, seq_lens
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     need = kvq_decode_workspace_bytes(cache, B, Hq, max_seq_len)
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)   # split counters start at zero
     ks, vs = _dev_f32(k_scale, dev), _dev_f32(v_scale, dev)
     _check(_lib().kvq_decode(cache.handle, _ptr(q), B, Hq, _ptr(page_table), page_table.shape[1], _ptr(seq_lens),
                              max_seq_len, float(sm_scale), _ptr(ks), _ptr(vs), _ptr(out), _ptr(lse),
