@@ -78,7 +78,7 @@ typedef struct kvq_cache_desc {
  *   GQA x FP4_MX16:     head_dim == 128
  *   MLA x NVFP4:        head_dim == 576, v_dim == 512
  *   decode, GQA:        G = Hq / Hkv in [1, 16], max_seq_len <= 2,097,152
- *   decode, MLA:        Hq a multiple of 16, at most 128                     */
+ *   decode, MLA:        Hq in {64, 128}                                      */
 
 /* Byte offsets (from the start of the caller's cache memory) and sizes of the
  * buffers inside one cache. Absent buffers have size 0. Each buffer is
@@ -94,11 +94,18 @@ typedef struct kvq_cache_desc {
  *     V code:  1024*(d/128) + 16*(16*(t16/4) + (d%128)/8) + 4*(t16%4) + (d%8)/2
  *     K scale: 32*(b/2) + 2*t16 + b%2             (E8M0 code)
  *     V scale: 4*((D/16)*(t16/4) + b) + t16%4     (E8M0 code)
- *   MLA NVFP4 (token-major): code t*Dk/2 + d/2, scale t*Dk/16 + b (E4M3 code).
+ *   MLA NVFP4 (Dk 576, Dv 512), code tile = 4608 B, scale tile = 576 B,
+ *   g4 = t16/4, tt = t16%4:
+ *     code,  d < 512:  2*(((d/64*4 + g4)*16 + (d%64)/4)*4 + tt) + (d%4)/2
+ *     code,  d >= 512: 4096 + 2*((g4*16 + (d-512)/4)*4 + tt) + (d%4)/2
+ *     scale, b < 32:   4*((b/4*4 + g4)*4 + b%4) + tt      (E4M3 code)
+ *     scale, b >= 32:  512 + 4*(g4*4 + b-32) + tt
  * The K layouts put the 16 tokens of a tile at consecutive 16-byte lanes and
- * the V layouts put 4 consecutive tokens of one element in one dword, so each
- * wave of the decode kernel reads a tile with fully coalesced 16-byte loads
- * straight into matrix-core operand order.                                 */
+ * the V layouts put 4 consecutive tokens of one element (FP8) or of one
+ * 4- or 8-element group (MLA, FP4) in one lane load, so each wave of the
+ * decode kernels reads a tile with fully coalesced 16-byte loads straight
+ * into matrix-core operand order. Every byte holds codes of one token only,
+ * so a store never rewrites another token's bits.                          */
 typedef struct kvq_layout {
   size_t k_codes_offset, k_codes_bytes;
   size_t v_codes_offset, v_codes_bytes;

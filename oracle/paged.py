@@ -26,8 +26,13 @@ page, t16 = t % 16, tile = t // 16, d = element index, b = d // 16):
                   + 4 * (t16 % 4) + (d % 8) // 2
     K scale byte: 32 * (b // 2) + 2 * t16 + b % 2
     V scale byte: 4 * ((D // 16) * (t16 // 4) + b) + t16 % 4
-  MLA, NVFP4 (one latent row of Dk elements per token, num_kv_heads = 1),
-  token-major: code byte t * Dk/2 + d // 2, E4M3 scale byte t * Dk/16 + b.
+  MLA, NVFP4 (one latent row of Dk = 576 elements per token, the first
+  Dv = 512 of them are V; num_kv_heads = 1), tile = 4608 code bytes and 576
+  E4M3 scale bytes; g4 = t16 // 4, tt = t16 % 4:
+    code byte, d < 512:  2 * (((d // 64 * 4 + g4) * 16 + (d % 64) // 4) * 4 + tt) + (d % 4) // 2
+    code byte, d >= 512: 4096 + 2 * ((g4 * 16 + (d - 512) // 4) * 4 + tt) + (d % 4) // 2
+    scale byte, b < 32:  4 * ((b // 4 * 4 + g4) * 4 + b % 4) + tt
+    scale byte, b >= 32: 512 + 4 * (g4 * 4 + b - 32) + tt
 """
 from __future__ import annotations
 
@@ -66,12 +71,21 @@ def _tile_base(t, row_bytes):
     return (t // TILE) * TILE * row_bytes
 
 
+def _mla_code_byte(t, d):
+    t16 = t % TILE
+    g4, tt = t16 // 4, t16 % 4
+    lo = 2 * (((d // 64 * 4 + g4) * 16 + (d % 64) // 4) * 4 + tt) + (d % 4) // 2
+    hi = 4096 + 2 * ((g4 * 16 + (d - 512) // 4) * 4 + tt) + (d % 4) // 2
+    return _tile_base(t, 288) + np.where(d < 512, lo, hi)
+
+
 def k_code_pos(spec: CacheSpec, t, d):
     """(byte offset inside the page-head block, nibble) of K element (t, d)."""
     t = np.asarray(t); d = np.asarray(d)
     t16 = t % TILE
     if spec.kind == "mla":
-        return t * (spec.head_dim // 2) + d // 2, d % 2
+        assert spec.head_dim == 576 and spec.v_dim == 512
+        return _mla_code_byte(t, d), d % 2
     if spec.dtype in ("e4m3", "e5m2"):
         return _tile_base(t, spec.head_dim) + 256 * (d // 16) + 16 * t16 + d % 16, np.zeros_like(d)
     base = _tile_base(t, spec.head_dim // 2)
@@ -94,7 +108,11 @@ def v_code_pos(spec: CacheSpec, t, d):
 def k_scale_pos(spec: CacheSpec, t, b):
     t = np.asarray(t); b = np.asarray(b)
     if spec.kind == "mla":
-        return t * (spec.head_dim // 16) + b
+        t16 = t % TILE
+        g4, tt = t16 // 4, t16 % 4
+        lo = 4 * ((b // 4 * 4 + g4) * 4 + b % 4) + tt
+        hi = 512 + 4 * (g4 * 4 + b - 32) + tt
+        return _tile_base(t, 36) + np.where(b < 32, lo, hi)
     return _tile_base(t, spec.head_dim // 16) + 32 * (b // 2) + 2 * (t % TILE) + b % 2
 
 

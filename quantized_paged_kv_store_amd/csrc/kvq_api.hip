@@ -96,6 +96,31 @@ SplitPlan plan_gqa(int batch, int hkv, int max_len) {
   return {(int)tps, (int)ns};
 }
 
+// MLA: one workgroup per (sequence, split, 64-head group), one per CU; about
+// two rounds of 256 workgroups.
+SplitPlan plan_mla(int batch, int hq, int max_len) {
+  const int ntiles = (max_len + kvq::kTile - 1) / kvq::kTile;
+  const int64_t units = (int64_t)batch * (hq / 64);
+  int64_t target = 512;
+  if (const char* e = getenv("KVQ_DECODE_TARGET_WGS")) {
+    const long v = strtol(e, nullptr, 10);
+    if (v >= 1 && v <= (1 << 20)) target = v;
+  }
+  int64_t tps = units > 0 ? (ntiles * units + target - 1) / target : ntiles;
+  if (tps < 4) tps = 4;
+  tps = (tps + 1) & ~(int64_t)1;
+  if (tps > 1024) tps = 1024;
+  int64_t ns = ntiles > 0 ? (ntiles + tps - 1) / tps : 1;
+  if (ns > 128) {
+    ns = 128;
+    tps = (ntiles + ns - 1) / ns;
+    tps = (tps + 1) & ~(int64_t)1;
+    ns = (ntiles + tps - 1) / tps;
+  }
+  if (ns < 1) ns = 1;
+  return {(int)tps, (int)ns};
+}
+
 // Workspace: [partial outputs fp32 B*Hq*S*Dv] [partial LSEs fp32 B*Hq*S].
 struct WsLayout {
   size_t o, lse, total;
@@ -205,7 +230,8 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* c, int32_t batch, int32_t hq,
   if (!c || batch < 0 || hq < 1 || max_len < 0) return 0;
   if (c->desc.kind == KVQ_GQA)
     return workspace_for(plan_gqa(batch, c->desc.num_kv_heads, max_len), batch, hq, c->desc.v_dim).total;
-  return 0;
+  if (hq != 64 && hq != 128) return 0;
+  return workspace_for(plan_mla(batch, hq, max_len), batch, hq, c->desc.v_dim).total;
 }
 
 int kvq_decode(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, const int32_t* page_table,
@@ -278,7 +304,54 @@ int kvq_decode(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, con
     }
     return KVQ_OK;
   }
-  return KVQ_ERR_UNSUPPORTED;  // MLA decode: see decode_mla.hip
+  // MLA
+  if (hq != 64 && hq != 128) return KVQ_ERR_UNSUPPORTED;
+  if (!k_scale) return KVQ_ERR_ARG;  // the NVFP4 global scale
+  const SplitPlan plan = plan_mla(batch, hq, max_len);
+  const WsLayout wl = workspace_for(plan, batch, hq, d.v_dim);
+  const size_t need = wl.total;
+  if (need && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % kAlign)) return KVQ_ERR_SIZE;
+  MlaDecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.codes = c->base + c->layout.k_codes_offset;
+  a.scales = c->base + c->layout.k_scales_offset;
+  a.num_pages = d.num_pages;
+  a.q = static_cast<const uint16_t*>(q);
+  a.page_table = page_table;
+  a.page_table_stride = page_table_stride;
+  a.seq_lens = seq_lens;
+  a.g_scale = k_scale;
+  a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
+  a.batch = batch;
+  a.hq = hq;
+  a.page_size = P;
+  a.max_len = max_len;
+  a.tiles_per_split = plan.tiles_per_split;
+  a.num_splits = plan.num_splits;
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  a.ws_o = need ? reinterpret_cast<float*>(wsb + wl.o) : nullptr;
+  a.ws_lse = need ? reinterpret_cast<float*>(wsb + wl.lse) : nullptr;
+  a.out = out;
+  a.lse = lse;
+  hipError_t e = kvq_launch_decode_mla(c, a, s);
+  if (e != hipSuccess) return KVQ_ERR_HIP;
+  if (plan.num_splits > 1) {
+    CombineArgs cb;
+    cb.ws_o = a.ws_o;
+    cb.ws_lse = a.ws_lse;
+    cb.seq_lens = seq_lens;
+    cb.out = out;
+    cb.lse = lse;
+    cb.batch = batch;
+    cb.hq = hq;
+    cb.dv = d.v_dim;
+    cb.num_splits = plan.num_splits;
+    cb.tokens_per_split = plan.tiles_per_split * kvq::kTile;
+    cb.max_len = max_len;
+    e = kvq_launch_combine(cb, s);
+    if (e != hipSuccess) return KVQ_ERR_HIP;
+  }
+  return KVQ_OK;
 }
 
 }  // extern "C"

@@ -256,10 +256,31 @@ __global__ void __launch_bounds__(256) store_nvfp4_kernel(
     for (int i = 0; i < 16; ++i) x[i] = fminf(fmaxf(x[i] / sd, -6.0f), 6.0f);
   }
   const uint32_t c0 = encode_e2m1x8(x), c1 = encode_e2m1x8(x + 8);
-  // token-major layout: codes t*dim/2 + d/2, scales t*dim/16 + b
-  const int64_t t_glob = slot;  // page*page_size + t: both layouts are token-major per page
-  *reinterpret_cast<uint2*>(codes + t_glob * (dim / 2) + 8 * b) = make_uint2(c0, c1);
-  scales[t_glob * nb + b] = (uint8_t)sc;
+  // MLA tile layout (16 tokens, 4608 code + 576 scale bytes): the 8-element
+  // groups of one token and lane group sit in dwords laid out for the decode
+  // kernel's loads (see include/kvq.h)
+  const int page = (int)(slot / page_size);
+  const int t = (int)(slot % page_size);
+  const int t16 = t & 15, g4 = t16 >> 2, tt = t16 & 3;
+  uint8_t* cb = codes + (int64_t)page * page_size * (dim / 2) + (int64_t)(t >> 4) * 16 * (dim / 2);
+  uint8_t* sb = scales + (int64_t)page * page_size * nb + (int64_t)(t >> 4) * 16 * nb;
+  // 16 elements = four 4-element groups, 2 code bytes each
+  int64_t oc[4], os;
+  if (b < 32) {
+    const int w8 = b >> 2;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) oc[q] = 2 * (((w8 * 4 + g4) * 16 + 4 * (b & 3) + q) * 4 + tt);
+    os = 4 * ((w8 * 4 + g4) * 4 + (b & 3)) + tt;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) oc[q] = 4096 + 2 * ((g4 * 16 + 4 * (b - 32) + q) * 4 + tt);
+    os = 512 + 4 * (g4 * 4 + b - 32) + tt;
+  }
+  *reinterpret_cast<uint16_t*>(cb + oc[0]) = (uint16_t)(c0 & 0xffffu);
+  *reinterpret_cast<uint16_t*>(cb + oc[1]) = (uint16_t)(c0 >> 16);
+  *reinterpret_cast<uint16_t*>(cb + oc[2]) = (uint16_t)(c1 & 0xffffu);
+  *reinterpret_cast<uint16_t*>(cb + oc[3]) = (uint16_t)(c1 >> 16);
+  sb[os] = (uint8_t)sc;
 }
 
 }  // namespace

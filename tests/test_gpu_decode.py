@@ -87,3 +87,28 @@ def test_llama3_8b_decode_sampled():
     mab, r = _check(c, [0, 5], "llama3_8b")
     q_err = rel_l2(c.out.cpu().numpy()[0], c.unquantized(0))
     print(f"llama3_8b: max-abs {mab:.2e} rel-L2 {r:.2e}; quantization error vs BF16 attention rel-L2 {q_err:.3e}")
+
+
+@pytest.mark.parametrize("hq,P", [(128, 64), (64, 16), (128, 32)])
+def test_mla_ragged_lengths(hq, P):
+    lens = [0, 1, 17, 64, 100, 1000, 2500]
+    w = I.Workload(f"mla-ragged-{hq}", "nvfp4", "mla", len(lens), hq, 1, 576, 512, P, max(lens), 0, 1, "mla", seed=9)
+    c = Case(w, lens=lens).run_gpu()
+    ids = list(range(len(lens)))
+    _check(c, ids, f"mla Hq{hq} P{P}")
+    assert np.all(c.out.cpu().numpy()[0] == 0)
+
+
+def test_mla_split_count_invariance():
+    w = I.WORKLOADS["dsr1_mla"].with_(batch=2, max_len=9000, min_len=9000)
+    c = Case(w).run_gpu(decode=False)
+    outs = []
+    for target in ("1", "32", "100000"):
+        os.environ["KVQ_DECODE_TARGET_WGS"] = target
+        try:
+            o, l = K.kvq_decode(c.cache, c.q_dev, c.table_dev, c.lens_dev, c.max_len, I.sm_scale(w), c.k_scale, None)
+            outs.append((o.cpu().numpy(), l.cpu().numpy()))
+        finally:
+            del os.environ["KVQ_DECODE_TARGET_WGS"]
+    for o, l in outs[1:]:
+        assert rel_l2(o, outs[0][0]) < 3e-4 and np.allclose(l, outs[0][1], atol=1e-5)
