@@ -29,6 +29,26 @@ if ROOT not in sys.path:
 
 METRIC = "decode-attn effective KV GB/s (% HBM peak), 8B-shape FP8 bs8 ctx20K"
 PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E, vendor figure
+PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, vendor figure
+
+
+def measured_traffic(w):
+    """HBM bytes per launch of the decode kernel from the committed rocprofv3
+    counter runs, or None when no measurement exists for this workload or the
+    kernel's sources changed since it was taken."""
+    import hashlib
+    kind = "gqa" if w.kind == "gqa" else "mla"
+    path = os.path.join(ROOT, "profiles", f"kvq_decode_{kind}_{w.name}_{w.dtype}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None
+    return int(round(1024 * (rec["fetch_size_kib_per_dispatch"] * rec["fetch_scale"]
+                             + rec["write_size_kib_per_dispatch"] * rec["write_scale"])))
 
 
 def log(*a):
@@ -187,6 +207,25 @@ def cpu_baseline(w, seconds_hint=20.0):
             "decode_s": round(t_dec, 3), "codec_s": round(t_codec, 3)}
 
 
+def copy_reference(nbytes=1 << 30, reps=10):
+    """A plain device copy of known size (src -> dst), the reference the HBM
+    traffic counters are scaled by."""
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "ms": round(ms, 4),
+                      "GBps_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,7 +235,11 @@ def main():
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay captured HIP graphs instead of eager launches")
+    ap.add_argument("--copy-ref", action="store_true", help="only run the 1 GiB reference copy (for counters)")
     args = ap.parse_args()
+    if args.copy_ref:
+        copy_reference()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the decode path shards across (sequence, KV head) with no "
               f"exchange, so a multi-GPU figure is N independent copies of this one; got --gpus {args.gpus}",
@@ -223,6 +266,19 @@ def main():
     ms_step = timed(st, args.steps, True, True, g_step)
     ms_dec = timed(st, args.steps, False, True, g_dec)
     ms_store = timed(st, args.steps, True, False, g_store)
+    # per-kernel device time: the library brackets each launch with HIP events
+    # on the launch stream while instrumentation is on
+    import quantized_paged_kv_store_amd as K
+    K.kvq_profile_enable(True)
+    run_loop(st, args.steps, True, True)
+    torch.cuda.synchronize()
+    dec_tot, dec_n = K.kvq_profile_read("decode")
+    mer_tot, mer_n = K.kvq_profile_read("merge")
+    sto_tot, sto_n = K.kvq_profile_read("store")
+    K.kvq_profile_enable(False)
+    kern_ms = dec_tot / max(dec_n, 1)
+    merge_ms = mer_tot / max(mer_n, 1) if mer_n else 0.0
+    store_kern_ms = sto_tot / max(sto_n, 1)
     kv_bytes = float(st["lens_h"].astype(np.int64).sum()) * st["bpt"]
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     dec_gbps = kv_bytes / (ms_dec * 1e-3) / 1e9
@@ -237,7 +293,9 @@ def main():
                         f"batch {w.batch}, context {w.max_len}, page {w.page_size}, {w.dtype} KV "
                         f"({w.scale_mode} scales); step = store {w.new_tokens} new token(s)/sequence + decode",
             "global_batch": w.batch, "seq_len": w.max_len, "kv_dtype": w.dtype,
-            "compute": "KV codes dequantized in registers to bf16 (QK) / f16 (PV) MFMA operands, f32 accumulate",
+            "compute": ("latent codes dequantized to fp16 (E2M1 x E4M3 exact) for QK and PV MFMAs, f32 accumulate"
+                        if w.kind == "mla" else
+                        "KV codes dequantized in registers to bf16 (QK) / f16 (PV) MFMA operands, f32 accumulate"),
             "cache_copies_rotated": args.rotate,
             "launch": "HIP graph replay per step" if use_graph else "eager launches",
         },
@@ -245,11 +303,24 @@ def main():
         "decode_only_GBps": round(dec_gbps, 2), "decode_ms": round(ms_dec, 5), "store_ms": round(ms_store, 5),
         "context_tokens_per_s": round(float(st["lens_h"].sum()) / (ms_step * 1e-3), 1),
         "decode_tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),
-        "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
-                     "kernel": "kvq_decode (decode + combine launches), algorithmic KV bytes / HIP-event time",
-                     "algorithmic_bytes_per_launch": kv_bytes},
     }
+    traffic = measured_traffic(w)
+    if w.kind == "mla":
+        flops = float(st["lens_h"].astype(np.int64).sum()) * w.q_heads * (w.head_dim + w.v_dim) * 2
+        ach = flops / (kern_ms * 1e-3) / 1e12
+        res["roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(ach / PEAK_F16_TFLOPS, 4), "traffic": traffic,
+                           "kernel": "decode_mla_kernel (fp16 MFMA)", "kernel_ms": round(kern_ms, 5),
+                           "algorithmic_flops_per_launch": flops,
+                           "hbm_GBps": round(kv_bytes / (kern_ms * 1e-3) / 1e9, 2)}
+    else:
+        ach = kv_bytes / (kern_ms * 1e-3) / 1e9
+        res["roofline"] = {"bound": "hbm", "achieved": round(ach, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                           "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                           "kernel": f"decode_gqa_kernel ({w.dtype}, head_dim {w.head_dim})",
+                           "kernel_ms": round(kern_ms, 5), "algorithmic_bytes_per_launch": kv_bytes}
+    res["roofline"]["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)"
+    res["kernel_ms"] = {"decode": round(kern_ms, 5), "merge": round(merge_ms, 5), "store": round(store_kern_ms, 5)}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(res), flush=True)

@@ -202,6 +202,17 @@ int kvq_decode(const kvq_cache* cache, const void* q, int32_t batch, int32_t num
                int32_t max_seq_len, float sm_scale, const float* k_scale, const float* v_scale,
                float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Instrumentation (off by default). While enabled, every kernel launched by
+ * kvq_store / kvq_decode / kvq_compute_scale is bracketed by two HIP events
+ * recorded on the call's stream (nothing else changes; do not enable while
+ * capturing a HIP graph). Enabling or disabling clears the records.
+ * kvq_profile_read synchronizes the recorded events and returns, for one
+ * kernel family ("store", "decode", "merge", "amax"), the summed device
+ * time in milliseconds and the number of launches, then forgets them.
+ * Errors: KVQ_ERR_ARG (unknown name, null outputs), KVQ_ERR_HIP. */
+int kvq_profile_enable(int on);
+int kvq_profile_read(const char* kernel, double* total_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -3,7 +3,10 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
+#include <string>
+#include <vector>
 
 #include "kvq_internal.h"
 
@@ -137,9 +140,97 @@ WsLayout workspace_for(const SplitPlan& p, int batch, int hq, int dv) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// ------------------------------------------------------------ instrumentation
+struct ProfRecord {
+  int family;  // 0 store, 1 decode, 2 merge, 3 amax
+  hipEvent_t start, stop;
+};
+const char* const kFamilies[] = {"store", "decode", "merge", "amax"};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRecord> g_prof;
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+void clear_records_locked() {
+  for (auto& r : g_prof) {
+    hipEventSynchronize(r.stop);
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  g_prof.clear();
+}
+
+// Brackets one launch with events when instrumentation is on.
+struct Timed {
+  int family;
+  hipStream_t stream;
+  hipEvent_t start = nullptr, stop = nullptr;
+  Timed(int f, hipStream_t s) : family(f), stream(s) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on) return;
+    start = take_event();
+    stop = take_event();
+    if (start && stop) hipEventRecord(start, stream);
+  }
+  ~Timed() {
+    if (!start || !stop) return;
+    hipEventRecord(stop, stream);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof.push_back({family, start, stop});
+  }
+};
+
 }  // namespace
 
 extern "C" {
+
+int kvq_profile_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  clear_records_locked();
+  g_prof_on = on != 0;
+  return KVQ_OK;
+}
+
+int kvq_profile_read(const char* kernel, double* total_ms, int64_t* launches) {
+  if (!kernel || !total_ms || !launches) return KVQ_ERR_ARG;
+  int fam = -1;
+  for (int i = 0; i < 4; ++i)
+    if (std::string(kernel) == kFamilies[i]) fam = i;
+  if (fam < 0) return KVQ_ERR_ARG;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  double tot = 0.0;
+  int64_t n = 0;
+  int status = KVQ_OK;
+  std::vector<ProfRecord> keep;
+  for (auto& r : g_prof) {
+    if (r.family != fam) {
+      keep.push_back(r);
+      continue;
+    }
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
+      status = KVQ_ERR_HIP;
+    tot += ms;
+    ++n;
+    g_event_pool.push_back(r.start);
+    g_event_pool.push_back(r.stop);
+  }
+  g_prof.swap(keep);
+  *total_ms = tot;
+  *launches = n;
+  return status;
+}
 
 const char* kvq_status_string(int status) {
   switch (status) {
@@ -205,6 +296,7 @@ int kvq_compute_scale(const kvq_cache* c, const void* x0, int64_t n0, const void
     default: return KVQ_ERR_UNSUPPORTED;
   }
   unsigned* scratch = reinterpret_cast<unsigned*>(c->base + c->layout.scratch_offset);
+  Timed timer(3, static_cast<hipStream_t>(stream));
   const hipError_t e = kvq_launch_amax(static_cast<const uint16_t*>(x0), n0, static_cast<const uint16_t*>(x1), n1,
                                        scratch, div, scale_out, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
@@ -221,6 +313,7 @@ int kvq_store(const kvq_cache* c, const void* k, const void* v, const int64_t* s
     if (v) return KVQ_ERR_ARG;
     if (!k_scale) return KVQ_ERR_ARG;  // NVFP4 needs its global scale
   }
+  Timed timer(0, static_cast<hipStream_t>(stream));
   const hipError_t e = kvq_launch_store(c, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), slots, n,
                                         k_scale, v_scale, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
@@ -284,9 +377,14 @@ int kvq_decode(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, con
     a.ws_lse = need ? reinterpret_cast<float*>(wsb + wl.lse) : nullptr;
     a.out = out;
     a.lse = lse;
-    hipError_t e = kvq_launch_decode_gqa(c, a, s);
+    hipError_t e;
+    {
+      Timed timer(1, s);
+      e = kvq_launch_decode_gqa(c, a, s);
+    }
     if (e != hipSuccess) return KVQ_ERR_HIP;
     if (plan.num_splits > 1) {
+      Timed timer(2, s);
       CombineArgs cb;
       cb.ws_o = a.ws_o;
       cb.ws_lse = a.ws_lse;
@@ -333,9 +431,14 @@ int kvq_decode(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, con
   a.ws_lse = need ? reinterpret_cast<float*>(wsb + wl.lse) : nullptr;
   a.out = out;
   a.lse = lse;
-  hipError_t e = kvq_launch_decode_mla(c, a, s);
+  hipError_t e;
+  {
+    Timed timer(1, s);
+    e = kvq_launch_decode_mla(c, a, s);
+  }
   if (e != hipSuccess) return KVQ_ERR_HIP;
   if (plan.num_splits > 1) {
+    Timed timer(2, s);
     CombineArgs cb;
     cb.ws_o = a.ws_o;
     cb.ws_lse = a.ws_lse;

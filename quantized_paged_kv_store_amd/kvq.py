@@ -66,6 +66,10 @@ def _lib():
         L.kvq_decode.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_int32,
                                  c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
         L.kvq_decode.restype = c_int32
+        L.kvq_profile_enable.argtypes = [c_int32]
+        L.kvq_profile_enable.restype = c_int32
+        L.kvq_profile_read.argtypes = [c_char_p, POINTER(c_double), POINTER(c_int64)]
+        L.kvq_profile_read.restype = c_int32
         _LIB = L
     return _LIB
 
@@ -201,3 +205,16 @@ def kvq_decode(cache: Cache, q: torch.Tensor, page_table: torch.Tensor, seq_lens
                              _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(dev)),
            "kvq_decode")
     return out, lse
+
+
+def kvq_profile_enable(on: bool = True) -> None:
+    """Bracket every library kernel launch with HIP events (instrumentation)."""
+    _check(_lib().kvq_profile_enable(1 if on else 0), "kvq_profile_enable")
+
+
+def kvq_profile_read(kernel: str) -> tuple[float, int]:
+    """(summed device ms, launches) of one kernel family since the last read:
+    "store", "decode", "merge" or "amax"."""
+    ms, n = c_double(), c_int64()
+    _check(_lib().kvq_profile_read(kernel.encode(), byref(ms), byref(n)), "kvq_profile_read")
+    return ms.value, n.value

@@ -34,7 +34,8 @@ def test_exports_every_declared_function():
     names = _declared()
     assert set(names) >= {"kvq_alloc_pages", "kvq_store", "kvq_decode", "kvq_compute_scale",
                           "kvq_bytes_per_token", "kvq_status_string", "kvq_cache_layout",
-                          "kvq_free_handle", "kvq_decode_workspace_bytes"}
+                          "kvq_free_handle", "kvq_decode_workspace_bytes", "kvq_profile_enable",
+                          "kvq_profile_read"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -167,3 +168,22 @@ def test_decode_argument_errors(handles):
     bad = list(args(8, 4, 64, None, 0))
     bad[1] = None
     assert lib.kvq_decode(*bad) == ARG
+
+
+def test_profile_entry_points_without_gpu():
+    lib = _lib()
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    assert lib.kvq_profile_enable(1) == OK
+    assert lib.kvq_profile_read(b"decode", byref(ms), byref(n)) == OK and n.value == 0
+    assert lib.kvq_profile_read(b"bogus", byref(ms), byref(n)) == ARG
+    assert lib.kvq_profile_read(b"merge", None, byref(n)) == ARG
+    assert lib.kvq_profile_enable(0) == OK
+
+
+def test_mla_decode_argument_errors(handles):
+    lib, h = handles
+    P = c_void_p(FAKE_DEV)
+    mla = lambda hq, ks, batch=2: (h["mla"], P, batch, hq, P, 16, P, 1000, 0.04, ks, None, P, None, None, 0, None)
+    assert lib.kvq_decode(*mla(96, P)) == UNSUP          # 64 or 128 heads only
+    assert lib.kvq_decode(*mla(128, None)) == ARG        # the NVFP4 global scale is required
+    assert lib.kvq_decode_workspace_bytes(h["mla"], 2, 96, 1000) == 0
