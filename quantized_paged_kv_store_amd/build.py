@@ -22,6 +22,12 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 
+# per-source extras: the MLA kernel keeps its MFMA accumulators in VGPR form
+# (otherwise the compiler parks them in AGPRs and copies all 128 of them
+# through VGPRs on every step)
+EXTRA = {"decode_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _hipcc() -> str:
     p = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(p):
@@ -45,7 +51,8 @@ def build(verbose: bool = False) -> str:
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     objs = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in srcs]
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        futs = [ex.submit(_run, [hipcc, *FLAGS, "-c", s, "-o", o]) for s, o in zip(srcs, objs)]
+        futs = [ex.submit(_run, [hipcc, *FLAGS, *EXTRA.get(os.path.basename(s), []), "-c", s, "-o", o])
+                for s, o in zip(srcs, objs)]
         for f in futs:
             msg = f.result()
             if verbose and msg.strip():

@@ -6,62 +6,101 @@
 // E2M1 with one E4M3 scale per 16 elements and a global fp32 scale g (the
 // two-level NVFP4 scaling of the SGLang PR #21954 analysis page); the
 // dequantization happens inside this kernel (SGLang "Quantized KV Cache"
-// page, performance warning), into registers and LDS, never back to HBM.
+// page, performance warning), into LDS, never back to HBM.
 //
 // This is a dense contraction (the query heads share each latent element),
 // so both products run on matrix cores in fp16, where E2M1 x E4M3 is exact:
-//   S^T[t][h]  = K^[t][:] . Qs^T[:][h]      v_mfma_f32_16x16x32_f16
+//   S^T[t][h]  = K^[t][:] . Qs^T[:][h]      v_mfma_f32_32x32x16_f16
 //                 Qs = Q * 2^s_h (a per-head power of two, so fp16 holds the
 //                 BF16 query exactly; 2^-s_h goes into the score scale)
-//   O^T[d][h] += V^T[d][t] . P^T[t][h]      v_mfma_f32_16x16x32_f16, P * 2^15
+//   O^T[d][h] += V^T[d][t] . P^T[t][h]      v_mfma_f32_32x32x16_f16, P * 2^7
 // and g is factored out of both (applied to the scores and to the output).
+// The 32x32x16 shape is used throughout: on gfx950 it sustains close to the
+// matrix-core peak with two independent accumulators per wave, and its
+// operand pattern (32 rows x 16 B) reads LDS without bank conflicts.
 //
-// Workgroup = 8 waves (2 per SIMD) = 64 query heads of one (sequence,
-// context split); the two 64-head groups of a split get block ids 8 apart,
-// i.e. the same XCD, so the second reads the latent tile from that L2.
-// Per 32-token step (two 16-token tiles):
-//   1. wave w loads the V elements [64w, 64w+64) of the 32 tokens in
-//      PV-operand order (lane = 4 tokens x 4 elements, 8 bytes per tile) and
-//      one rope group, dequantizes in registers, keeps its V slice for PV and
-//      writes everything token-major into the LDS K^ tile;
-//   2. wave w computes S for heads 16(w%4)..+15 and tokens 16(w/4)..+15 from
-//      the LDS K^ tile and the LDS copy of Q (18 MFMAs), the two waves of a
-//      head block exchange their maxima,
-//      and publish P (fp16) and the rescale factors in LDS;
-//   3. wave w accumulates O for its 64 V elements and all 64 heads (16 MFMAs).
+// Workgroup = 4 waves, one per SIMD (each wave may hold 512 registers) = 64
+// query heads of one (sequence, context split); the two 64-head groups of a
+// split get block ids 8 apart, i.e. the same XCD, so the second reads the
+// latent tiles from that L2. A step covers 64 tokens (four 16-token tiles):
+//   1. every wave dequantizes elements [128w, 128w+128) and a quarter of the
+//      rope group of the 64 tokens into the LDS K^ tile (token-major, fp16);
+//   2. wave w scores heads 32(w&1)..+31 against all 64 tokens over half of
+//      the dot product (elements [288(w>>1), +288)): Q of those heads and
+//      elements stays in registers for the whole kernel (72 registers; the
+//      whole row would not fit beside the output accumulators). The two
+//      waves of a head block add each other's partial scores through LDS,
+//      so both hold the full scores and the same softmax state;
+//   3. each wave writes the P (fp16) of its 32-token half in the exact
+//      register layout of the PV B operand, so the PV waves read it back
+//      with conflict-free 16 B reads;
+//   4. wave w accumulates O^T for elements [128w, 128w+128) and all 64 heads.
+//      Its A operand (V^T: one element, 8 tokens per lane) is read straight
+//      from the token-major K^ tile with ds_read_b64_tr_b16, gfx950's
+//      transposing LDS read, so the latent is dequantized only once.
+#include <type_traits>
+
 #include "kvq_internal.h"
 
 namespace kvq {
 namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr float kPBias = 15.0f;
+constexpr float kPBias = 7.0f;   // P is stored as p * 2^7 in fp16
+constexpr float kSlack = 8.0f;   // log2 headroom of the lazy reference maximum
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kDk = 576, kDv = 512;
 constexpr int kHeadsPerWG = 64;
-constexpr int kThreads = 512;
-constexpr int kKRow = kDk * 2 + 16;   // bytes per token row of the LDS K^ tile (padded)
-constexpr int kPRow = 32 * 2 + 16;    // bytes per head row of the LDS P tile (padded)
+constexpr int kThreads = 256;
+constexpr int kStepTiles = 4;                 // 64 tokens per step
+constexpr int kStepTokens = kStepTiles * kTile;
+constexpr int kKRow = kDk * 2 + 16;           // bytes per token row of the LDS K^ tile (padded)
 constexpr int kTileCodes = 4608, kTileScales = 576;
-constexpr int kMaxSplitPages = 1024;
 
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
 
-// raw per-lane bytes of one 16-token tile
-struct MTile {
-  uint2 v;      // V slice: tokens 4g..4g+3, elements 64w + 4*col .. +3 (2 bytes per token)
-  uint32_t vs;  // E4M3 scales of those tokens (their 16-element block), one byte per token
-};
+__device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
 
-__device__ __forceinline__ uint32_t e4m3_to_f16x2_bcast(uint32_t byte) {
-  // E4M3 code -> the same fp16 value in both halves (exact)
-  f16x2 r = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(byte | (byte << 8), 1.0f, false);
-  return __builtin_bit_cast(uint32_t, r);
+// transposed 4 x 16-bit LDS read (see the lane mapping where it is used)
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
 }
 
-__device__ __forceinline__ uint32_t pk_mul_f16(uint32_t a, uint32_t b) {
-  f16x2 r = __builtin_bit_cast(f16x2, a) * __builtin_bit_cast(f16x2, b);
-  return __builtin_bit_cast(uint32_t, r);
+// raw per-lane bytes of one 64-token step
+struct Step {
+  uint2 v[kStepTiles][2];      // [tile][64-element group]: tokens 4g..4g+3, elements 4*col..+3 of the group
+  uint32_t vs[kStepTiles][2];  // their E4M3 block scales, one byte per token
+  uint32_t r[kStepTiles];      // rope codes of this lane's item (2 bytes) per tile
+  uint32_t rs[kStepTiles];     // rope scale byte per tile
+  int ok;                      // bit s: tile s holds real tokens
+  int tA;                      // first tile of the step
+};
+
+// buffer descriptor over one tile's bytes: loads past `bytes` return zero
+constexpr int kRsrcWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, bytes, kRsrcWord3);
+}
+
+// fp16 values of elements 4*col .. 4*col+3 of group j, tokens 4g + tt (tt =
+// 0..3) of tile s: x[tt] = {elements 0,1 | elements 2,3}
+__device__ __forceinline__ void dequant16(const Step& S, int s, int j, uint2 (&x)[4]) {
+  const f16x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(S.vs[s][j], 1.0f, false);
+  const f16x2 s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(S.vs[s][j], 1.0f, true);
+  const f16x2 sc[4] = {f16x2{s01[0], s01[0]}, f16x2{s01[1], s01[1]}, f16x2{s23[0], s23[0]}, f16x2{s23[1], s23[1]}};
+  const uint32_t lo = S.v[s][j].x, hi = S.v[s][j].y;  // tokens 0,1 | 2,3
+  const f16x2 c[8] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo, 1.0f, 0), __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo, 1.0f, 1),
+                      __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo, 1.0f, 2), __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo, 1.0f, 3),
+                      __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(hi, 1.0f, 0), __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(hi, 1.0f, 1),
+                      __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(hi, 1.0f, 2), __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(hi, 1.0f, 3)};
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt)
+    x[tt] = make_uint2(__builtin_bit_cast(uint32_t, c[2 * tt] * sc[tt]), __builtin_bit_cast(uint32_t, c[2 * tt + 1] * sc[tt]));
 }
 
 __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecodeArgs a) {
@@ -74,8 +113,9 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
   const int b = unit / a.num_splits, split = unit - b * a.num_splits;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g = lane >> 4, col = lane & 15;
-  const int hb = wave & 3, tb = wave >> 2;  // QK role: head block, token block
+  const int g = lane >> 4, col = lane & 15;   // dequant role: token group, element quad
+  const int r32 = lane & 31, hh = lane >> 5;  // MFMA role: row / column, k half
+  const int hgp = wave & 1, kh = wave >> 1;   // score role: 32-head block, half of the dot product
 
   const int L = min(max(a.seq_lens[b], 0), a.max_len);
   const int ntiles = (L + kTile - 1) / kTile;
@@ -93,14 +133,14 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
     return;
   }
 
-  __shared__ __attribute__((aligned(16))) uint8_t sm_k[32 * kKRow];
-  __shared__ __attribute__((aligned(16))) uint8_t sm_p[kHeadsPerWG * kPRow];
-  __shared__ float sm_mx[2][kHeadsPerWG];
+  __shared__ __attribute__((aligned(16))) uint8_t sm_k[kStepTokens * kKRow];
+  __shared__ __attribute__((aligned(16))) uint8_t sm_p[4 * 2 * 64 * 16];  // [k step][head block][lane][8 x fp16]
+  __shared__ __attribute__((aligned(16))) float sm_s[2 * 2 * 2 * 4 * 64 * 4];  // partial scores [hgp][kh][tb][quad][lane][4]
   __shared__ float sm_alpha[kHeadsPerWG];
   __shared__ float sm_l[2][kHeadsPerWG];
+  __shared__ float sm_e[2][kHeadsPerWG];
   __shared__ float sm_m[kHeadsPerWG];
-  __shared__ int sm_pg[kMaxSplitPages];
-  __shared__ __attribute__((aligned(16))) uint8_t sm_q[kHeadsPerWG * kKRow];  // Q^T, fp16, per-head scaled
+  __shared__ int sm_pg[kMlaMaxSplitPages];
 
   const int tpp = a.page_size / kTile;
   const int fp = t_begin / tpp;
@@ -108,23 +148,23 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
   const int32_t* pt = a.page_table + (int64_t)b * a.page_table_stride;
   for (int i = tid; i < n_pg; i += kThreads) sm_pg[i] = pt[fp + i];
 
-  // ---- Q of head block hb, scaled by a per-head power of two, staged in LDS ----
-  // (kept in LDS rather than registers: with 64 accumulators per lane the
-  // fragments would spill, and spill reloads queue behind the prefetch loads)
+  // ---- Q of this wave's 32 heads, scaled by a per-head power of two, in registers ----
+  // B operand of step ks: head 32*hgp + r32, elements 288*kh + 16*ks + 8*hh .. +7
+  f16x8 qf[18];
   float sscale;
   {
-    const int head = h0 + 16 * hb + col;
-    const uint16_t* qrow = a.q + ((int64_t)b * a.hq + head) * kDk + 8 * g;
-    uint4 raw[18];
+    const int head = h0 + 32 * hgp + r32;
+    const uint16_t* qrow = a.q + ((int64_t)b * a.hq + head) * kDk;
     uint32_t mx = 0;
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) {
-      raw[ks] = *reinterpret_cast<const uint4*>(qrow + 32 * ks);
-      const uint32_t w4[4] = {raw[ks].x, raw[ks].y, raw[ks].z, raw[ks].w};
+    for (int ks = 0; ks < 36; ++ks) {
+      // the per-head maximum needs the whole row; only this wave's half is kept
+      const uint4 raw = *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * hh);
+      const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) mx = max(mx, max(w4[j] & 0x7fffu, (w4[j] >> 16) & 0x7fffu));
+      if (ks / 18 == kh) qf[ks % 18] = __builtin_bit_cast(f16x8, raw);
     }
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16, 64));
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32, 64));
     // power of two putting the head's largest |q| in [2^14, 2^15)
     const int e = mx ? (int)(mx >> 7) - 127 : 0;
@@ -133,231 +173,300 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
     sscale = a.sm_scale_log2 * a.g_scale[0] * __builtin_ldexpf(1.0f, -sh);
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
-      const uint32_t w4[4] = {raw[ks].x, raw[ks].y, raw[ks].z, raw[ks].w};
+      const u32x4 w4 = __builtin_bit_cast(u32x4, qf[ks]);
       u32x4 h;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         h[j] = pack_f16x2(bf16_bits_to_f32(w4[j] & 0xffffu) * qmul, bf16_bits_to_f32(w4[j] >> 16) * qmul);
-      if (tb == 0)
-        *reinterpret_cast<u32x4*>(sm_q + (16 * hb + col) * kKRow + 16 * g + 64 * ks) = h;
+      qf[ks] = __builtin_bit_cast(f16x8, h);
     }
   }
-  __syncthreads();  // sm_pg, sm_q
+  __syncthreads();  // sm_pg
 
   const int64_t page_codes = (int64_t)a.page_size * (kDk / 2);
   const int64_t page_scales = (int64_t)a.page_size * (kDk / 16);
-  // rope item of this lane: tile s (0/1 of the step), token 4*rg + rtt, elements 512 + 4*ri .. +3
+  // rope item of this lane (per tile): token 4*r_g + r_tt, elements 512 + 4*r_i .. +3
   const int r_item = wave * 64 + lane;
-  const int r_tile = r_item >> 8, r_g = (r_item >> 6) & 3, r_i = (r_item >> 2) & 15, r_tt = r_item & 3;
+  const int r_g = r_item >> 6, r_i = (r_item >> 2) & 15, r_tt = r_item & 3;
 
-  struct Step {
-    MTile t[2];
-    uint32_t r;   // rope codes (2 bytes)
-    uint32_t rs;  // rope scale byte
-    int ok;       // bit s: tile s holds real tokens
-    int tA;
-  };
-  auto tile_base = [&](int tile, bool& v, int64_t& cbase, int64_t& sbase) {
-    const int tl = min(tile, t_end - 1);
-    const int page = __builtin_amdgcn_readfirstlane(sm_pg[tl / tpp - fp]);
-    v = tile < t_end && (unsigned)page < (unsigned)a.num_pages;
-    const int64_t pg = v ? page : 0;
-    const int sub = tl - (tl / tpp) * tpp;
-    cbase = pg * page_codes + (int64_t)sub * kTileCodes;
-    sbase = pg * page_scales + (int64_t)sub * kTileScales;
-  };
-  // loads of one step: issued one step ahead and unconditionally (a missing
-  // tile reads an in-pool stand-in and is masked), so waits are exact
-  auto issue = [&](int pr, Step& S) {
-    const int tA = t_begin + 2 * pr;
-    S.tA = tA;
+  // tile cursor: page slot and tile within the page of the next tile to load
+  // (advanced tile by tile, so no division sits in the step loop)
+  int cur_tile = t_begin, cur_pg = 0, cur_sub = t_begin - fp * tpp;
+  // loads of one step, issued ahead and unconditionally: a tile past the
+  // split or on an out-of-pool page reads page 0 instead and is masked, so
+  // every wait count stays static
+  auto issue = [&](Step& S) {
+    S.tA = cur_tile;
     int ok = 0;
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      bool v;
-      int64_t cb, sb;
-      tile_base(tA + s2, v, cb, sb);
-      ok |= (int)v << s2;
-      S.t[s2].v = __builtin_bit_cast(uint2, __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(
-                                                 a.codes + cb + 8 * ((wave * 4 + g) * 16 + col))));
-      S.t[s2].vs = __builtin_nontemporal_load(
-          reinterpret_cast<const uint32_t*>(a.scales + sb + 4 * ((wave * 4 + g) * 4 + (col >> 2))));
-    }
-    {
-      bool v;
-      int64_t cb, sb;
-      tile_base(tA + r_tile, v, cb, sb);
-      S.r = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(a.codes + cb + 4096 + 2 * (r_item & 255)));
-      S.rs = a.scales[sb + 512 + 4 * (r_g * 4 + (r_i >> 2)) + r_tt];
+    for (int s = 0; s < kStepTiles; ++s) {
+      const int slot = min(cur_pg, n_pg - 1);
+      const int page = __builtin_amdgcn_readfirstlane(sm_pg[slot]);
+      const bool v = cur_tile < t_end && (unsigned)page < (unsigned)a.num_pages;
+      ok |= (int)v << s;
+      const int64_t pg = v ? page : 0;
+      const int sub = v ? cur_sub : 0;
+      const auto rc = tile_rsrc(a.codes + pg * page_codes + (int64_t)sub * kTileCodes, kTileCodes);
+      const auto rs = tile_rsrc(a.scales + pg * page_scales + (int64_t)sub * kTileScales, kTileScales);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int grp = 2 * wave + j;
+        S.v[s][j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rc, 8 * ((grp * 4 + g) * 16 + col), 0, 0));
+        S.vs[s][j] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * ((grp * 4 + g) * 4 + (col >> 2)), 0, 0);
+      }
+      S.r[s] = __builtin_amdgcn_raw_buffer_load_b16(rc, 4096 + 2 * r_item, 0, 0);
+      S.rs[s] = __builtin_amdgcn_raw_buffer_load_b8(rs, 512 + 4 * (r_g * 4 + (r_i >> 2)) + r_tt, 0, 0);
+      ++cur_tile;
+      if (++cur_sub == tpp) {
+        cur_sub = 0;
+        ++cur_pg;
+      }
     }
     S.ok = ok;
   };
 
-  f32x4 o[4][4];  // [V tile j][head block n]
+  f32x16 o[4][2];  // O^T accumulators [32-element block db][32-head block hb]
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int n = 0; n < 4; ++n) o[j][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf, l_run = 0.f;  // head 16*hb + col, this wave's token block
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][hb][i] = 0.f;
+  // head 32*hgp + r32: reference maximum, sums over this wave's token blocks
+  // of the fp16 weights (normalize the output) and of the unrounded weights
+  // (for the LSE)
+  float m_run = kNegInf, l_run = 0.f, e_run = 0.f;
 
-  auto compute = [&](Step& S) {
+  // 1. dequantize elements [128w, 128w+128) and a quarter of the rope group into the LDS K^ tile
+  auto dequant = [&](const Step& S, auto tail_tag) {
+    constexpr bool kTail = decltype(tail_tag)::value;
     const int tA = S.tA;
-    const bool tail = (tA + 2) * kTile > L || S.ok != 3;
-    // 1. dequantize the V slice (kept for PV) and the rope group into the LDS K^ tile
-    uint32_t x[2][4][2];  // [tile][token tt][pair k]: fp16 pairs, elements 4*col + 2k, +1
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      const int nvalid = tail ? (((S.ok >> s2) & 1) ? max(0, min(4, L - (tA + s2) * kTile - 4 * g)) : 0) : 4;
-      const uint32_t wlo = S.t[s2].v.x, whi = S.t[s2].v.y;  // tokens 0,1 | 2,3
+    for (int s = 0; s < kStepTiles; ++s) {
+      const int nvalid = kTail ? (((S.ok >> s) & 1) ? max(0, min(4, L - (tA + s) * kTile - 4 * g)) : 0) : 4;
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const uint32_t w = (tt < 2 ? wlo : whi) >> (16 * (tt & 1));
-        const uint32_t sc = e4m3_to_f16x2_bcast((S.t[s2].vs >> (8 * tt)) & 0xffu);
-        x[s2][tt][0] = pk_mul_f16(fp4x2_to_f16x2<0>(w), sc);
-        x[s2][tt][1] = pk_mul_f16(fp4x2_to_f16x2<1>(w), sc);
-        if (tt >= nvalid) x[s2][tt][0] = x[s2][tt][1] = 0u;
-        const int row = 16 * s2 + 4 * g + tt;
-        *reinterpret_cast<uint2*>(sm_k + row * kKRow + 2 * (64 * wave + 4 * col)) = make_uint2(x[s2][tt][0], x[s2][tt][1]);
+      for (int j = 0; j < 2; ++j) {
+        uint2 x[4];
+        dequant16(S, s, j, x);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          if (kTail && tt >= nvalid) x[tt] = make_uint2(0u, 0u);
+          const int row = 16 * s + 4 * g + tt;
+          *reinterpret_cast<uint2*>(sm_k + row * kKRow + 2 * (64 * (2 * wave + j) + 4 * col)) = x[tt];
+        }
       }
-    }
-    {
-      const uint32_t sc = e4m3_to_f16x2_bcast(S.rs & 0xffu);
-      uint32_t r0 = pk_mul_f16(fp4x2_to_f16x2<0>(S.r), sc), r1 = pk_mul_f16(fp4x2_to_f16x2<1>(S.r), sc);
-      const int tok = (tA + r_tile) * kTile + 4 * r_g + r_tt;
-      if (tail && (!((S.ok >> r_tile) & 1) || tok >= L)) r0 = r1 = 0u;
-      const int row = 16 * r_tile + 4 * r_g + r_tt;
+      const f16x2 rsc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(S.rs[s], 1.0f, false);
+      const f16x2 rs2 = {rsc[0], rsc[0]};
+      uint32_t r0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(S.r[s], 1.0f, 0) * rs2);
+      uint32_t r1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(S.r[s], 1.0f, 1) * rs2);
+      if (kTail) {
+        const int tok = (tA + s) * kTile + 4 * r_g + r_tt;
+        if (!((S.ok >> s) & 1) || tok >= L) r0 = r1 = 0u;
+      }
+      const int row = 16 * s + 4 * r_g + r_tt;
       *reinterpret_cast<uint2*>(sm_k + row * kKRow + 2 * (512 + 4 * r_i)) = make_uint2(r0, r1);
-    }
-    __syncthreads();
-
-    // 2. scores: heads 16hb + col, tokens 16tb + 4g + i
-    float s[4];
-    {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const uint8_t* krow = sm_k + (16 * tb + col) * kKRow + 16 * g;
-      const uint8_t* qrow2 = sm_q + (16 * hb + col) * kKRow + 16 * g;
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
-        const f16x8 ka = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(krow + 64 * ks));
-        const f16x8 qb = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(qrow2 + 64 * ks));
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb, acc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s[i] = acc[i] * sscale;
-    }
-    if (tail) {
-      const int tok0 = (tA + tb) * kTile + 4 * g;
-      const int nvalid = ((S.ok >> tb) & 1) ? max(0, min(4, L - tok0)) : 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (i >= nvalid) s[i] = kNegInf;
-    }
-    float mx = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    mx = fmaxf(mx, shfl_xor_f32(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f32(mx, 32));
-    if (g == 0) sm_mx[tb][16 * hb + col] = mx;
-    __syncthreads();
-    mx = fmaxf(mx, sm_mx[tb ^ 1][16 * hb + col]);
-    const float m_new = fmaxf(m_run, mx);
-    const float mb2 = (m_new == kNegInf) ? 0.f : m_new - kPBias;
-    const float alpha = (m_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(s[i] - mb2);
-    l_run = l_run * alpha + (p[0] + p[1]) + (p[2] + p[3]);
-    m_run = m_new;
-    // P^T row of head 16hb + col: K order [tile A 4g..4g+3, tile B 4g..4g+3]
-    *reinterpret_cast<uint2*>(sm_p + (16 * hb + col) * kPRow + 16 * g + 8 * tb) =
-        make_uint2(pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]));
-    if (g == 0 && tb == 0) sm_alpha[16 * hb + col] = alpha;
-    __syncthreads();
-
-    // 3. O^T[d][h] += V^T[d][t] P^T[t][h]: elements 64w + 4*row + j, all 64 heads
-    {
-      float al[4];
-      bool need = false;
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        al[n] = sm_alpha[16 * n + col];
-        need |= al[n] != 1.0f;
-      }
-      if (__any(need)) {  // once the running maxima settle, most steps skip this
-#pragma unroll
-        for (int n = 0; n < 4; ++n)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) o[j][n] *= al[n];
-      }
-    }
-    f16x8 pb[4];
-#pragma unroll
-    for (int n = 0; n < 4; ++n)
-      pb[n] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(sm_p + (16 * n + col) * kPRow + 16 * g));
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      u32x4 lo = {lo_halves(x[0][0][k], x[0][1][k]), lo_halves(x[0][2][k], x[0][3][k]),
-                  lo_halves(x[1][0][k], x[1][1][k]), lo_halves(x[1][2][k], x[1][3][k])};
-      u32x4 hi = {hi_halves(x[0][0][k], x[0][1][k]), hi_halves(x[0][2][k], x[0][3][k]),
-                  hi_halves(x[1][0][k], x[1][1][k]), hi_halves(x[1][2][k], x[1][3][k])};
-      const f16x8 vlo = __builtin_bit_cast(f16x8, lo), vhi = __builtin_bit_cast(f16x8, hi);
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        o[2 * k][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vlo, pb[n], o[2 * k][n], 0, 0, 0);
-        o[2 * k + 1][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vhi, pb[n], o[2 * k + 1][n], 0, 0, 0);
-      }
     }
   };
 
-  // Steps are prefetched three ahead through a ring of registers. One
-  // workgroup per CU steps through the tiles in lockstep, so a single step
-  // in flight (~10 KB) cannot cover HBM latency. The loads of the last few
-  // ring slots may run past the split: they read in-pool stand-ins (masked,
-  // never computed), which keeps every wait count in the loop static.
-  const int nsteps = (t_end - t_begin + 1) >> 1;
+  auto attend = [&](const int tA, const int ok) {
+    const bool tail = (tA + kStepTiles) * kTile > L || ok != (1 << kStepTiles) - 1;
+    __syncthreads();
+
+    // 2. partial scores S^T[token 32tb + i][head 32hgp + r32] over this wave's half of the elements
+    f32x16 sc[2];
+    {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc[0][i] = sc[1][i] = 0.f;
+      const uint8_t* krow = sm_k + r32 * kKRow + 576 * kh + 16 * hh;
+      constexpr int kDepth = 4;  // K^ fragments (both token blocks) read ahead of their MFMAs
+      f16x8 ka[kDepth][2];
+      auto rd = [&](int ks) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          ka[ks % kDepth][t] =
+              __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(krow + 32 * t * kKRow + 32 * ks));
+      };
+#pragma unroll
+      for (int ks = 0; ks < kDepth - 1; ++ks) rd(ks);
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks) {
+        if (ks + kDepth - 1 < 18) rd(ks + kDepth - 1);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[ks % kDepth][t], qf[ks], sc[t], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (kDepth - 1), 0);
+#pragma unroll
+      for (int i = 0; i < 36 - 2 * (kDepth - 1); ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * (kDepth - 1), 0);
+    }
+    // publish the partial scores for the other half's wave, add its partials
+    float* s_mine = sm_s + ((hgp * 2 + kh) * 2) * 4 * 64 * 4;
+    const float* s_other = sm_s + ((hgp * 2 + (kh ^ 1)) * 2) * 4 * 64 * 4;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4*>(s_mine + ((t * 4 + q) * 64 + lane) * 4) =
+            f32x4{sc[t][4 * q], sc[t][4 * q + 1], sc[t][4 * q + 2], sc[t][4 * q + 3]};
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 o4 = *reinterpret_cast<const f32x4*>(s_other + ((t * 4 + q) * 64 + lane) * 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[t][4 * q + i] = (sc[t][4 * q + i] + o4[i]) * sscale;
+      }
+    // lane value v of block t holds token 32t + 8(v/4) + 4hh + v%4 of the step
+    if (tail) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int tl = 32 * t + 8 * (v >> 2) + 4 * hh + (v & 3);
+          if (!((ok >> (tl >> 4)) & 1) || tA * kTile + tl >= L) sc[t][v] = kNegInf;
+        }
+    }
+    float mx = sc[0][0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[0][v]);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[1][v]);
+    mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+    const int hl = 32 * hgp + r32;
+    {
+      // the reference maximum only moves when a score exceeds it by more
+      // than 2^kSlack, so the rescale of the accumulators below is rare; P
+      // then stays <= 2^(kSlack + kPBias) = 2^15 in fp16. Both waves of the
+      // head block see the same scores, so they take the same decisions.
+      const bool move = mx > m_run + kSlack;
+      const float m_new = move ? mx : m_run;
+      const float mb2 = (m_new == kNegInf) ? 0.f : m_new - kPBias;
+      const float alpha = move ? ((m_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new)) : 1.0f;
+      // this wave turns the token block t = kh into P
+      const f32x16 sk = kh ? sc[1] : sc[0];
+      float p[16];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(sk[v] - mb2);
+      uint32_t pk[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pk[i] = pack_f16x2(p[2 * i], p[2 * i + 1]);
+      // the normalizer sums the fp16-rounded weights the PV products use, so
+      // the output stays an exact weighted average of V whatever the rounding
+      float ls = 0.f, es = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ls += f16_lo(pk[i]) + f16_hi(pk[i]);
+        es += p[2 * i] + p[2 * i + 1];
+      }
+      l_run = l_run * alpha + ls;
+      e_run = e_run * alpha + es;
+      m_run = m_new;
+      // values 8m..8m+7 are the B operand of PV k step 2kh + m, head block hgp, this lane
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        *reinterpret_cast<u32x4*>(sm_p + (((2 * kh + m) * 2 + hgp) * 64 + lane) * 16) =
+            u32x4{pk[4 * m], pk[4 * m + 1], pk[4 * m + 2], pk[4 * m + 3]};
+      if (kh == 0 && hh == 0) sm_alpha[hl] = alpha;
+    }
+    __syncthreads();
+
+    // 4. O^T[d][h] += V^T[d][t] P^T[t][h]: d = 128w + 32db + row, heads 32hb + r32
+    {
+      float al[2];
+      bool need = false;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        al[hb] = sm_alpha[32 * hb + r32];
+        need |= al[hb] != 1.0f;
+      }
+      if (__any(need)) {  // the reference maxima rarely move after the first steps
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) o[db][hb] *= al[hb];
+      }
+    }
+    // k step kk = 2tb' + m covers tokens 32tb' + 16m + 8r + 4hh + e (r = 0,1; e = 0..3)
+    // for the lanes of k half hh. ds_read_b64_tr_b16: in each 16-lane group,
+    // lane i receives element i%4 of the 8-byte reads of lanes i/4 + 4e
+    // (e = 0..3); lane 4e + c therefore addresses token row e, elements
+    // D + 4c, and lane i gets element D + i of rows 0..3.
+    const int tr_e = col >> 2, tr_c = col & 3;
+    const uint8_t* vbase = sm_k + (4 * hh + tr_e) * kKRow + 2 * (128 * wave + 16 * ((lane >> 4) & 1) + 4 * tr_c);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      f16x8 pb[2];
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+        pb[hb] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(sm_p + ((kk * 2 + hb) * 64 + lane) * 16));
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const uint8_t* vp = vbase + (16 * kk) * kKRow + 2 * 32 * db;
+        const u32x2 lo = lds_read_tr16(vp);               // tokens +0..3
+        const u32x2 hi = lds_read_tr16(vp + 8 * kKRow);   // tokens +8..11
+        const f16x8 va = __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) o[db][hb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pb[hb], o[db][hb], 0, 0, 0);
+      }
+    }
+    __syncthreads();  // the next step overwrites the K^ tile
+  };
+
+  // One step of loads is in flight while the previous step is scored and
+  // accumulated: the raw registers are refilled right after they have been
+  // dequantized into LDS. The last step's loads run past the split; they read
+  // in-pool stand-ins that are never used, which keeps every wait static.
+  const int nsteps = (t_end - t_begin + kStepTiles - 1) / kStepTiles;
   {
-    Step R0, R1, R2, R3;
-    issue(0, R0);
-    issue(1, R1);
-    issue(2, R2);
-    for (int st = 0;; st += 4) {
-      issue(st + 3, R3);
-      compute(R0);
-      if (st + 1 >= nsteps) break;
-      issue(st + 4, R0);
-      compute(R1);
-      if (st + 2 >= nsteps) break;
-      issue(st + 5, R1);
-      compute(R2);
-      if (st + 3 >= nsteps) break;
-      issue(st + 6, R2);
-      compute(R3);
-      if (st + 4 >= nsteps) break;
+    Step R;
+    issue(R);
+    for (int st = 0; st < nsteps; ++st) {
+      const int tA = R.tA, ok = R.ok;
+      const bool tail = (tA + kStepTiles) * kTile > L || ok != (1 << kStepTiles) - 1;
+      if (tail)
+        dequant(R, std::true_type{});
+      else
+        dequant(R, std::false_type{});
+      issue(R);
+      attend(tA, ok);
     }
   }
 
   // ---- epilogue: normalize and write this split's partial (or the output) ----
-  l_run += shfl_xor_f32(l_run, 16);
   l_run += shfl_xor_f32(l_run, 32);
-  if (g == 0) {
-    sm_l[tb][16 * hb + col] = l_run;
-    if (tb == 0) sm_m[16 * hb + col] = m_run;
+  e_run += shfl_xor_f32(e_run, 32);
+  if (hh == 0) {
+    sm_l[kh][32 * hgp + r32] = l_run;
+    sm_e[kh][32 * hgp + r32] = e_run;
+    if (kh == 0) sm_m[32 * hgp + r32] = m_run;
   }
   __syncthreads();
   const float g_scale = a.g_scale[0];
   const bool direct = a.num_splits == 1;
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
-    const int hl = 16 * n + col;
+  for (int hb = 0; hb < 2; ++hb) {
+    const int hl = 32 * hb + r32;
     const float lsum = sm_l[0][hl] + sm_l[1][hl];
     const float inv = lsum > 0.f ? g_scale / lsum : 0.f;
     const int64_t hq = (int64_t)b * a.hq + h0 + hl;
     float* dst = direct ? a.out + hq * kDv : a.ws_o + (hq * a.num_splits + split) * kDv;
+    // value v of accumulator (db, hb): element 128w + 32db + 8(v/4) + 4hh + v%4
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float4 v4 = make_float4(o[0][n][r] * inv, o[1][n][r] * inv, o[2][n][r] * inv, o[3][n][r] * inv);
-      *reinterpret_cast<float4*>(dst + 64 * wave + 4 * (4 * g + r)) = v4;
-    }
-    if (wave == 0 && g == 0) {
-      const float lse2 = lsum > 0.f ? sm_m[hl] + __log2f(lsum) - kPBias : kNegInf;
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float4 v4 = make_float4(o[db][hb][4 * q] * inv, o[db][hb][4 * q + 1] * inv, o[db][hb][4 * q + 2] * inv,
+                                o[db][hb][4 * q + 3] * inv);
+        *reinterpret_cast<float4*>(dst + 128 * wave + 32 * db + 8 * q + 4 * hh) = v4;
+      }
+    if (wave == 0 && hh == 0) {
+      const float esum = sm_e[0][hl] + sm_e[1][hl];
+      const float lse2 = esum > 0.f ? sm_m[hl] + __log2f(esum) - kPBias : kNegInf;
       if (direct) {
         if (a.lse) a.lse[hq] = lse2 * kLn2;
       } else {

@@ -99,20 +99,23 @@ SplitPlan plan_gqa(int batch, int hkv, int max_len) {
   return {(int)tps, (int)ns};
 }
 
-// MLA: one workgroup per (sequence, split, 64-head group), one per CU; about
-// two rounds of 256 workgroups.
-SplitPlan plan_mla(int batch, int hq, int max_len) {
+// MLA: one workgroup (4 waves) per (sequence, split, 64-head group) and one
+// per CU, so the default target is one round of 256 workgroups; each split
+// is an even number of 16-token tiles whose pages fit the LDS page-id stage.
+SplitPlan plan_mla(int batch, int hq, int max_len, int page_size) {
   const int ntiles = (max_len + kvq::kTile - 1) / kvq::kTile;
+  const int tpp = page_size / kvq::kTile;
   const int64_t units = (int64_t)batch * (hq / 64);
-  int64_t target = 512;
+  int64_t target = 256;
   if (const char* e = getenv("KVQ_DECODE_TARGET_WGS")) {
     const long v = strtol(e, nullptr, 10);
     if (v >= 1 && v <= (1 << 20)) target = v;
   }
+  const int64_t cap = ((int64_t)(kvq::kMlaMaxSplitPages - 1) * tpp) & ~(int64_t)1;
   int64_t tps = units > 0 ? (ntiles * units + target - 1) / target : ntiles;
   if (tps < 4) tps = 4;
   tps = (tps + 1) & ~(int64_t)1;
-  if (tps > 1024) tps = 1024;
+  if (tps > cap) tps = cap;
   int64_t ns = ntiles > 0 ? (ntiles + tps - 1) / tps : 1;
   if (ns > 128) {
     ns = 128;
@@ -324,7 +327,7 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* c, int32_t batch, int32_t hq,
   if (c->desc.kind == KVQ_GQA)
     return workspace_for(plan_gqa(batch, c->desc.num_kv_heads, max_len), batch, hq, c->desc.v_dim).total;
   if (hq != 64 && hq != 128) return 0;
-  return workspace_for(plan_mla(batch, hq, max_len), batch, hq, c->desc.v_dim).total;
+  return workspace_for(plan_mla(batch, hq, max_len, c->desc.page_size), batch, hq, c->desc.v_dim).total;
 }
 
 int kvq_decode(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, const int32_t* page_table,
@@ -405,7 +408,9 @@ int kvq_decode(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, con
   // MLA
   if (hq != 64 && hq != 128) return KVQ_ERR_UNSUPPORTED;
   if (!k_scale) return KVQ_ERR_ARG;  // the NVFP4 global scale
-  const SplitPlan plan = plan_mla(batch, hq, max_len);
+  const SplitPlan plan = plan_mla(batch, hq, max_len, c->desc.page_size);
+  // pages one split touches, whatever its alignment to page boundaries
+  if ((plan.tiles_per_split - 1) / (P / kvq::kTile) + 2 > kvq::kMlaMaxSplitPages) return KVQ_ERR_UNSUPPORTED;
   const WsLayout wl = workspace_for(plan, batch, hq, d.v_dim);
   const size_t need = wl.total;
   if (need && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % kAlign)) return KVQ_ERR_SIZE;

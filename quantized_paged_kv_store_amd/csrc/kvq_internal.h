@@ -21,6 +21,7 @@ namespace kvq {
 constexpr int kTile = 16;      // tokens per tile inside a page
 constexpr int kWaves = 4;      // waves per decode workgroup
 constexpr int kAmaxBlocks = 1024;
+constexpr int kMlaMaxSplitPages = 1024;  // page ids one MLA split stages in LDS
 
 // ------------------------------------------------------- vector typedefs --
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
