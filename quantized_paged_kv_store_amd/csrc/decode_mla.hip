@@ -15,29 +15,28 @@
 //                 BF16 query exactly; 2^-s_h goes into the score scale)
 //   O^T[d][h] += V^T[d][t] . P^T[t][h]      v_mfma_f32_32x32x16_f16, P * 2^7
 // and g is factored out of both (applied to the scores and to the output).
-// The 32x32x16 shape is used throughout: on gfx950 it sustains close to the
-// matrix-core peak with two independent accumulators per wave, and its
-// operand pattern (32 rows x 16 B) reads LDS without bank conflicts.
+// The 32x32x16 shape sustains close to the matrix-core peak on gfx950 and
+// its operand pattern (32 rows x 16 B) reads LDS without bank conflicts.
 //
-// Workgroup = 4 waves, one per SIMD (each wave may hold 512 registers) = 64
-// query heads of one (sequence, context split); the two 64-head groups of a
-// split get block ids 8 apart, i.e. the same XCD, so the second reads the
-// latent tiles from that L2. A step covers 64 tokens (four 16-token tiles):
-//   1. every wave dequantizes elements [128w, 128w+128) and a quarter of the
-//      rope group of the 64 tokens into the LDS K^ tile (token-major, fp16);
-//   2. wave w scores heads 32(w&1)..+31 against all 64 tokens over half of
-//      the dot product (elements [288(w>>1), +288)): Q of those heads and
-//      elements stays in registers for the whole kernel (72 registers; the
-//      whole row would not fit beside the output accumulators). The two
-//      waves of a head block add each other's partial scores through LDS,
-//      so both hold the full scores and the same softmax state;
-//   3. each wave writes the P (fp16) of its 32-token half in the exact
-//      register layout of the PV B operand, so the PV waves read it back
-//      with conflict-free 16 B reads;
-//   4. wave w accumulates O^T for elements [128w, 128w+128) and all 64 heads.
-//      Its A operand (V^T: one element, 8 tokens per lane) is read straight
-//      from the token-major K^ tile with ds_read_b64_tr_b16, gfx950's
-//      transposing LDS read, so the latent is dequantized only once.
+// Workgroup = 8 waves, two per SIMD (one wave's LDS and matrix latencies
+// are covered by the other's work), = 64 query heads of one (sequence,
+// context split); the two 64-head groups of a split get block ids 8 apart,
+// i.e. the same XCD, so the second reads the latent tiles from that L2. A
+// step covers 64 tokens (four 16-token tiles); wave w:
+//   1. dequantizes elements [64w, 64w+64) and an eighth of the rope group of
+//      the 64 tokens into the LDS K^ tile (token-major, fp16);
+//   2. scores heads 32(w&1)..+31 against tokens 32(w>>2)..+31 over half of
+//      the dot product (elements [288((w>>1)&1), +288)); Q of those heads and
+//      elements stays in registers (72 registers). The two waves splitting a
+//      dot product add each other's partial scores through LDS; the two
+//      token halves exchange their block maxima;
+//   3. turns half of its (now complete) scores into P (fp16), written in the
+//      exact register layout of the PV B operand, so the PV waves read it
+//      back with conflict-free 16 B reads;
+//   4. accumulates O^T for elements [64w, 64w+64) and all 64 heads. Its A
+//      operand (V^T: one element, 8 tokens per lane) is read straight from
+//      the token-major K^ tile with ds_read_b64_tr_b16, gfx950's transposing
+//      LDS read, so the latent is dequantized once.
 #include <type_traits>
 
 #include "kvq_internal.h"
@@ -51,7 +50,8 @@ constexpr float kSlack = 8.0f;   // log2 headroom of the lazy reference maximum
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kDk = 576, kDv = 512;
 constexpr int kHeadsPerWG = 64;
-constexpr int kThreads = 256;
+constexpr int kWavesMla = 8;
+constexpr int kThreads = 64 * kWavesMla;
 constexpr int kStepTiles = 4;                 // 64 tokens per step
 constexpr int kStepTokens = kStepTiles * kTile;
 constexpr int kKRow = kDk * 2 + 16;           // bytes per token row of the LDS K^ tile (padded)
@@ -73,12 +73,12 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint8_t* p) {
 
 // raw per-lane bytes of one 64-token step
 struct Step {
-  uint2 v[kStepTiles][2];      // [tile][64-element group]: tokens 4g..4g+3, elements 4*col..+3 of the group
-  uint32_t vs[kStepTiles][2];  // their E4M3 block scales, one byte per token
-  uint32_t r[kStepTiles];      // rope codes of this lane's item (2 bytes) per tile
-  uint32_t rs[kStepTiles];     // rope scale byte per tile
-  int ok;                      // bit s: tile s holds real tokens
-  int tA;                      // first tile of the step
+  uint2 v[kStepTiles];      // [tile]: tokens 4g..4g+3, elements 4*col..+3 of this wave's group
+  uint32_t vs[kStepTiles];  // their E4M3 block scales, one byte per token
+  uint32_t r[2];            // rope codes of this lane's item (2 bytes) in two of the tiles
+  uint32_t rs[2];           // rope scale byte per such tile
+  int ok;                   // bit s: tile s holds real tokens
+  int tA;                   // first tile of the step
 };
 
 // buffer descriptor over one tile's bytes: loads past `bytes` return zero
@@ -87,13 +87,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base,
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, bytes, kRsrcWord3);
 }
 
-// fp16 values of elements 4*col .. 4*col+3 of group j, tokens 4g + tt (tt =
-// 0..3) of tile s: x[tt] = {elements 0,1 | elements 2,3}
-__device__ __forceinline__ void dequant16(const Step& S, int s, int j, uint2 (&x)[4]) {
-  const f16x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(S.vs[s][j], 1.0f, false);
-  const f16x2 s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(S.vs[s][j], 1.0f, true);
+// fp16 values of elements 4*col .. 4*col+3 of the wave's group, tokens 4g + tt
+// (tt = 0..3) of tile s: x[tt] = {elements 0,1 | elements 2,3}
+__device__ __forceinline__ void dequant16(const Step& S, int s, uint2 (&x)[4]) {
+  const f16x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(S.vs[s], 1.0f, false);
+  const f16x2 s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(S.vs[s], 1.0f, true);
   const f16x2 sc[4] = {f16x2{s01[0], s01[0]}, f16x2{s01[1], s01[1]}, f16x2{s23[0], s23[0]}, f16x2{s23[1], s23[1]}};
-  const uint32_t lo = S.v[s][j].x, hi = S.v[s][j].y;  // tokens 0,1 | 2,3
+  const uint32_t lo = S.v[s].x, hi = S.v[s].y;  // tokens 0,1 | 2,3
   const f16x2 c[8] = {__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo, 1.0f, 0), __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo, 1.0f, 1),
                       __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo, 1.0f, 2), __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(lo, 1.0f, 3),
                       __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(hi, 1.0f, 0), __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(hi, 1.0f, 1),
@@ -103,6 +103,10 @@ __device__ __forceinline__ void dequant16(const Step& S, int s, int j, uint2 (&x
     x[tt] = make_uint2(__builtin_bit_cast(uint32_t, c[2 * tt] * sc[tt]), __builtin_bit_cast(uint32_t, c[2 * tt + 1] * sc[tt]));
 }
 
+// kWholeSteps: every 64-token step lies inside one page (pages of a multiple
+// of 64 tokens, splits of a multiple of 4 tiles), so a step needs one page
+// lookup and one buffer descriptor; otherwise every tile is looked up.
+template <bool kWholeSteps>
 __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecodeArgs a) {
   // ---- block -> (sequence, split, head group); both head groups of a split share an XCD ----
   const int n_units = a.batch * a.num_splits;
@@ -115,7 +119,8 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, col = lane & 15;   // dequant role: token group, element quad
   const int r32 = lane & 31, hh = lane >> 5;  // MFMA role: row / column, k half
-  const int hgp = wave & 1, kh = wave >> 1;   // score role: 32-head block, half of the dot product
+  // score role: 32-head block, half of the dot product, 32-token block
+  const int hgp = wave & 1, kh = (wave >> 1) & 1, tb = wave >> 2;
 
   const int L = min(max(a.seq_lens[b], 0), a.max_len);
   const int ntiles = (L + kTile - 1) / kTile;
@@ -134,11 +139,12 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
   }
 
   __shared__ __attribute__((aligned(16))) uint8_t sm_k[kStepTokens * kKRow];
-  __shared__ __attribute__((aligned(16))) uint8_t sm_p[4 * 2 * 64 * 16];  // [k step][head block][lane][8 x fp16]
-  __shared__ __attribute__((aligned(16))) float sm_s[2 * 2 * 2 * 4 * 64 * 4];  // partial scores [hgp][kh][tb][quad][lane][4]
+  __shared__ __attribute__((aligned(16))) uint8_t sm_p[4 * 2 * 64 * 16];           // [k step][head block][lane][8 x fp16]
+  __shared__ __attribute__((aligned(16))) float sm_s[kWavesMla * 4 * 64 * 4];     // partial scores [wave][quad][lane][4]
+  __shared__ float sm_mx[2][kHeadsPerWG];
   __shared__ float sm_alpha[kHeadsPerWG];
-  __shared__ float sm_l[2][kHeadsPerWG];
-  __shared__ float sm_e[2][kHeadsPerWG];
+  __shared__ float sm_l[4][kHeadsPerWG];
+  __shared__ float sm_e[4][kHeadsPerWG];
   __shared__ float sm_m[kHeadsPerWG];
   __shared__ int sm_pg[kMlaMaxSplitPages];
 
@@ -148,7 +154,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
   const int32_t* pt = a.page_table + (int64_t)b * a.page_table_stride;
   for (int i = tid; i < n_pg; i += kThreads) sm_pg[i] = pt[fp + i];
 
-  // ---- Q of this wave's 32 heads, scaled by a per-head power of two, in registers ----
+  // ---- Q of this wave's 32 heads and half of the elements, per-head power-of-two scaled ----
   // B operand of step ks: head 32*hgp + r32, elements 288*kh + 16*ks + 8*hh .. +7
   f16x8 qf[18];
   float sscale;
@@ -185,8 +191,8 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
 
   const int64_t page_codes = (int64_t)a.page_size * (kDk / 2);
   const int64_t page_scales = (int64_t)a.page_size * (kDk / 16);
-  // rope item of this lane (per tile): token 4*r_g + r_tt, elements 512 + 4*r_i .. +3
-  const int r_item = wave * 64 + lane;
+  // rope item of this lane in tiles 2tb, 2tb+1: token 4*r_g + r_tt, elements 512 + 4*r_i .. +3
+  const int r_item = tid & 255;
   const int r_g = r_item >> 6, r_i = (r_item >> 2) & 15, r_tt = r_item & 3;
 
   // tile cursor: page slot and tile within the page of the next tile to load
@@ -198,67 +204,94 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
   auto issue = [&](Step& S) {
     S.tA = cur_tile;
     int ok = 0;
-#pragma unroll
-    for (int s = 0; s < kStepTiles; ++s) {
+    if constexpr (kWholeSteps) {
       const int slot = min(cur_pg, n_pg - 1);
       const int page = __builtin_amdgcn_readfirstlane(sm_pg[slot]);
-      const bool v = cur_tile < t_end && (unsigned)page < (unsigned)a.num_pages;
-      ok |= (int)v << s;
-      const int64_t pg = v ? page : 0;
-      const int sub = v ? cur_sub : 0;
-      const auto rc = tile_rsrc(a.codes + pg * page_codes + (int64_t)sub * kTileCodes, kTileCodes);
-      const auto rs = tile_rsrc(a.scales + pg * page_scales + (int64_t)sub * kTileScales, kTileScales);
+      const bool pv = (unsigned)page < (unsigned)a.num_pages;
+      const int64_t pg = pv ? page : 0;
+      const int sub = pv ? cur_sub : 0;
+      const auto rc = tile_rsrc(a.codes + pg * page_codes + (int64_t)sub * kTileCodes, kStepTiles * kTileCodes);
+      const auto rs = tile_rsrc(a.scales + pg * page_scales + (int64_t)sub * kTileScales, kStepTiles * kTileScales);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int grp = 2 * wave + j;
-        S.v[s][j] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rc, 8 * ((grp * 4 + g) * 16 + col), 0, 0));
-        S.vs[s][j] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * ((grp * 4 + g) * 4 + (col >> 2)), 0, 0);
+      for (int s = 0; s < kStepTiles; ++s) {
+        ok |= (int)(pv && cur_tile + s < t_end) << s;
+        S.v[s] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rc, 8 * ((wave * 4 + g) * 16 + col), s * kTileCodes, 0));
+        S.vs[s] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * ((wave * 4 + g) * 4 + (col >> 2)), s * kTileScales, 0);
       }
-      S.r[s] = __builtin_amdgcn_raw_buffer_load_b16(rc, 4096 + 2 * r_item, 0, 0);
-      S.rs[s] = __builtin_amdgcn_raw_buffer_load_b8(rs, 512 + 4 * (r_g * 4 + (r_i >> 2)) + r_tt, 0, 0);
-      ++cur_tile;
-      if (++cur_sub == tpp) {
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int s = 2 * tb + s2;
+        S.r[s2] = __builtin_amdgcn_raw_buffer_load_b16(rc, 4096 + 2 * r_item, s * kTileCodes, 0);
+        S.rs[s2] = __builtin_amdgcn_raw_buffer_load_b8(rs, 512 + 4 * (r_g * 4 + (r_i >> 2)) + r_tt, s * kTileScales, 0);
+      }
+      cur_tile += kStepTiles;
+      cur_sub += kStepTiles;
+      if (cur_sub == tpp) {
         cur_sub = 0;
         ++cur_pg;
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < kStepTiles; ++s) {
+        const int slot = min(cur_pg, n_pg - 1);
+        const int page = __builtin_amdgcn_readfirstlane(sm_pg[slot]);
+        const bool v = cur_tile < t_end && (unsigned)page < (unsigned)a.num_pages;
+        ok |= (int)v << s;
+        const int64_t pg = v ? page : 0;
+        const int sub = v ? cur_sub : 0;
+        const auto rc = tile_rsrc(a.codes + pg * page_codes + (int64_t)sub * kTileCodes, kTileCodes);
+        const auto rs = tile_rsrc(a.scales + pg * page_scales + (int64_t)sub * kTileScales, kTileScales);
+        S.v[s] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rc, 8 * ((wave * 4 + g) * 16 + col), 0, 0));
+        S.vs[s] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * ((wave * 4 + g) * 4 + (col >> 2)), 0, 0);
+        if ((s >> 1) == tb) {  // uniform per wave
+          S.r[s & 1] = __builtin_amdgcn_raw_buffer_load_b16(rc, 4096 + 2 * r_item, 0, 0);
+          S.rs[s & 1] = __builtin_amdgcn_raw_buffer_load_b8(rs, 512 + 4 * (r_g * 4 + (r_i >> 2)) + r_tt, 0, 0);
+        }
+        ++cur_tile;
+        if (++cur_sub == tpp) {
+          cur_sub = 0;
+          ++cur_pg;
+        }
       }
     }
     S.ok = ok;
   };
 
-  f32x16 o[4][2];  // O^T accumulators [32-element block db][32-head block hb]
+  f32x16 o[2][2];  // O^T accumulators [32-element block db][32-head block hb]
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 2; ++db)
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[db][hb][i] = 0.f;
-  // head 32*hgp + r32: reference maximum, sums over this wave's token blocks
-  // of the fp16 weights (normalize the output) and of the unrounded weights
+  // head 32*hgp + r32: reference maximum, sums over this wave's P values of
+  // the fp16 weights (normalize the output) and of the unrounded weights
   // (for the LSE)
   float m_run = kNegInf, l_run = 0.f, e_run = 0.f;
 
-  // 1. dequantize elements [128w, 128w+128) and a quarter of the rope group into the LDS K^ tile
+  // 1. dequantize elements [64w, 64w+64) and an eighth of the rope group into the LDS K^ tile
   auto dequant = [&](const Step& S, auto tail_tag) {
     constexpr bool kTail = decltype(tail_tag)::value;
     const int tA = S.tA;
 #pragma unroll
     for (int s = 0; s < kStepTiles; ++s) {
       const int nvalid = kTail ? (((S.ok >> s) & 1) ? max(0, min(4, L - (tA + s) * kTile - 4 * g)) : 0) : 4;
+      uint2 x[4];
+      dequant16(S, s, x);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        uint2 x[4];
-        dequant16(S, s, j, x);
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          if (kTail && tt >= nvalid) x[tt] = make_uint2(0u, 0u);
-          const int row = 16 * s + 4 * g + tt;
-          *reinterpret_cast<uint2*>(sm_k + row * kKRow + 2 * (64 * (2 * wave + j) + 4 * col)) = x[tt];
-        }
+      for (int tt = 0; tt < 4; ++tt) {
+        if (kTail && tt >= nvalid) x[tt] = make_uint2(0u, 0u);
+        const int row = 16 * s + 4 * g + tt;
+        *reinterpret_cast<uint2*>(sm_k + row * kKRow + 2 * (64 * wave + 4 * col)) = x[tt];
       }
-      const f16x2 rsc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(S.rs[s], 1.0f, false);
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int s = 2 * tb + s2;
+      const f16x2 rsc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(S.rs[s2], 1.0f, false);
       const f16x2 rs2 = {rsc[0], rsc[0]};
-      uint32_t r0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(S.r[s], 1.0f, 0) * rs2);
-      uint32_t r1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(S.r[s], 1.0f, 1) * rs2);
+      uint32_t r0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(S.r[s2], 1.0f, 0) * rs2);
+      uint32_t r1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(S.r[s2], 1.0f, 1) * rs2);
       if (kTail) {
         const int tok = (tA + s) * kTile + 4 * r_g + r_tt;
         if (!((S.ok >> s) & 1) || tok >= L) r0 = r1 = 0u;
@@ -272,110 +305,93 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
     const bool tail = (tA + kStepTiles) * kTile > L || ok != (1 << kStepTiles) - 1;
     __syncthreads();
 
-    // 2. partial scores S^T[token 32tb + i][head 32hgp + r32] over this wave's half of the elements
-    f32x16 sc[2];
+    // 2. partial scores S^T[token 32tb + i][head 32hgp + r32] over elements [288kh, +288)
+    f32x16 sc;
     {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sc[0][i] = sc[1][i] = 0.f;
-      const uint8_t* krow = sm_k + r32 * kKRow + 576 * kh + 16 * hh;
-      constexpr int kDepth = 4;  // K^ fragments (both token blocks) read ahead of their MFMAs
-      f16x8 ka[kDepth][2];
-      auto rd = [&](int ks) {
+      for (int i = 0; i < 16; ++i) sc[i] = 0.f;
+      const uint8_t* krow = sm_k + (32 * tb + r32) * kKRow + 576 * kh + 16 * hh;
+      constexpr int kDepth = 4;  // K^ fragments read ahead of their MFMAs
+      f16x8 ka[kDepth];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-          ka[ks % kDepth][t] =
-              __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(krow + 32 * t * kKRow + 32 * ks));
-      };
-#pragma unroll
-      for (int ks = 0; ks < kDepth - 1; ++ks) rd(ks);
+      for (int ks = 0; ks < kDepth - 1; ++ks) ka[ks] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(krow + 32 * ks));
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
-        if (ks + kDepth - 1 < 18) rd(ks + kDepth - 1);
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[ks % kDepth][t], qf[ks], sc[t], 0, 0, 0);
+        if (ks + kDepth - 1 < 18)
+          ka[(ks + kDepth - 1) % kDepth] =
+              __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(krow + 32 * (ks + kDepth - 1)));
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[ks % kDepth], qf[ks], sc, 0, 0, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (kDepth - 1), 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, kDepth - 1, 0);
 #pragma unroll
-      for (int i = 0; i < 36 - 2 * (kDepth - 1); ++i) {
+      for (int i = 0; i < 18 - (kDepth - 1); ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2 * (kDepth - 1), 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, kDepth - 1, 0);
     }
-    // publish the partial scores for the other half's wave, add its partials
-    float* s_mine = sm_s + ((hgp * 2 + kh) * 2) * 4 * 64 * 4;
-    const float* s_other = sm_s + ((hgp * 2 + (kh ^ 1)) * 2) * 4 * 64 * 4;
+    // publish the partial scores for the wave holding the other half of the dot product
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<f32x4*>(s_mine + ((t * 4 + q) * 64 + lane) * 4) =
-            f32x4{sc[t][4 * q], sc[t][4 * q + 1], sc[t][4 * q + 2], sc[t][4 * q + 3]};
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<f32x4*>(sm_s + ((wave * 4 + q) * 64 + lane) * 4) =
+          f32x4{sc[4 * q], sc[4 * q + 1], sc[4 * q + 2], sc[4 * q + 3]};
     __syncthreads();
+    // both waves add the same two partials, so they hold identical scores
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 o4 = *reinterpret_cast<const f32x4*>(sm_s + (((wave ^ 2) * 4 + q) * 64 + lane) * 4);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 o4 = *reinterpret_cast<const f32x4*>(s_other + ((t * 4 + q) * 64 + lane) * 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc[t][4 * q + i] = (sc[t][4 * q + i] + o4[i]) * sscale;
-      }
-    // lane value v of block t holds token 32t + 8(v/4) + 4hh + v%4 of the step
-    if (tail) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int tl = 32 * t + 8 * (v >> 2) + 4 * hh + (v & 3);
-          if (!((ok >> (tl >> 4)) & 1) || tA * kTile + tl >= L) sc[t][v] = kNegInf;
-        }
+      for (int i = 0; i < 4; ++i) sc[4 * q + i] += o4[i];
     }
-    float mx = sc[0][0];
+    // lane value v holds token 32tb + 8(v/4) + 4hh + v%4 of the step
+    if (__builtin_expect(tail, 0)) {
 #pragma unroll
-    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[0][v]);
+      for (int v = 0; v < 16; ++v) {
+        const int tl = 32 * tb + 8 * (v >> 2) + 4 * hh + (v & 3);
+        if (!((ok >> (tl >> 4)) & 1) || tA * kTile + tl >= L) sc[v] = kNegInf;
+      }
+    }
+    float mx = sc[0];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[1][v]);
-    mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[v]);
+    mx = fmaxf(mx, shfl_xor_f32(mx, 32)) * sscale;
     const int hl = 32 * hgp + r32;
+    if (kh == 0 && hh == 0) sm_mx[tb][hl] = mx;
+    __syncthreads();
     {
+      mx = fmaxf(mx, sm_mx[tb ^ 1][hl]);
       // the reference maximum only moves when a score exceeds it by more
       // than 2^kSlack, so the rescale of the accumulators below is rare; P
-      // then stays <= 2^(kSlack + kPBias) = 2^15 in fp16. Both waves of the
-      // head block see the same scores, so they take the same decisions.
+      // then stays <= 2^(kSlack + kPBias) = 2^15 in fp16. The four waves of
+      // a head block see the same maxima and take the same decisions.
       const bool move = mx > m_run + kSlack;
       const float m_new = move ? mx : m_run;
       const float mb2 = (m_new == kNegInf) ? 0.f : m_new - kPBias;
       const float alpha = move ? ((m_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new)) : 1.0f;
-      // this wave turns the token block t = kh into P
-      const f32x16 sk = kh ? sc[1] : sc[0];
-      float p[16];
+      // this wave turns values 8kh..8kh+7 into P: the B operand of PV k step 2tb + kh
+      float p[8];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) p[v] = __builtin_amdgcn_exp2f(sk[v] - mb2);
-      uint32_t pk[8];
+      for (int u = 0; u < 8; ++u) p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(kh ? sc[8 + u] : sc[u], sscale, -mb2));
+      uint32_t pk[4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pk[i] = pack_f16x2(p[2 * i], p[2 * i + 1]);
+      for (int i = 0; i < 4; ++i) pk[i] = pack_f16x2(p[2 * i], p[2 * i + 1]);
       // the normalizer sums the fp16-rounded weights the PV products use, so
       // the output stays an exact weighted average of V whatever the rounding
       float ls = 0.f, es = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < 4; ++i) {
         ls += f16_lo(pk[i]) + f16_hi(pk[i]);
         es += p[2 * i] + p[2 * i + 1];
       }
       l_run = l_run * alpha + ls;
       e_run = e_run * alpha + es;
       m_run = m_new;
-      // values 8m..8m+7 are the B operand of PV k step 2kh + m, head block hgp, this lane
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-        *reinterpret_cast<u32x4*>(sm_p + (((2 * kh + m) * 2 + hgp) * 64 + lane) * 16) =
-            u32x4{pk[4 * m], pk[4 * m + 1], pk[4 * m + 2], pk[4 * m + 3]};
-      if (kh == 0 && hh == 0) sm_alpha[hl] = alpha;
+      *reinterpret_cast<u32x4*>(sm_p + (((2 * tb + kh) * 2 + hgp) * 64 + lane) * 16) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+      if (kh == 0 && tb == 0 && hh == 0) sm_alpha[hl] = alpha;
     }
     __syncthreads();
 
-    // 4. O^T[d][h] += V^T[d][t] P^T[t][h]: d = 128w + 32db + row, heads 32hb + r32
+    // 4. O^T[d][h] += V^T[d][t] P^T[t][h]: d = 64w + 32db + row, heads 32hb + r32
     {
       float al[2];
       bool need = false;
@@ -386,7 +402,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
       }
       if (__any(need)) {  // the reference maxima rarely move after the first steps
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+        for (int db = 0; db < 2; ++db)
 #pragma unroll
           for (int hb = 0; hb < 2; ++hb) o[db][hb] *= al[hb];
       }
@@ -397,7 +413,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
     // (e = 0..3); lane 4e + c therefore addresses token row e, elements
     // D + 4c, and lane i gets element D + i of rows 0..3.
     const int tr_e = col >> 2, tr_c = col & 3;
-    const uint8_t* vbase = sm_k + (4 * hh + tr_e) * kKRow + 2 * (128 * wave + 16 * ((lane >> 4) & 1) + 4 * tr_c);
+    const uint8_t* vbase = sm_k + (4 * hh + tr_e) * kKRow + 2 * (64 * wave + 16 * ((lane >> 4) & 1) + 4 * tr_c);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       f16x8 pb[2];
@@ -405,7 +421,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
       for (int hb = 0; hb < 2; ++hb)
         pb[hb] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(sm_p + ((kk * 2 + hb) * 64 + lane) * 16));
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
+      for (int db = 0; db < 2; ++db) {
         const uint8_t* vp = vbase + (16 * kk) * kKRow + 2 * 32 * db;
         const u32x2 lo = lds_read_tr16(vp);               // tokens +0..3
         const u32x2 hi = lds_read_tr16(vp + 8 * kKRow);   // tokens +8..11
@@ -441,9 +457,9 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
   l_run += shfl_xor_f32(l_run, 32);
   e_run += shfl_xor_f32(e_run, 32);
   if (hh == 0) {
-    sm_l[kh][32 * hgp + r32] = l_run;
-    sm_e[kh][32 * hgp + r32] = e_run;
-    if (kh == 0) sm_m[32 * hgp + r32] = m_run;
+    sm_l[2 * tb + kh][32 * hgp + r32] = l_run;
+    sm_e[2 * tb + kh][32 * hgp + r32] = e_run;
+    if (kh == 0 && tb == 0) sm_m[32 * hgp + r32] = m_run;
   }
   __syncthreads();
   const float g_scale = a.g_scale[0];
@@ -451,21 +467,21 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     const int hl = 32 * hb + r32;
-    const float lsum = sm_l[0][hl] + sm_l[1][hl];
+    const float lsum = (sm_l[0][hl] + sm_l[1][hl]) + (sm_l[2][hl] + sm_l[3][hl]);
     const float inv = lsum > 0.f ? g_scale / lsum : 0.f;
     const int64_t hq = (int64_t)b * a.hq + h0 + hl;
     float* dst = direct ? a.out + hq * kDv : a.ws_o + (hq * a.num_splits + split) * kDv;
-    // value v of accumulator (db, hb): element 128w + 32db + 8(v/4) + 4hh + v%4
+    // value v of accumulator (db, hb): element 64w + 32db + 8(v/4) + 4hh + v%4
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 2; ++db)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float4 v4 = make_float4(o[db][hb][4 * q] * inv, o[db][hb][4 * q + 1] * inv, o[db][hb][4 * q + 2] * inv,
                                 o[db][hb][4 * q + 3] * inv);
-        *reinterpret_cast<float4*>(dst + 128 * wave + 32 * db + 8 * q + 4 * hh) = v4;
+        *reinterpret_cast<float4*>(dst + 64 * wave + 32 * db + 8 * q + 4 * hh) = v4;
       }
     if (wave == 0 && hh == 0) {
-      const float esum = sm_e[0][hl] + sm_e[1][hl];
+      const float esum = (sm_e[0][hl] + sm_e[1][hl]) + (sm_e[2][hl] + sm_e[3][hl]);
       const float lse2 = esum > 0.f ? sm_m[hl] + __log2f(esum) - kPBias : kNegInf;
       if (direct) {
         if (a.lse) a.lse[hq] = lse2 * kLn2;
@@ -483,6 +499,10 @@ hipError_t kvq_launch_decode_mla(const kvq_cache* c, const MlaDecodeArgs& a, hip
   (void)c;
   const int n_units = a.batch * a.num_splits;
   const int blocks = (n_units + 7) / 8 * 16;
-  kvq::decode_mla_kernel<<<blocks, kvq::kThreads, 0, s>>>(a);
+  const int tpp = a.page_size / kvq::kTile;
+  if (tpp % kvq::kStepTiles == 0 && a.tiles_per_split % kvq::kStepTiles == 0)
+    kvq::decode_mla_kernel<true><<<blocks, kvq::kThreads, 0, s>>>(a);
+  else
+    kvq::decode_mla_kernel<false><<<blocks, kvq::kThreads, 0, s>>>(a);
   return hipGetLastError();
 }

@@ -111,20 +111,26 @@ SplitPlan plan_mla(int batch, int hq, int max_len, int page_size) {
     const long v = strtol(e, nullptr, 10);
     if (v >= 1 && v <= (1 << 20)) target = v;
   }
-  const int64_t cap = ((int64_t)(kvq::kMlaMaxSplitPages - 1) * tpp) & ~(int64_t)1;
+  const int64_t cap = ((int64_t)(kvq::kMlaMaxSplitPages - 1) * tpp) & ~(int64_t)3;
   int64_t tps = units > 0 ? (ntiles * units + target - 1) / target : ntiles;
   if (tps < 4) tps = 4;
-  tps = (tps + 1) & ~(int64_t)1;
+  tps = (tps + 3) & ~(int64_t)3;  // whole 64-token steps
   if (tps > cap) tps = cap;
   int64_t ns = ntiles > 0 ? (ntiles + tps - 1) / tps : 1;
   if (ns > 128) {
     ns = 128;
     tps = (ntiles + ns - 1) / ns;
-    tps = (tps + 1) & ~(int64_t)1;
+    tps = (tps + 3) & ~(int64_t)3;
     ns = (ntiles + tps - 1) / tps;
   }
   if (ns < 1) ns = 1;
   return {(int)tps, (int)ns};
+}
+
+// Pages one MLA split touches at most (splits start at multiples of the split size).
+int64_t mla_split_pages(const SplitPlan& p, int page_size) {
+  const int64_t tpp = page_size / kvq::kTile, tps = p.tiles_per_split;
+  return tps % tpp == 0 ? tps / tpp : (tps - 1) / tpp + 2;
 }
 
 // Workspace: [partial outputs fp32 B*Hq*S*Dv] [partial LSEs fp32 B*Hq*S].
@@ -410,7 +416,7 @@ int kvq_decode(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, con
   if (!k_scale) return KVQ_ERR_ARG;  // the NVFP4 global scale
   const SplitPlan plan = plan_mla(batch, hq, max_len, c->desc.page_size);
   // pages one split touches, whatever its alignment to page boundaries
-  if ((plan.tiles_per_split - 1) / (P / kvq::kTile) + 2 > kvq::kMlaMaxSplitPages) return KVQ_ERR_UNSUPPORTED;
+  if (mla_split_pages(plan, P) > kvq::kMlaMaxSplitPages) return KVQ_ERR_UNSUPPORTED;
   const WsLayout wl = workspace_for(plan, batch, hq, d.v_dim);
   const size_t need = wl.total;
   if (need && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % kAlign)) return KVQ_ERR_SIZE;
