@@ -113,16 +113,26 @@ def setup(w, dev, rotate):
     lse = torch.empty((w.batch, w.q_heads), dtype=torch.float32, device=dev)
     need = K.kvq_decode_workspace_bytes(cache, w.batch, w.q_heads, max_len)
     ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
-    return dict(caches=caches, new=(new_k, new_v, new_s), q=q, table=table_d, lens=lens_d, lens_h=lens,
+    # one new token per sequence: the same rows as [B, Hkv, D] ([B, 576] for MLA) for kvq_decode_append
+    new_rows = None
+    if w.new_tokens == 1 and int((lens >= 1).sum()) == w.batch:
+        new_rows = (new_k.view(w.batch, *row), None if new_v is None else new_v.view(w.batch, *row))
+    return dict(caches=caches, new=(new_k, new_v, new_s), new_rows=new_rows, q=q, table=table_d, lens=lens_d, lens_h=lens,
                 max_len=max_len, ks=ks, vs=vs, out=out, lse=lse, ws=ws, sm=I.sm_scale(w),
                 bpt=K.kvq_bytes_per_token(cache.desc))
 
 
-def run_loop(st, steps, do_store, do_decode, offset=0):
+def run_loop(st, steps, do_store, do_decode, offset=0, fused=False):
+    """fused: each step appends its token and decodes in one kvq_decode_append call."""
     import quantized_paged_kv_store_amd as K
     caches = st["caches"]
     for i in range(steps):
         c = caches[(i + offset) % len(caches)]
+        if fused:
+            K.kvq_decode_append(c, st["new_rows"][0], st["new_rows"][1], st["q"], st["table"], st["lens"],
+                                st["max_len"], st["sm"], st["ks"], st["vs"], out=st["out"], lse=st["lse"],
+                                workspace=st["ws"])
+            continue
         if do_store:
             K.kvq_store(c, *st["new"], st["ks"], st["vs"])
         if do_decode:
@@ -130,7 +140,7 @@ def run_loop(st, steps, do_store, do_decode, offset=0):
                          out=st["out"], lse=st["lse"], workspace=st["ws"])
 
 
-def capture(st, do_store, do_decode):
+def capture(st, do_store, do_decode, fused=False):
     """One HIP graph per rotated cache copy holding the step's launches (the
     library neither allocates nor synchronizes, so the calls are capturable)."""
     import torch
@@ -138,13 +148,13 @@ def capture(st, do_store, do_decode):
     for r in range(len(st["caches"])):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            run_loop(st, 1, do_store, do_decode, offset=r)
+            run_loop(st, 1, do_store, do_decode, offset=r, fused=fused)
         graphs.append(g)
     torch.cuda.synchronize()
     return graphs
 
 
-def timed(st, steps, do_store, do_decode, graphs=None):
+def timed(st, steps, do_store, do_decode, graphs=None, fused=False):
     import torch
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -153,7 +163,7 @@ def timed(st, steps, do_store, do_decode, graphs=None):
         for i in range(steps):
             graphs[i % len(graphs)].replay()
     else:
-        run_loop(st, steps, do_store, do_decode)
+        run_loop(st, steps, do_store, do_decode, fused=fused)
     end.record()
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps     # ms per iteration
@@ -254,26 +264,33 @@ def main():
     t0 = time.time()
     st = setup(w, dev, args.rotate)
     log(f"setup {time.time() - t0:.1f} s")
-    run_loop(st, args.warmup, True, True)
+    # a decode step with one new token per sequence appends it and decodes in
+    # one launch (kvq_decode_append); a chunked step stores, then decodes
+    fused = st["new_rows"] is not None
+    run_loop(st, args.warmup, True, True, fused=fused)
     torch.cuda.synchronize()
     use_graph = args.graph
-    g_step = capture(st, True, True) if use_graph else None
+    g_step = capture(st, True, True, fused) if use_graph else None
+    g_sep = capture(st, True, True) if use_graph else None
     g_dec = capture(st, False, True) if use_graph else None
     g_store = capture(st, True, False) if use_graph else None
     if use_graph:
         for i in range(args.warmup):
             g_step[i % len(g_step)].replay()
-    ms_step = timed(st, args.steps, True, True, g_step)
+    ms_step = timed(st, args.steps, True, True, g_step, fused=fused)
+    ms_sep = timed(st, args.steps, True, True, g_sep) if fused else ms_step
     ms_dec = timed(st, args.steps, False, True, g_dec)
     ms_store = timed(st, args.steps, True, False, g_store)
     # per-kernel device time: the library brackets each launch with HIP events
     # on the launch stream while instrumentation is on
     import quantized_paged_kv_store_amd as K
     K.kvq_profile_enable(True)
-    run_loop(st, args.steps, True, True)
+    run_loop(st, args.steps, True, True, fused=fused)
     torch.cuda.synchronize()
     dec_tot, dec_n = K.kvq_profile_read("decode")
     mer_tot, mer_n = K.kvq_profile_read("merge")
+    run_loop(st, args.steps, True, False)
+    torch.cuda.synchronize()
     sto_tot, sto_n = K.kvq_profile_read("store")
     K.kvq_profile_enable(False)
     kern_ms = dec_tot / max(dec_n, 1)
@@ -282,7 +299,8 @@ def main():
     kv_bytes = float(st["lens_h"].astype(np.int64).sum()) * st["bpt"]
     value = kv_bytes / (ms_step * 1e-3) / 1e9
     dec_gbps = kv_bytes / (ms_dec * 1e-3) / 1e9
-    log(f"step {ms_step * 1e3:.1f} us, decode {ms_dec * 1e3:.1f} us, store {ms_store * 1e3:.1f} us, "
+    log(f"step {ms_step * 1e3:.1f} us (store then decode {ms_sep * 1e3:.1f} us), decode {ms_dec * 1e3:.1f} us, "
+        f"store {ms_store * 1e3:.1f} us, "
         f"{value:.0f} GB/s per step, {dec_gbps:.0f} GB/s decode")
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -291,7 +309,9 @@ def main():
         "config": {
             "workload": f"{w.name}: {w.q_heads} q heads / {w.kv_heads} kv heads, head_dim {w.head_dim}, "
                         f"batch {w.batch}, context {w.max_len}, page {w.page_size}, {w.dtype} KV "
-                        f"({w.scale_mode} scales); step = store {w.new_tokens} new token(s)/sequence + decode",
+                        f"({w.scale_mode} scales); step = "
+                        + ("append 1 new token/sequence + decode in one kvq_decode_append launch (+ split merge)"
+                           if fused else f"store {w.new_tokens} new token(s)/sequence, then decode (+ split merge)"),
             "global_batch": w.batch, "seq_len": w.max_len, "kv_dtype": w.dtype,
             "compute": ("latent codes dequantized to fp16 (E2M1 x E4M3 exact) for QK and PV MFMAs, f32 accumulate"
                         if w.kind == "mla" else
@@ -301,6 +321,7 @@ def main():
         },
         "pct_hbm_peak": round(100 * value / PEAK_HBM_GBPS, 2),
         "decode_only_GBps": round(dec_gbps, 2), "decode_ms": round(ms_dec, 5), "store_ms": round(ms_store, 5),
+        "store_then_decode_ms": round(ms_sep, 5),
         "context_tokens_per_s": round(float(st["lens_h"].sum()) / (ms_step * 1e-3), 1),
         "decode_tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),
     }

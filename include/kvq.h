@@ -202,8 +202,27 @@ int kvq_decode(const kvq_cache* cache, const void* q, int32_t batch, int32_t num
                int32_t max_seq_len, float sm_scale, const float* k_scale, const float* v_scale,
                float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* One decode step in one launch: appends the token at position seq_lens[b] - 1
+ * of every sequence b, then decodes. Equivalent to kvq_store of those tokens
+ * with slot = page_table[b*stride + (L-1)/P] * P + (L-1)%P (L = seq_lens[b];
+ * a sequence with L = 0 or an out-of-pool page stores nothing), followed by
+ * kvq_decode with the same arguments: the quantization is the store's and
+ * the codes written are bit-identical ([P4] quantize_and_store, then decode
+ * over the quantized cache). The context split that holds position L-1
+ * quantizes and writes that token before it reads its tiles, which saves the
+ * separate store launch of a decode step.
+ *   k_new, v_new: [dev] BF16, GQA [batch][num_kv_heads][head_dim] each;
+ *                 MLA: k_new = latent rows [batch][head_dim], v_new must be NULL.
+ * All other arguments, the workspace and the errors are kvq_decode's; a NULL
+ * k_new (or, for GQA, v_new) is KVQ_ERR_ARG. */
+int kvq_decode_append(const kvq_cache* cache, const void* k_new, const void* v_new, const void* q,
+                      int32_t batch, int32_t num_q_heads, const int32_t* page_table,
+                      int32_t page_table_stride, const int32_t* seq_lens, int32_t max_seq_len,
+                      float sm_scale, const float* k_scale, const float* v_scale, float* out,
+                      float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Instrumentation (off by default). While enabled, every kernel launched by
- * kvq_store / kvq_decode / kvq_compute_scale is bracketed by two HIP events
+ * kvq_store / kvq_decode(_append) / kvq_compute_scale is bracketed by two HIP events
  * recorded on the call's stream (nothing else changes; do not enable while
  * capturing a HIP graph). Enabling or disabling clears the records.
  * kvq_profile_read synchronizes the recorded events and returns, for one

@@ -26,7 +26,7 @@
 // The QK accumulator layout (lane = head column, 4 tokens per lane) is
 // exactly the PV B-operand layout once the 32 tokens of a pair are ordered
 // [tile A: 4g..4g+3, tile B: 4g..4g+3] along K, so scores never leave the lane.
-#include "kvq_internal.h"
+#include "store_row.h"
 
 namespace kvq {
 namespace {
@@ -258,6 +258,29 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
   const int fp = t_begin / tpp;
   const int n_pg = (t_end - 1) / tpp - fp + 1;
   for (int i = tid; i < n_pg; i += 256) sm_pg[i] = pt[fp + i];
+  // Append (kvq_decode_append): the split holding position L-1 quantizes the
+  // new token's K/V rows and writes them into the cache before any of its
+  // loads; the barrier below orders those stores before this workgroup's
+  // reads of the tile (no other workgroup reads it).
+  if (a.new_k != nullptr && (L - 1) / kTile < t_end && (L - 1) / kTile >= t_begin && tid < D / 16) {
+    const int pos = L - 1;
+    const int page = pt[pos / a.page_size];
+    if ((unsigned)page < (unsigned)a.num_pages) {
+      const int t = pos % a.page_size;
+      const int64_t row = ((int64_t)b * a.hkv + kvh) * D;
+      uint8_t* kc = const_cast<uint8_t*>(a.k_codes);
+      uint8_t* vc = const_cast<uint8_t*>(a.v_codes);
+      if constexpr (FMT == KVQ_FP4_MX16) {
+        const int64_t cbase = (int64_t)page * page_code + head_code + (int64_t)(t >> 4) * tile_code_bytes;
+        const int64_t sbase = (int64_t)page * page_scale + head_scale + (int64_t)(t >> 4) * tile_scale_bytes;
+        put_mx16_block(a.new_k + row, a.new_v + row, tid, D / 16, D, t & 15, kc, vc, const_cast<uint8_t*>(a.k_scales),
+                       const_cast<uint8_t*>(a.v_scales), cbase, sbase);
+      } else {
+        const int64_t base = (int64_t)page * page_code + head_code + (int64_t)(t >> 4) * tile_code_bytes;
+        put_fp8_chunk<FMT>(a.new_k + row, a.new_v + row, tid, t & 15, kscale, vscale, kc, vc, base);
+      }
+    }
+  }
   __syncthreads();
 
   // One tile pair in flight: loads are issued unconditionally (a missing or

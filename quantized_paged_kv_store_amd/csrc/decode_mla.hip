@@ -39,7 +39,7 @@
 //      LDS read, so the latent is dequantized once.
 #include <type_traits>
 
-#include "kvq_internal.h"
+#include "store_row.h"
 
 namespace kvq {
 namespace {
@@ -153,6 +153,20 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
   const int n_pg = (t_end - 1) / tpp - fp + 1;
   const int32_t* pt = a.page_table + (int64_t)b * a.page_table_stride;
   for (int i = tid; i < n_pg; i += kThreads) sm_pg[i] = pt[fp + i];
+  // Append (kvq_decode_append): the split holding position L-1 quantizes the
+  // new latent row and writes it into the cache before any of its loads (the
+  // barrier after the Q staging orders them). Both head-group workgroups of
+  // the split read that tile, so both write the same bytes.
+  if (a.new_k != nullptr && (L - 1) / kTile < t_end && (L - 1) / kTile >= t_begin && tid < kDk / 16) {
+    const int pos = L - 1;
+    const int page = pt[pos / a.page_size];
+    if ((unsigned)page < (unsigned)a.num_pages) {
+      const int t = pos % a.page_size;
+      uint8_t* cb = const_cast<uint8_t*>(a.codes) + (int64_t)page * a.page_size * (kDk / 2) + (int64_t)(t >> 4) * kTileCodes;
+      uint8_t* sb = const_cast<uint8_t*>(a.scales) + (int64_t)page * a.page_size * (kDk / 16) + (int64_t)(t >> 4) * kTileScales;
+      put_nvfp4_block(a.new_k + (int64_t)b * kDk, tid, t & 15, a.g_scale[0], cb, sb);
+    }
+  }
 
   // ---- Q of this wave's 32 heads and half of the elements, per-head power-of-two scaled ----
   // B operand of step ks: head 32*hgp + r32, elements 288*kh + 16*ks + 8*hh .. +7

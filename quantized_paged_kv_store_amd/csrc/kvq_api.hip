@@ -336,14 +336,22 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* c, int32_t batch, int32_t hq,
   return workspace_for(plan_mla(batch, hq, max_len, c->desc.page_size), batch, hq, c->desc.v_dim).total;
 }
 
-int kvq_decode(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, const int32_t* page_table,
-               int32_t page_table_stride, const int32_t* seq_lens, int32_t max_len, float sm_scale,
-               const float* k_scale, const float* v_scale, float* out, float* lse, void* ws, size_t ws_bytes,
-               void* stream) {
+namespace {
+
+// kvq_decode, optionally appending the token at position seq_lens[b] - 1 of
+// every sequence first (k_new / v_new non-null: kvq_decode_append)
+int decode_impl(const kvq_cache* c, const void* k_new, const void* v_new, const void* q, int32_t batch, int32_t hq,
+                const int32_t* page_table, int32_t page_table_stride, const int32_t* seq_lens, int32_t max_len,
+                float sm_scale, const float* k_scale, const float* v_scale, float* out, float* lse, void* ws,
+                size_t ws_bytes, void* stream) {
   if (!c || batch < 0 || hq < 1 || max_len < 0) return KVQ_ERR_ARG;
   if (batch == 0) return KVQ_OK;
   if (!q || !page_table || !seq_lens || !out || !aligned16(q)) return KVQ_ERR_ARG;
   const kvq_cache_desc& d = c->desc;
+  if (k_new) {
+    if (!aligned16(k_new)) return KVQ_ERR_ARG;
+    if (d.kind == KVQ_GQA ? (!v_new || !aligned16(v_new)) : v_new != nullptr) return KVQ_ERR_ARG;
+  }
   const int P = d.page_size;
   if (page_table_stride < (max_len + P - 1) / P || page_table_stride < 1) return KVQ_ERR_ARG;
   const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -386,6 +394,8 @@ int kvq_decode(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, con
     a.ws_lse = need ? reinterpret_cast<float*>(wsb + wl.lse) : nullptr;
     a.out = out;
     a.lse = lse;
+    a.new_k = static_cast<const uint16_t*>(k_new);
+    a.new_v = static_cast<const uint16_t*>(v_new);
     hipError_t e;
     {
       Timed timer(1, s);
@@ -442,6 +452,7 @@ int kvq_decode(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, con
   a.ws_lse = need ? reinterpret_cast<float*>(wsb + wl.lse) : nullptr;
   a.out = out;
   a.lse = lse;
+  a.new_k = static_cast<const uint16_t*>(k_new);
   hipError_t e;
   {
     Timed timer(1, s);
@@ -466,6 +477,25 @@ int kvq_decode(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, con
     if (e != hipSuccess) return KVQ_ERR_HIP;
   }
   return KVQ_OK;
+}
+
+}  // namespace
+
+int kvq_decode(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, const int32_t* page_table,
+               int32_t page_table_stride, const int32_t* seq_lens, int32_t max_len, float sm_scale,
+               const float* k_scale, const float* v_scale, float* out, float* lse, void* ws, size_t ws_bytes,
+               void* stream) {
+  return decode_impl(c, nullptr, nullptr, q, batch, hq, page_table, page_table_stride, seq_lens, max_len, sm_scale,
+                     k_scale, v_scale, out, lse, ws, ws_bytes, stream);
+}
+
+int kvq_decode_append(const kvq_cache* c, const void* k_new, const void* v_new, const void* q, int32_t batch,
+                      int32_t hq, const int32_t* page_table, int32_t page_table_stride, const int32_t* seq_lens,
+                      int32_t max_len, float sm_scale, const float* k_scale, const float* v_scale, float* out,
+                      float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (!k_new) return KVQ_ERR_ARG;
+  return decode_impl(c, k_new, v_new, q, batch, hq, page_table, page_table_stride, seq_lens, max_len, sm_scale,
+                     k_scale, v_scale, out, lse, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -118,6 +118,10 @@ struct GqaDecodeArgs {
   float* ws_lse;  // [B][Hq][S]   (log2 domain)
   float* out;     // [B][Hq][D]
   float* lse;     // [B][Hq] or null (natural log)
+  // optional append (kvq_decode_append): BF16 K/V rows [B][Hkv][D] of the token
+  // at position seq_lens[b] - 1, quantized and written by the split holding it
+  const uint16_t* new_k;
+  const uint16_t* new_v;
 };
 
 struct MlaDecodeArgs {
@@ -136,6 +140,9 @@ struct MlaDecodeArgs {
   float* ws_lse;
   float* out;
   float* lse;
+  // optional append (kvq_decode_append): BF16 latent rows [B][576] of the token
+  // at position seq_lens[b] - 1, quantized and written before it is read
+  const uint16_t* new_k;
 };
 
 struct CombineArgs {

@@ -1,17 +1,6 @@
-// kvq_store / kvq_compute_scale kernels for gfx950.
-//
-// Quantization rules (the pages: SGLang "Quantized KV Cache" page, sections
-// "Supported formats" and "Scaling factors"; PR #21954 analysis page,
-// NVFP4KVMethod / BlockFP4KVMethod and quantize_and_store):
-//   FP8:   code = RNE(clamp(x / s, -max, max)) with x / s IEEE binary32
-//   MX16:  per 16 elements e = floor(log2 amax) - 2 (clamped to [-127, 127]),
-//          element = RNE_sat_E2M1(x * 2^-e), scale byte = e + 127
-//   NVFP4: per 16 elements s = amax / fl32(6 g) -> E4M3 (saturating),
-//          sd = E4M3(s) * g, element = RNE_sat_E2M1(x / sd) (signed zero if sd == 0)
-// The gfx950 converts round to nearest even; the FP8 ones turn out-of-range
-// inputs into NaN/Inf, so values are clamped to the format maximum first
-// (which equals round-then-saturate). The E2M1 convert saturates by itself.
-#include "kvq_internal.h"
+// kvq_store / kvq_compute_scale kernels for gfx950. The per-chunk quantize-
+// and-place routines (and the quantization rules) are in store_row.h.
+#include "store_row.h"
 
 namespace kvq {
 namespace {
@@ -68,39 +57,6 @@ __global__ void __launch_bounds__(256) amax_final_kernel(const unsigned* __restr
   }
 }
 
-// ------------------------------------------------------------------- FP8 --
-template <int FMT>
-__device__ __forceinline__ uint32_t encode_fp8x4(float a, float b, float c, float d) {
-  constexpr float MX = (FMT == KVQ_FP8_E4M3) ? 448.0f : 57344.0f;
-  a = fminf(fmaxf(a, -MX), MX);
-  b = fminf(fmaxf(b, -MX), MX);
-  c = fminf(fmaxf(c, -MX), MX);
-  d = fminf(fmaxf(d, -MX), MX);
-  uint32_t w;
-  if (FMT == KVQ_FP8_E4M3) {
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  } else {
-    w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
-    w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
-  }
-  return w;
-}
-
-// 16 BF16 (two uint4) / s -> 16 FP8 codes (uint4).
-template <int FMT>
-__device__ __forceinline__ uint4 quant_fp8_16(const uint4 lo, const uint4 hi, float s) {
-  const uint32_t in[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-  uint32_t out[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t w0 = in[2 * i], w1 = in[2 * i + 1];
-    out[i] = encode_fp8x4<FMT>(bf16_bits_to_f32(w0 & 0xffffu) / s, bf16_bits_to_f32(w0 >> 16) / s,
-                               bf16_bits_to_f32(w1 & 0xffffu) / s, bf16_bits_to_f32(w1 >> 16) / s);
-  }
-  return make_uint4(out[0], out[1], out[2], out[3]);
-}
-
 // one thread per (token, kv head, 16-element chunk)
 template <int FMT>
 __global__ void __launch_bounds__(256) store_fp8_kernel(
@@ -122,67 +78,9 @@ __global__ void __launch_bounds__(256) store_fp8_kernel(
   const int t16 = t & 15;
   const float ks = k_scale ? k_scale[0] : 1.0f;
   const float vs = v_scale ? v_scale[0] : 1.0f;
-  const int64_t row = (tok * hkv + h) * dim + c * 16;
-  const uint4* kp = reinterpret_cast<const uint4*>(k + row);
-  const uint4* vp = reinterpret_cast<const uint4*>(v + row);
-  const uint4 kq = quant_fp8_16<FMT>(kp[0], kp[1], ks);
-  const uint4 vq = quant_fp8_16<FMT>(vp[0], vp[1], vs);
+  const int64_t row = (tok * hkv + h) * dim;
   const int64_t base = (page * hkv + h) * block_bytes + (int64_t)(t >> 4) * 16 * dim;
-  // K: the 16 elements of chunk c are 16 contiguous bytes
-  *reinterpret_cast<uint4*>(kc + base + 256 * c + 16 * t16) = kq;
-  // V: element d = 16c + r at 1024*(d/64) + 16*(16*(t16/4) + r) + 4*(c%4) + t16%4
-  uint8_t* vb = vc + base + 1024 * (c >> 2) + 16 * (16 * (t16 >> 2)) + 4 * (c & 3) + (t16 & 3);
-  const uint32_t vw[4] = {vq.x, vq.y, vq.z, vq.w};
-#pragma unroll
-  for (int r = 0; r < 16; ++r) vb[16 * r] = (uint8_t)(vw[r >> 2] >> (8 * (r & 3)));
-}
-
-// ------------------------------------------------------------- FP4 (E2M1) --
-// Eight floats -> one dword of E2M1 codes (element 2i in the low nibble of byte i).
-__device__ __forceinline__ uint32_t encode_e2m1x8(const float* f) {
-  uint32_t w = 0;
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[0], f[1], 1.0f, 0);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[2], f[3], 1.0f, 1);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[4], f[5], 1.0f, 2);
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, f[6], f[7], 1.0f, 3);
-  return w;
-}
-
-__device__ __forceinline__ void unpack_bf16x16(const uint4 lo, const uint4 hi, float* x, uint32_t& amax_bits) {
-  const uint32_t in[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-  uint32_t m = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    x[2 * i] = bf16_bits_to_f32(in[i] & 0xffffu);
-    x[2 * i + 1] = bf16_bits_to_f32(in[i] >> 16);
-    m = max(m, in[i] & 0x7fffu);
-    m = max(m, (in[i] >> 16) & 0x7fffu);
-  }
-  amax_bits = m;
-}
-
-// OCP shared exponent of a block whose largest magnitude has BF16 bits m:
-// floor(log2 amax) - 2, clamped to [-127, 127]; -127 for an all-zero block.
-__device__ __forceinline__ int mx_exponent(uint32_t m) {
-  if (m == 0) return -127;
-  const int ef = (int)(m >> 7);
-  const int fl = ef > 0 ? ef - 127 : (31 - __clz((int)m)) - 133;  // subnormal: m * 2^-133
-  const int e = fl - 2;
-  return e < -127 ? -127 : (e > 127 ? 127 : e);
-}
-
-__device__ __forceinline__ void quant_mx16(const uint4 lo, const uint4 hi, uint32_t& c0, uint32_t& c1,
-                                           uint8_t& sc) {
-  float x[16];
-  uint32_t m;
-  unpack_bf16x16(lo, hi, x, m);
-  const int e = mx_exponent(m);
-  const float mul = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, a normal float
-#pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] *= mul;                       // exact
-  c0 = encode_e2m1x8(x);
-  c1 = encode_e2m1x8(x + 8);
-  sc = (uint8_t)(e + 127);
+  put_fp8_chunk<FMT>(k + row, v + row, c, t16, ks, vs, kc, vc, base);
 }
 
 // one thread per (token, kv head, 16-element block)
@@ -203,26 +101,10 @@ __global__ void __launch_bounds__(256) store_mx16_kernel(
   const int64_t page = slot / page_size;
   const int t = (int)(slot % page_size);
   const int t16 = t & 15;
-  const int64_t row = (tok * hkv + h) * dim + b * 16;
-  const uint4* kp = reinterpret_cast<const uint4*>(k + row);
-  const uint4* vp = reinterpret_cast<const uint4*>(v + row);
-  uint32_t k0, k1, v0, v1;
-  uint8_t kse, vse;
-  quant_mx16(kp[0], kp[1], k0, k1, kse);
-  quant_mx16(vp[0], vp[1], v0, v1, vse);
+  const int64_t row = (tok * hkv + h) * dim;
   const int64_t cbase = (page * hkv + h) * code_block + (int64_t)(t >> 4) * 8 * dim;
   const int64_t sbase = (page * hkv + h) * scale_block + (int64_t)(t >> 4) * dim;
-  const int d0 = 16 * b;
-  // K codes: byte 256*(d/32) + 16*t16 + (d%32)/2 -> 8 contiguous bytes
-  *reinterpret_cast<uint2*>(kc + cbase + 256 * (d0 >> 5) + 16 * t16 + ((d0 & 31) >> 1)) = make_uint2(k0, k1);
-  // V codes: byte 1024*(d/128) + 16*(16*(t16/4) + (d%128)/8) + 4*(t16%4) + (d%8)/2
-  uint8_t* vb = vc + cbase + 1024 * (d0 >> 7) + 16 * (16 * (t16 >> 2)) + 4 * (t16 & 3);
-  const int c8 = (d0 & 127) >> 3;
-  *reinterpret_cast<uint32_t*>(vb + 16 * c8) = v0;
-  *reinterpret_cast<uint32_t*>(vb + 16 * (c8 + 1)) = v1;
-  // scales
-  ksc[sbase + 32 * (b >> 1) + 2 * t16 + (b & 1)] = kse;
-  vsc[sbase + 4 * (nb * (t16 >> 2) + b) + (t16 & 3)] = vse;
+  put_mx16_block(k + row, v + row, b, nb, dim, t16, kc, vc, ksc, vsc, cbase, sbase);
 }
 
 // ----------------------------------------------------------------- NVFP4 --
@@ -238,49 +120,11 @@ __global__ void __launch_bounds__(256) store_nvfp4_kernel(
   const int64_t tok = gid / nb;
   const int64_t slot = slots[tok];
   if (slot < 0 || slot >= capacity) return;
-  const uint4* kp = reinterpret_cast<const uint4*>(k + tok * dim + b * 16);
-  float x[16];
-  uint32_t m;
-  unpack_bf16x16(kp[0], kp[1], x, m);
-  const float g = g_scale[0];
-  const float d6 = 6.0f * g;
-  float s = bf16_bits_to_f32(m) / d6;         // >= 0
-  s = fminf(s, 448.0f);
-  const uint32_t sc = __builtin_amdgcn_cvt_pk_fp8_f32(s, 0.0f, 0, false) & 0xffu;
-  const float sd = __builtin_amdgcn_cvt_pk_f32_fp8(sc, false)[0] * g;
-  if (sd == 0.0f) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = __builtin_copysignf(0.0f, x[i]);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = fminf(fmaxf(x[i] / sd, -6.0f), 6.0f);
-  }
-  const uint32_t c0 = encode_e2m1x8(x), c1 = encode_e2m1x8(x + 8);
-  // MLA tile layout (16 tokens, 4608 code + 576 scale bytes): the 8-element
-  // groups of one token and lane group sit in dwords laid out for the decode
-  // kernel's loads (see include/kvq.h)
   const int page = (int)(slot / page_size);
   const int t = (int)(slot % page_size);
-  const int t16 = t & 15, g4 = t16 >> 2, tt = t16 & 3;
   uint8_t* cb = codes + (int64_t)page * page_size * (dim / 2) + (int64_t)(t >> 4) * 16 * (dim / 2);
   uint8_t* sb = scales + (int64_t)page * page_size * nb + (int64_t)(t >> 4) * 16 * nb;
-  // 16 elements = four 4-element groups, 2 code bytes each
-  int64_t oc[4], os;
-  if (b < 32) {
-    const int w8 = b >> 2;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) oc[q] = 2 * (((w8 * 4 + g4) * 16 + 4 * (b & 3) + q) * 4 + tt);
-    os = 4 * ((w8 * 4 + g4) * 4 + (b & 3)) + tt;
-  } else {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) oc[q] = 4096 + 2 * ((g4 * 16 + 4 * (b - 32) + q) * 4 + tt);
-    os = 512 + 4 * (g4 * 4 + b - 32) + tt;
-  }
-  *reinterpret_cast<uint16_t*>(cb + oc[0]) = (uint16_t)(c0 & 0xffffu);
-  *reinterpret_cast<uint16_t*>(cb + oc[1]) = (uint16_t)(c0 >> 16);
-  *reinterpret_cast<uint16_t*>(cb + oc[2]) = (uint16_t)(c1 & 0xffffu);
-  *reinterpret_cast<uint16_t*>(cb + oc[3]) = (uint16_t)(c1 >> 16);
-  sb[os] = (uint8_t)sc;
+  put_nvfp4_block(k + tok * dim, b, t & 15, g_scale[0], cb, sb);
 }
 
 }  // namespace

@@ -66,6 +66,10 @@ def _lib():
         L.kvq_decode.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_int32,
                                  c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
         L.kvq_decode.restype = c_int32
+        L.kvq_decode_append.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_int32,
+                                        c_void_p, c_int32, c_float, c_void_p, c_void_p, c_void_p, c_void_p,
+                                        c_void_p, c_size_t, c_void_p]
+        L.kvq_decode_append.restype = c_int32
         L.kvq_profile_enable.argtypes = [c_int32]
         L.kvq_profile_enable.restype = c_int32
         L.kvq_profile_read.argtypes = [c_char_p, POINTER(c_double), POINTER(c_int64)]
@@ -198,12 +202,42 @@ def kvq_decode(cache: Cache, q: torch.Tensor, page_table: torch.Tensor, seq_lens
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     need = kvq_decode_workspace_bytes(cache, B, Hq, max_seq_len)
     if workspace is None and need:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)   # split counters start at zero
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ks, vs = _dev_f32(k_scale, dev), _dev_f32(v_scale, dev)
     _check(_lib().kvq_decode(cache.handle, _ptr(q), B, Hq, _ptr(page_table), page_table.shape[1], _ptr(seq_lens),
                              max_seq_len, float(sm_scale), _ptr(ks), _ptr(vs), _ptr(out), _ptr(lse),
                              _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(dev)),
            "kvq_decode")
+    return out, lse
+
+
+def kvq_decode_append(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor | None, q: torch.Tensor,
+                      page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, sm_scale: float,
+                      k_scale=None, v_scale=None, out=None, lse=None, workspace=None):
+    """Append the token at position seq_lens[b]-1 of every sequence (k_new, v_new:
+    [B, Hkv, D] BF16; MLA: k_new [B, 576], v_new None) and decode, in one
+    launch. Returns (out fp32 [B, Hq, Dv], lse fp32 [B, Hq])."""
+    dev = cache.device
+    B, Hq, _ = q.shape
+    assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.device == dev
+    assert k_new.dtype == torch.bfloat16 and k_new.is_contiguous() and k_new.device == dev
+    if v_new is not None:
+        assert v_new.dtype == torch.bfloat16 and v_new.is_contiguous() and v_new.device == dev
+    assert page_table.dtype == torch.int32 and page_table.is_contiguous() and page_table.dim() == 2
+    assert seq_lens.dtype == torch.int32 and seq_lens.numel() == B
+    if out is None:
+        out = torch.empty((B, Hq, cache.desc.v_dim), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    need = kvq_decode_workspace_bytes(cache, B, Hq, max_seq_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ks, vs = _dev_f32(k_scale, dev), _dev_f32(v_scale, dev)
+    _check(_lib().kvq_decode_append(cache.handle, _ptr(k_new), _ptr(v_new), _ptr(q), B, Hq, _ptr(page_table),
+                                    page_table.shape[1], _ptr(seq_lens), max_seq_len, float(sm_scale), _ptr(ks),
+                                    _ptr(vs), _ptr(out), _ptr(lse), _ptr(workspace),
+                                    0 if workspace is None else workspace.numel(), _stream(dev)),
+           "kvq_decode_append")
     return out, lse
 
 

@@ -80,8 +80,12 @@ class Case:
         return self._to_dev(a).view(torch.bfloat16)
 
     # ------------------------------------------------------------ HIP path --
-    def run_gpu(self, decode=True):
+    def run_gpu(self, decode=True, append=False):
+        """append: the last token of every sequence is not stored separately;
+        kvq_decode_append stores it and decodes in one call (one new token per
+        sequence required)."""
         w = self.w
+        assert not append or w.new_tokens == 1
         self.cache = K.kvq_alloc_pages(w.dtype, w.kind, w.kv_heads, w.head_dim, w.v_dim, w.page_size,
                                        self.npages, device=self.dev, fill=FILL[w.dtype])
         pre = [(b, 0, int(self.prefill[b])) for b in range(w.batch) if self.prefill[b] > 0]
@@ -114,14 +118,29 @@ class Case:
         del kp, vp
         kn, vn, sn = self.data["new"]
         self.new_inputs = (kn, vn, sn)
-        if kn is not None and len(kn):
+        if kn is not None and len(kn) and not append:
             self.new_dev = (self._bf16(kn), None if vn is None else self._bf16(vn), self._to_dev(sn))
             K.kvq_store(self.cache, *self.new_dev, self.k_scale, self.v_scale)
         self.q = I.queries(w)
         self.q_dev = self._bf16(self.q)
         self.table_dev = self._to_dev(self.table)
         self.lens_dev = self._to_dev(self.lens.astype(np.int32))
-        if decode:
+        if append:
+            # row b = the token at position L_b - 1 (zeros where L_b = 0: nothing is stored)
+            row = (w.kv_heads, w.head_dim) if w.kind == "gqa" else (w.head_dim,)
+            kb = np.zeros((w.batch, *row), np.uint16)
+            vb = None if w.kind == "mla" else np.zeros((w.batch, *row), np.uint16)
+            i = 0
+            for b in range(w.batch):
+                if self.lens[b] > self.prefill[b]:
+                    kb[b] = kn[i].reshape(row)
+                    if vb is not None:
+                        vb[b] = vn[i].reshape(row)
+                    i += 1
+            self.out, self.lse = K.kvq_decode_append(
+                self.cache, self._bf16(kb), None if vb is None else self._bf16(vb), self.q_dev, self.table_dev,
+                self.lens_dev, self.max_len, I.sm_scale(w), self.k_scale, self.v_scale)
+        elif decode:
             self.out, self.lse = K.kvq_decode(self.cache, self.q_dev, self.table_dev, self.lens_dev, self.max_len,
                                               I.sm_scale(w), self.k_scale, self.v_scale)
         torch.cuda.synchronize(self.dev)

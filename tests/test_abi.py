@@ -35,7 +35,7 @@ def test_exports_every_declared_function():
     assert set(names) >= {"kvq_alloc_pages", "kvq_store", "kvq_decode", "kvq_compute_scale",
                           "kvq_bytes_per_token", "kvq_status_string", "kvq_cache_layout",
                           "kvq_free_handle", "kvq_decode_workspace_bytes", "kvq_profile_enable",
-                          "kvq_profile_read"}
+                          "kvq_profile_read", "kvq_decode_append"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -187,3 +187,18 @@ def test_mla_decode_argument_errors(handles):
     assert lib.kvq_decode(*mla(96, P)) == UNSUP          # 64 or 128 heads only
     assert lib.kvq_decode(*mla(128, None)) == ARG        # the NVFP4 global scale is required
     assert lib.kvq_decode_workspace_bytes(h["mla"], 2, 96, 1000) == 0
+
+
+def test_decode_append_argument_errors(handles):
+    lib, h = handles
+    P = c_void_p(FAKE_DEV)
+    tail = (P, 4, 8, P, 4, P, 64, 0.1, None, None, P, None, None, 0, None)
+    assert lib.kvq_decode_append(h["fp8"], None, P, *tail) == ARG                  # k_new required
+    assert lib.kvq_decode_append(h["fp8"], P, None, *tail) == ARG                  # GQA needs v_new
+    assert lib.kvq_decode_append(h["fp8"], c_void_p(FAKE_DEV + 2), P, *tail) == ARG  # 16-byte aligned rows
+    mla = (P, 2, 128, P, 16, P, 1000, 0.04, P, None, P, None, None, 0, None)
+    assert lib.kvq_decode_append(h["mla"], P, P, *mla) == ARG                      # MLA has no V rows
+    assert lib.kvq_decode_append(h["mla"], P, None, P, 2, 96, P, 16, P, 1000, 0.04, P, None, P, None, None, 0,
+                                 None) == UNSUP
+    assert lib.kvq_decode_append(h["fp8"], P, P, P, 0, 8, P, 4, P, 64, 0.1, None, None, P, None, None, 0,
+                                 None) == OK                                       # empty batch
