@@ -357,25 +357,27 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
     pv_pair<FMT, D>(P.t[0], P.t[1], p, o);
   };
 
+  // Tile pairs in flight per wave: two for FP8 at D = 128 (8 KB per wave in
+  // flight), four for the smaller tiles of FP4-MX16 and FP8 at D = 64, which
+  // otherwise leave too few bytes in flight to cover HBM latency. Every slot
+  // of the unrolled body issues and computes unconditionally (so every wait
+  // count is static); the wave's pair count is rounded up to whole bodies.
+  // Pairs past the split are clamped in-pool stand-ins whose tokens are all
+  // masked: they add exactly nothing to the softmax state.
+  constexpr int kDepth = (FMT == KVQ_FP4_MX16 || D == 64) ? 4 : 2;
   int pr = __builtin_amdgcn_readfirstlane(wave);
   if (pr < npairs) {
-    Pair PA, PB;
-    issue(pr, PA);
-    while (true) {
-      if (pr + kWaves >= npairs) {
-        compute(PA);
-        break;
+    const int iters = ((npairs - pr + kWaves - 1) / kWaves + kDepth - 1) / kDepth;
+    Pair R[kDepth];
+#pragma unroll
+    for (int i = 0; i < kDepth - 1; ++i) issue(pr + i * kWaves, R[i]);
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int slot = 0; slot < kDepth; ++slot) {
+        issue(pr + (kDepth - 1) * kWaves, R[(slot + kDepth - 1) % kDepth]);
+        compute(R[slot]);
+        pr += kWaves;
       }
-      issue(pr + kWaves, PB);
-      compute(PA);
-      pr += kWaves;
-      if (pr + kWaves >= npairs) {
-        compute(PB);
-        break;
-      }
-      issue(pr + kWaves, PA);
-      compute(PB);
-      pr += kWaves;
     }
   }
 
