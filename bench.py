@@ -66,7 +66,7 @@ def setup(w, dev, rotate):
     max_len = int(lens.max())
     pre = np.maximum(lens - w.new_tokens, 0)
     cache = K.kvq_alloc_pages(w.dtype, w.kind, w.kv_heads, w.head_dim, w.v_dim, w.page_size, npages,
-                              device=dev, fill=0)
+                              device=dev, fill=0, scale_per_head=w.scale_mode == "amax_head")
     # prefill, one sequence at a time (bounded host memory); scales first need the
     # whole prefill, so K (and V) are staged on the device
     n_pre = int(pre.sum())
@@ -86,7 +86,7 @@ def setup(w, dev, rotate):
         sd[off:off + n] = torch.from_numpy(I.slots_for(table[b], np.arange(n), w.page_size)).to(dev)
         off += n
     ks = vs = None
-    if w.dtype in ("e4m3", "e5m2") and w.scale_mode == "amax":
+    if w.dtype in ("e4m3", "e5m2") and w.scale_mode in ("amax", "amax_head"):
         ks = K.kvq_compute_scale(cache, kd, vd) if w.dist == "tiny" else K.kvq_compute_scale(cache, kd)
         vs = ks if w.dist == "tiny" else K.kvq_compute_scale(cache, vd)
     elif w.dtype == "nvfp4":
@@ -191,6 +191,9 @@ def cpu_baseline(w, seconds_hint=20.0):
     if w.dtype in ("e4m3", "e5m2") and w.scale_mode == "amax":
         fmt = E4M3 if w.dtype == "e4m3" else E5M2
         ks, vs = Q.fp8_scale(np.abs(kf).max(), fmt), Q.fp8_scale(np.abs(vf).max(), fmt)
+    elif w.dtype in ("e4m3", "e5m2") and w.scale_mode == "amax_head":
+        fmt = E4M3 if w.dtype == "e4m3" else E5M2
+        ks, vs = Q.fp8_head_scales(kf, fmt), Q.fp8_head_scales(vf, fmt)
     elif w.dtype == "nvfp4":
         ks = Q.nvfp4_global_scale(np.abs(kf).max())
     oc = OracleCache(CacheSpec(w.dtype, w.kind, w.kv_heads, w.head_dim, w.v_dim, P, npg))
@@ -246,6 +249,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay captured HIP graphs instead of eager launches")
     ap.add_argument("--copy-ref", action="store_true", help="only run the 1 GiB reference copy (for counters)")
+    ap.add_argument("--per-head-scales", action="store_true",
+                    help="FP8 workloads: one calibrated k/v scale per KV head instead of per tensor")
     args = ap.parse_args()
     if args.copy_ref:
         copy_reference()
@@ -260,6 +265,9 @@ def main():
     from quantized_paged_kv_store_amd import inputs as I
 
     w = I.WORKLOADS[args.workload]
+    if args.per_head_scales:
+        assert w.dtype in ("e4m3", "e5m2"), "per-head scales apply to FP8 caches"
+        w = w.with_(scale_mode="amax_head")
     dev = torch.device("cuda:0")
     t0 = time.time()
     st = setup(w, dev, args.rotate)

@@ -71,10 +71,15 @@ typedef struct kvq_cache_desc {
   int32_t v_dim;        /* GQA: must equal head_dim; MLA: latent dims (Dv) */
   int32_t page_size;    /* tokens per page, a multiple of 16 */
   int64_t num_pages;    /* physical pages in the pool, >= 1 */
+  int32_t scale_per_head; /* FP8 GQA only: 0 = one k_scale / v_scale per tensor,
+                             1 = one per KV head ([P3] "Supported schemes":
+                             per-attention-head scales k/v_scale = [num_kv_heads]);
+                             every k_scale / v_scale argument is then an array
+                             of num_kv_heads floats. Must be 0 otherwise. */
 } kvq_cache_desc;
 
 /* Supported combinations (others return KVQ_ERR_UNSUPPORTED):
- *   GQA x {E4M3, E5M2}: head_dim in {64, 128}
+ *   GQA x {E4M3, E5M2}: head_dim in {64, 128}, scale_per_head 0 or 1
  *   GQA x FP4_MX16:     head_dim == 128
  *   MLA x NVFP4:        head_dim == 576, v_dim == 512
  *   decode, GQA:        G = Hq / Hkv in [1, 16], max_seq_len <= 2,097,152
@@ -151,6 +156,9 @@ void kvq_free_handle(kvq_cache* cache);
  *   x1[0..n1) (x1 may be NULL with n1 == 0); division is IEEE binary32.
  * x0, x1: [dev] BF16. scale_out: [dev] one float. Uses the cache's scratch
  * buffer: concurrent calls on one cache race.
+ * With scale_per_head = 1, x0 and x1 are [tokens][num_kv_heads][head_dim]
+ * (n0, n1 multiples of num_kv_heads*head_dim, both 16-byte aligned) and
+ * scale_out[h] = amax over head h / format max, for h < num_kv_heads.
  * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED (FP4_MX16 has no tensor scale). */
 int kvq_compute_scale(const kvq_cache* cache, const void* x0, int64_t n0, const void* x1,
                       int64_t n1, float* scale_out, void* stream);
@@ -162,7 +170,8 @@ int kvq_compute_scale(const kvq_cache* cache, const void* x0, int64_t n0, const 
  *   slot_mapping: [dev] int64 [num_tokens], slot = page * page_size + offset;
  *         a negative slot or one >= num_pages*page_size skips the token.
  *   k_scale, v_scale: [dev] fp32 scalars. FP8: per-tensor scales, NULL = 1.0
- *         ([P1]: default when no scale is given); code = RNE_sat(x / scale).
+ *         ([P1]: default when no scale is given); code = RNE_sat(x / scale);
+ *         with scale_per_head, [num_kv_heads] arrays indexed by KV head.
  *         NVFP4: k_scale = global scale g (required), v_scale unused.
  *         FP4_MX16: both unused (block exponents are computed here from each
  *         16-element block's amax: e = floor(log2 amax) - 2).
@@ -187,7 +196,8 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t
  *   page_table: [dev] int32, row stride page_table_stride (>= ceil(max_seq_len/P))
  *   seq_lens:   [dev] int32 [batch], each in [0, max_seq_len]
  *   max_seq_len [host]: upper bound used to size the launch
- *   k_scale, v_scale: [dev] fp32 (FP8: per-tensor scales, NULL = 1.0;
+ *   k_scale, v_scale: [dev] fp32 (FP8: per-tensor scales, NULL = 1.0, or
+ *               [num_kv_heads] arrays with scale_per_head;
  *               NVFP4: k_scale = global scale g, required; MX16: unused)
  *   out:        [dev] fp32 [batch][num_q_heads][v_dim]
  *   lse:        [dev] fp32 [batch][num_q_heads] (natural log) or NULL

@@ -124,6 +124,15 @@ def v_scale_pos(spec: CacheSpec, t, b):
 
 
 # ------------------------------ cache model -------------------------------
+def head_scale(scale, h) -> np.float32:
+    """FP8 scale of KV head h: a per-tensor scalar (None = 1.0) or element h
+    of a per-head sequence."""
+    if scale is None:
+        return np.float32(1.0)
+    a = np.asarray(scale, dtype=np.float32)
+    return np.float32(a) if a.ndim == 0 else a[h]
+
+
 class OracleCache:
     """Byte-exact model of the cache buffers: arrays [num_pages, Hkv, block]."""
 
@@ -164,7 +173,9 @@ class OracleCache:
         """Quantize and store tokens. k, v: float arrays [T, Hkv, D] (GQA) or
         k [T, Dk] with v None (MLA). slots[i] = page * page_size + offset;
         a negative slot skips the token. k_scale/v_scale: FP8 per-tensor
-        scales (None = 1.0); for NVFP4, k_scale is the global scale g."""
+        scales (None = 1.0) or, per attention head (vLLM page, "Supported
+        schemes"), sequences of Hkv scales, head h using element h; for NVFP4,
+        k_scale is the global scale g."""
         s = self.spec
         slots = np.asarray(slots, dtype=np.int64)
         keep = slots >= 0
@@ -178,8 +189,8 @@ class OracleCache:
         for h in range(s.num_kv_heads):
             if s.dtype in ("e4m3", "e5m2"):
                 fmt = E4M3 if s.dtype == "e4m3" else E5M2
-                kc = Q.quantize_fp8(k[:, h], 1.0 if k_scale is None else k_scale, fmt)
-                vc = Q.quantize_fp8(v[:, h], 1.0 if v_scale is None else v_scale, fmt)
+                kc = Q.quantize_fp8(k[:, h], head_scale(k_scale, h), fmt)
+                vc = Q.quantize_fp8(v[:, h], head_scale(v_scale, h), fmt)
                 self._put_codes(self.k_codes, k_code_pos, page, h, t, kc)
                 self._put_codes(self.v_codes, v_code_pos, page, h, t, vc)
             elif s.dtype == "mx16":
@@ -219,8 +230,8 @@ class OracleCache:
             codes = self._get_codes(self.v_codes, v_code_pos, page, head, t, n)
         if s.dtype in ("e4m3", "e5m2"):
             fmt = E4M3 if s.dtype == "e4m3" else E5M2
-            sc = k_scale if which == "k" else v_scale
-            return decode(codes, fmt) * float(np.float32(1.0 if sc is None else sc))
+            sc = head_scale(k_scale if which == "k" else v_scale, head)
+            return decode(codes, fmt) * float(sc)
         b = np.arange(n // 16)[None, :]
         if s.dtype == "mx16":
             sbuf, pfn = (self.k_scales, k_scale_pos) if which == "k" else (self.v_scales, v_scale_pos)

@@ -37,6 +37,15 @@ def fp8_scale(amax: float, fmt: Format) -> np.float32:
     return np.float32(amax / np.float32(fmt.max_value))
 
 
+def fp8_head_scales(x, fmt: Format) -> np.ndarray:
+    """Per-attention-head scales (vLLM page, "Supported schemes": one scale per
+    KV head, k/v_scale = [num_kv_heads]): fp8_scale of the amax of each head
+    h = x[..., h, :] of a [tokens, Hkv, D] tensor."""
+    x = np.asarray(x, dtype=np.float64)
+    amax = np.abs(x).max(axis=(0, 2)) if x.shape[0] else np.zeros(x.shape[1])
+    return np.array([fp8_scale(a, fmt) for a in amax], dtype=np.float32)
+
+
 def quantize_fp8(x, scale, fmt: Format) -> np.ndarray:
     """codes = encode(fl32(x / scale)); x holds BF16 values (exact in fp32)."""
     x32 = fl32(x)

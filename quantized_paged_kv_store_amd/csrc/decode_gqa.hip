@@ -228,8 +228,9 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
   const int64_t page_scale = (int64_t)a.hkv * a.scale_block_bytes;
   const int32_t* pt = a.page_table + (int64_t)b * a.page_table_stride;
 
-  const float kscale = a.k_scale ? a.k_scale[0] : 1.0f;
-  const float vscale = a.v_scale ? a.v_scale[0] : 1.0f;
+  const int si = a.scale_per_head ? kvh : 0;  // per-tensor or per-KV-head FP8 scales
+  const float kscale = a.k_scale ? a.k_scale[si] : 1.0f;
+  const float vscale = a.v_scale ? a.v_scale[si] : 1.0f;
   const float s_log2 = a.sm_scale_log2 * kscale;
 
   // Q^T operand fragments for head hc (zero beyond the group)

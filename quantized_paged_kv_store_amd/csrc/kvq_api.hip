@@ -29,6 +29,8 @@ int check_desc(const kvq_cache_desc* d) {
     return KVQ_ERR_ARG;
   if (d->page_size % kvq::kTile) return KVQ_ERR_ARG;
   if (d->head_dim % 16) return KVQ_ERR_ARG;
+  if (d->scale_per_head != 0 && d->scale_per_head != 1) return KVQ_ERR_ARG;
+  if (d->scale_per_head && !(d->kind == KVQ_GQA && is_fp8(d->dtype))) return KVQ_ERR_UNSUPPORTED;
   if (d->kind == KVQ_GQA) {
     if (d->v_dim != d->head_dim) return KVQ_ERR_ARG;
     if (is_fp8(d->dtype)) return (d->head_dim == 64 || d->head_dim == 128) ? KVQ_OK : KVQ_ERR_UNSUPPORTED;
@@ -305,6 +307,17 @@ int kvq_compute_scale(const kvq_cache* c, const void* x0, int64_t n0, const void
     default: return KVQ_ERR_UNSUPPORTED;
   }
   unsigned* scratch = reinterpret_cast<unsigned*>(c->base + c->layout.scratch_offset);
+  if (c->desc.scale_per_head) {
+    const int64_t row = (int64_t)c->desc.num_kv_heads * c->desc.head_dim;
+    if (n0 % row || n1 % row) return KVQ_ERR_ARG;
+    if ((n0 && !aligned16(x0)) || (n1 && !aligned16(x1))) return KVQ_ERR_ARG;
+    Timed timer(3, static_cast<hipStream_t>(stream));
+    const hipError_t e = kvq_launch_amax_heads(static_cast<const uint16_t*>(x0), n0 / row,
+                                               static_cast<const uint16_t*>(x1), n1 / row, c->desc.num_kv_heads,
+                                               c->desc.head_dim, scratch, div, scale_out,
+                                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+  }
   Timed timer(3, static_cast<hipStream_t>(stream));
   const hipError_t e = kvq_launch_amax(static_cast<const uint16_t*>(x0), n0, static_cast<const uint16_t*>(x1), n1,
                                        scratch, div, scale_out, static_cast<hipStream_t>(stream));
@@ -380,6 +393,7 @@ int decode_impl(const kvq_cache* c, const void* k_new, const void* v_new, const 
     const bool fp8 = is_fp8(d.dtype);
     a.k_scale = fp8 ? k_scale : nullptr;
     a.v_scale = fp8 ? v_scale : nullptr;
+    a.scale_per_head = d.scale_per_head;
     a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
     a.batch = batch;
     a.hq = hq;

@@ -111,6 +111,7 @@ struct GqaDecodeArgs {
   const int32_t* seq_lens;
   const float* k_scale;
   const float* v_scale;
+  int scale_per_head;   // FP8: k/v_scale are [hkv] arrays
   float sm_scale_log2;  // sm_scale * log2(e)
   int batch, hq, hkv, group, page_size, max_len;
   int tiles_per_split, num_splits;
@@ -162,3 +163,5 @@ hipError_t kvq_launch_store(const kvq_cache* c, const uint16_t* k, const uint16_
 hipError_t kvq_launch_decode_gqa(const kvq_cache* c, const GqaDecodeArgs& a, hipStream_t s);
 hipError_t kvq_launch_decode_mla(const kvq_cache* c, const MlaDecodeArgs& a, hipStream_t s);
 hipError_t kvq_launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t kvq_launch_amax_heads(const uint16_t* x0, int64_t rows0, const uint16_t* x1, int64_t rows1, int hkv,
+                                 int dim, unsigned* scratch, float fmt_div, float* scale_out, hipStream_t s);

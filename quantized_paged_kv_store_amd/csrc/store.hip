@@ -57,12 +57,61 @@ __global__ void __launch_bounds__(256) amax_final_kernel(const unsigned* __restr
   }
 }
 
+// Per-KV-head amax of x[rows][hkv][dim] BF16 (16-byte aligned rows): block
+// (bx, h) reduces head h over 8-element groups bx, bx + gridDim.x, ...
+__global__ void __launch_bounds__(256) amax_head_partial_kernel(const uint16_t* __restrict__ x0, int64_t rows0,
+                                                                const uint16_t* __restrict__ x1, int64_t rows1,
+                                                                int hkv, int dim, unsigned* __restrict__ partial) {
+  const int h = blockIdx.y;
+  const int gpr = dim / 8;
+  unsigned m = 0;
+  for (int which = 0; which < 2; ++which) {
+    const uint16_t* x = which ? x1 : x0;
+    const int64_t rows = which ? rows1 : rows0;
+    if (x == nullptr || rows <= 0) continue;
+    const int64_t n = rows * gpr;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+      const int64_t r = i / gpr;
+      const int q = (int)(i - r * gpr);
+      const uint4 w = *reinterpret_cast<const uint4*>(x + (r * hkv + h) * dim + 8 * q);
+      const uint32_t a4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        m = max(m, a4[j] & 0x7fffu);
+        m = max(m, (a4[j] >> 16) & 0x7fffu);
+      }
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, off, 64));
+  __shared__ unsigned red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) partial[h * gridDim.x + blockIdx.x] = max(max(red[0], red[1]), max(red[2], red[3]));
+}
+
+// out[h] = amax_h / fmt_div (1.0 for an all-zero head), one block per head
+__global__ void __launch_bounds__(256) amax_head_final_kernel(const unsigned* __restrict__ partial, int n,
+                                                              float fmt_div, float* __restrict__ out) {
+  const int h = blockIdx.x;
+  unsigned m = 0;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) m = max(m, partial[h * n + i]);
+  for (int off = 32; off > 0; off >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, off, 64));
+  __shared__ unsigned red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = max(max(red[0], red[1]), max(red[2], red[3]));
+    const float amax = bf16_bits_to_f32(m);
+    out[h] = (amax == 0.f) ? 1.0f : amax / fmt_div;  // IEEE binary32 division
+  }
+}
+
 // one thread per (token, kv head, 16-element chunk)
 template <int FMT>
 __global__ void __launch_bounds__(256) store_fp8_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const int64_t* __restrict__ slots,
     int32_t n_tok, int hkv, int dim, int page_size, int64_t capacity, const float* __restrict__ k_scale,
-    const float* __restrict__ v_scale, uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+    const float* __restrict__ v_scale, int scale_per_head, uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
     int64_t block_bytes) {
   const int chunks = dim / 16;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -76,8 +125,9 @@ __global__ void __launch_bounds__(256) store_fp8_kernel(
   const int64_t page = slot / page_size;
   const int t = (int)(slot % page_size);
   const int t16 = t & 15;
-  const float ks = k_scale ? k_scale[0] : 1.0f;
-  const float vs = v_scale ? v_scale[0] : 1.0f;
+  const int si = scale_per_head ? h : 0;
+  const float ks = k_scale ? k_scale[si] : 1.0f;
+  const float vs = v_scale ? v_scale[si] : 1.0f;
   const int64_t row = (tok * hkv + h) * dim;
   const int64_t base = (page * hkv + h) * block_bytes + (int64_t)(t >> 4) * 16 * dim;
   put_fp8_chunk<FMT>(k + row, v + row, c, t16, ks, vs, kc, vc, base);
@@ -146,6 +196,19 @@ hipError_t kvq_launch_amax(const uint16_t* x0, int64_t n0, const uint16_t* x1, i
   return hipGetLastError();
 }
 
+hipError_t kvq_launch_amax_heads(const uint16_t* x0, int64_t rows0, const uint16_t* x1, int64_t rows1, int hkv,
+                                 int dim, unsigned* scratch, float fmt_div, float* scale_out, hipStream_t s) {
+  // at most kAmaxBlocks partials in the scratch buffer, split over the heads
+  const int64_t items = (rows0 + rows1) * (dim / 8);
+  int per_head = (int)((items + 256 * 16 - 1) / (256 * 16));
+  const int cap = kAmaxBlocks / hkv;
+  per_head = per_head < 1 ? 1 : (per_head > cap ? cap : per_head);
+  if (cap < 1) return hipErrorInvalidValue;
+  amax_head_partial_kernel<<<dim3(per_head, hkv), 256, 0, s>>>(x0, rows0, x1, rows1, hkv, dim, scratch);
+  amax_head_final_kernel<<<hkv, 256, 0, s>>>(scratch, per_head, fmt_div, scale_out);
+  return hipGetLastError();
+}
+
 hipError_t kvq_launch_store(const kvq_cache* c, const uint16_t* k, const uint16_t* v, const int64_t* slots,
                             int32_t n, const float* k_scale, const float* v_scale, hipStream_t s) {
   const kvq_cache_desc& d = c->desc;
@@ -157,11 +220,13 @@ hipError_t kvq_launch_store(const kvq_cache* c, const uint16_t* k, const uint16_
     const int grid = (int)((threads + 255) / 256);
     if (d.dtype == KVQ_FP8_E4M3)
       store_fp8_kernel<KVQ_FP8_E4M3><<<grid, 256, 0, s>>>(k, v, slots, n, d.num_kv_heads, d.head_dim, d.page_size,
-                                                         capacity, k_scale, v_scale, base + L.k_codes_offset,
+                                                         capacity, k_scale, v_scale, d.scale_per_head,
+                                                         base + L.k_codes_offset,
                                                          base + L.v_codes_offset, c->code_block_bytes);
     else
       store_fp8_kernel<KVQ_FP8_E5M2><<<grid, 256, 0, s>>>(k, v, slots, n, d.num_kv_heads, d.head_dim, d.page_size,
-                                                         capacity, k_scale, v_scale, base + L.k_codes_offset,
+                                                         capacity, k_scale, v_scale, d.scale_per_head,
+                                                         base + L.k_codes_offset,
                                                          base + L.v_codes_offset, c->code_block_bytes);
   } else if (d.dtype == KVQ_FP4_MX16) {
     const int64_t threads = (int64_t)n * d.num_kv_heads * (d.head_dim / 16);

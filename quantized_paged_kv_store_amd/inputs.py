@@ -41,7 +41,7 @@ class Workload:
     min_len: int               # == max_len for fixed-length workloads
     new_tokens: int            # tokens stored per sequence by the timed step
     dist: str                  # "tiny" | "llama" | "qwen" | "mla"
-    scale_mode: str = "amax"   # FP8: "amax" (calibrated) | "one"
+    scale_mode: str = "amax"   # FP8: "amax" (calibrated per tensor) | "amax_head" (per KV head) | "one"
     seed: int = 1
     extra: dict = field(default_factory=dict)
 

@@ -28,7 +28,7 @@ class KVQError(RuntimeError):
 
 class CacheDesc(ctypes.Structure):
     _fields_ = [("dtype", c_int32), ("kind", c_int32), ("num_kv_heads", c_int32), ("head_dim", c_int32),
-                ("v_dim", c_int32), ("page_size", c_int32), ("num_pages", c_int64)]
+                ("v_dim", c_int32), ("page_size", c_int32), ("num_pages", c_int64), ("scale_per_head", c_int32)]
 
 
 class Layout(ctypes.Structure):
@@ -97,8 +97,9 @@ def _stream(device) -> c_void_p:
 
 
 def make_desc(dtype: str, kind: str, num_kv_heads: int, head_dim: int, v_dim: int, page_size: int,
-              num_pages: int) -> CacheDesc:
-    return CacheDesc(DTYPES[dtype], KINDS[kind], num_kv_heads, head_dim, v_dim, page_size, num_pages)
+              num_pages: int, scale_per_head: bool = False) -> CacheDesc:
+    return CacheDesc(DTYPES[dtype], KINDS[kind], num_kv_heads, head_dim, v_dim, page_size, num_pages,
+                     1 if scale_per_head else 0)
 
 
 def kvq_bytes_per_token(desc: CacheDesc) -> float:
@@ -140,8 +141,8 @@ class Cache:
 
 
 def kvq_alloc_pages(dtype: str, kind: str, num_kv_heads: int, head_dim: int, v_dim: int, page_size: int,
-                    num_pages: int, device="cuda", fill: int | None = None) -> Cache:
-    desc = make_desc(dtype, kind, num_kv_heads, head_dim, v_dim, page_size, num_pages)
+                    num_pages: int, device="cuda", fill: int | None = None, scale_per_head: bool = False) -> Cache:
+    desc = make_desc(dtype, kind, num_kv_heads, head_dim, v_dim, page_size, num_pages, scale_per_head)
     need = c_size_t()
     _check(_lib().kvq_alloc_pages(byref(desc), None, 0, byref(need), None), "kvq_alloc_pages(query)")
     mem = torch.empty(need.value, dtype=torch.uint8, device=device)
@@ -150,20 +151,26 @@ def kvq_alloc_pages(dtype: str, kind: str, num_kv_heads: int, head_dim: int, v_d
     return Cache(desc, mem)
 
 
-def _dev_f32(x, device):
+def _dev_f32(x, device, n=1):
+    """A device fp32 scale: n >= 1 values (n = num_kv_heads for per-head FP8 scales)."""
     if x is None:
         return None
     if not isinstance(x, torch.Tensor):
-        x = torch.tensor([float(x)], dtype=torch.float32, device=device)
-    assert x.dtype == torch.float32 and x.device == device and x.numel() >= 1
+        x = torch.tensor([float(v) for v in (x if hasattr(x, "__len__") else [x])], dtype=torch.float32,
+                         device=device)
+    assert x.dtype == torch.float32 and x.device == device and x.is_contiguous() and x.numel() >= n
     return x
+
+
+def _n_scales(cache: "Cache") -> int:
+    return cache.desc.num_kv_heads if cache.desc.scale_per_head else 1
 
 
 def kvq_compute_scale(cache: Cache, x0: torch.Tensor, x1: torch.Tensor | None = None,
                       out: torch.Tensor | None = None) -> torch.Tensor:
     dev = cache.device
     if out is None:
-        out = torch.empty(1, dtype=torch.float32, device=dev)
+        out = torch.empty(_n_scales(cache), dtype=torch.float32, device=dev)
     for x in (x0, x1):
         if x is not None:
             assert x.dtype == torch.bfloat16 and x.is_contiguous() and x.device == dev
@@ -179,7 +186,7 @@ def kvq_store(cache: Cache, k: torch.Tensor, v: torch.Tensor | None, slot_mappin
     if v is not None:
         assert v.dtype == torch.bfloat16 and v.is_contiguous() and v.device == dev
     assert slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous() and slot_mapping.device == dev
-    ks, vs = _dev_f32(k_scale, dev), _dev_f32(v_scale, dev)
+    ks, vs = _dev_f32(k_scale, dev, _n_scales(cache)), _dev_f32(v_scale, dev, _n_scales(cache))
     _check(_lib().kvq_store(cache.handle, _ptr(k), _ptr(v), _ptr(slot_mapping), slot_mapping.numel(), _ptr(ks),
                             _ptr(vs), _stream(dev)), "kvq_store")
 
@@ -203,7 +210,7 @@ def kvq_decode(cache: Cache, q: torch.Tensor, page_table: torch.Tensor, seq_lens
     need = kvq_decode_workspace_bytes(cache, B, Hq, max_seq_len)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ks, vs = _dev_f32(k_scale, dev), _dev_f32(v_scale, dev)
+    ks, vs = _dev_f32(k_scale, dev, _n_scales(cache)), _dev_f32(v_scale, dev, _n_scales(cache))
     _check(_lib().kvq_decode(cache.handle, _ptr(q), B, Hq, _ptr(page_table), page_table.shape[1], _ptr(seq_lens),
                              max_seq_len, float(sm_scale), _ptr(ks), _ptr(vs), _ptr(out), _ptr(lse),
                              _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(dev)),
@@ -232,7 +239,7 @@ def kvq_decode_append(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor | N
     need = kvq_decode_workspace_bytes(cache, B, Hq, max_seq_len)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ks, vs = _dev_f32(k_scale, dev), _dev_f32(v_scale, dev)
+    ks, vs = _dev_f32(k_scale, dev, _n_scales(cache)), _dev_f32(v_scale, dev, _n_scales(cache))
     _check(_lib().kvq_decode_append(cache.handle, _ptr(k_new), _ptr(v_new), _ptr(q), B, Hq, _ptr(page_table),
                                     page_table.shape[1], _ptr(seq_lens), max_seq_len, float(sm_scale), _ptr(ks),
                                     _ptr(vs), _ptr(out), _ptr(lse), _ptr(workspace),

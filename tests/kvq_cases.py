@@ -87,7 +87,8 @@ class Case:
         w = self.w
         assert not append or w.new_tokens == 1
         self.cache = K.kvq_alloc_pages(w.dtype, w.kind, w.kv_heads, w.head_dim, w.v_dim, w.page_size,
-                                       self.npages, device=self.dev, fill=FILL[w.dtype])
+                                       self.npages, device=self.dev, fill=FILL[w.dtype],
+                                       scale_per_head=w.scale_mode == "amax_head")
         pre = [(b, 0, int(self.prefill[b])) for b in range(w.batch) if self.prefill[b] > 0]
         new = [(b, int(self.prefill[b]), int(self.lens[b])) for b in range(w.batch) if self.lens[b] > self.prefill[b]]
         if self.data is None:
@@ -97,7 +98,7 @@ class Case:
         if kp is not None and len(kp):
             kd, sd = self._bf16(kp), self._to_dev(sp)
             vd = None if vp is None else self._bf16(vp)
-            if w.dtype in ("e4m3", "e5m2") and w.scale_mode == "amax":
+            if w.dtype in ("e4m3", "e5m2") and w.scale_mode in ("amax", "amax_head"):
                 if w.dist == "tiny":   # one scale for K and V jointly
                     self.k_scale = K.kvq_compute_scale(self.cache, kd, vd)
                     self.v_scale = self.k_scale
@@ -112,9 +113,13 @@ class Case:
             self.k_scale = torch.ones(1, dtype=torch.float32, device=self.dev)
         self.host_amax = None
         if kp is not None and len(kp):
-            ak = float(np.abs(I.bf16_to_f32(kp)).max())
-            av = None if vp is None else float(np.abs(I.bf16_to_f32(vp)).max())
-            self.host_amax = (ak, av)
+            if w.scale_mode == "amax_head":     # [Hkv] magnitudes per head (BF16 bits order like values)
+                mag = lambda a: I.bf16_to_f32((a.reshape(len(a), w.kv_heads, -1) & 0x7FFF).max(axis=(0, 2)).astype(np.uint16))
+                self.host_amax = (mag(kp), None if vp is None else mag(vp))
+            else:
+                ak = float(np.abs(I.bf16_to_f32(kp)).max())
+                av = None if vp is None else float(np.abs(I.bf16_to_f32(vp)).max())
+                self.host_amax = (ak, av)
         del kp, vp
         kn, vn, sn = self.data["new"]
         self.new_inputs = (kn, vn, sn)
@@ -147,7 +152,10 @@ class Case:
         return self
 
     def gpu_scales(self):
-        f = lambda t: None if t is None else np.float32(t.cpu().numpy()[0])
+        if self.w.scale_mode == "amax_head":
+            f = lambda t: None if t is None else t.cpu().numpy().astype(np.float32)
+        else:
+            f = lambda t: None if t is None else np.float32(t.cpu().numpy()[0])
         return f(self.k_scale), f(self.v_scale)
 
     # -------------------------------------------------------------- oracle --
@@ -156,6 +164,13 @@ class Case:
         if self.host_amax is None:
             return (np.float32(1.0) if w.dtype == "nvfp4" else None), None
         ak, av = self.host_amax
+        if w.dtype in ("e4m3", "e5m2") and w.scale_mode == "amax_head":
+            fmt = E4M3 if w.dtype == "e4m3" else E5M2
+            per_head = lambda a: Q.fp8_head_scales(np.asarray(a, np.float64)[None, :, None], fmt)
+            if w.dist == "tiny":
+                s = per_head(np.maximum(ak, av))
+                return s, s
+            return per_head(ak), per_head(av)
         if w.dtype in ("e4m3", "e5m2") and w.scale_mode == "amax":
             fmt = E4M3 if w.dtype == "e4m3" else E5M2
             if w.dist == "tiny":

@@ -202,3 +202,32 @@ def test_decode_append_argument_errors(handles):
                                  None) == UNSUP
     assert lib.kvq_decode_append(h["fp8"], P, P, P, 0, 8, P, 4, P, 64, 0.1, None, None, P, None, None, 0,
                                  None) == OK                                       # empty batch
+
+
+def test_per_head_scale_descriptor_rules():
+    lib = _lib()
+    need = c_size_t()
+    d = _desc("e4m3")
+    d.scale_per_head = 1
+    assert lib.kvq_alloc_pages(byref(d), None, 0, byref(need), None) == OK
+    for dtype, kind, args in (("mx16", "gqa", ()), ("nvfp4", "mla", (1, 576, 512, 64))):
+        d = _desc(dtype, kind, *args)
+        d.scale_per_head = 1
+        assert lib.kvq_alloc_pages(byref(d), None, 0, byref(need), None) == UNSUP
+    d = _desc("e4m3")
+    d.scale_per_head = 2
+    assert lib.kvq_alloc_pages(byref(d), None, 0, byref(need), None) == ARG
+
+
+def test_per_head_compute_scale_shape_errors():
+    lib = _lib()
+    d = _desc("e4m3", hkv=4)
+    d.scale_per_head = 1
+    need = c_size_t()
+    h = c_void_p()
+    assert lib.kvq_alloc_pages(byref(d), None, 0, byref(need), None) == OK
+    assert lib.kvq_alloc_pages(byref(d), c_void_p(FAKE_DEV), need.value, byref(need), byref(h)) == OK
+    P = c_void_p(FAKE_DEV)
+    assert lib.kvq_compute_scale(h, P, 4 * 128 + 1, None, 0, P, None) == ARG          # not whole rows
+    assert lib.kvq_compute_scale(h, c_void_p(FAKE_DEV + 2), 4 * 128, None, 0, P, None) == ARG  # unaligned
+    lib.kvq_free_handle(h)

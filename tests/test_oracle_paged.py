@@ -84,3 +84,23 @@ def test_negative_slots_are_skipped():
     byte, _ = k_code_pos(spec, np.array([3]), np.arange(64))
     assert np.all(cache.k_codes[0, 0, byte] == 0x38)
     assert np.count_nonzero(cache.k_codes != 0x11) == 2 * 64
+
+
+def test_per_head_scales_round_trip_on_grid():
+    """Per-head FP8 store: values built as (E4M3 value) * s_h round-trip
+    exactly through store + dequant with the per-head scale array, and head h
+    never uses another head's scale."""
+    spec = CacheSpec("e4m3", "gqa", 3, 64, 64, 16, 4)
+    rng = np.random.default_rng(13)
+    grid = F.decode(np.arange(0, 0x7F), F.E4M3)           # finite non-negative E4M3 values
+    s = np.array([0.25, 3.0, 0.0078125], np.float32)
+    vals = rng.choice(grid, size=(20, 3, 64)) * rng.choice([-1, 1], size=(20, 3, 64))
+    k = vals * s[None, :, None]
+    v = vals[::-1] * s[None, :, None]
+    oc = OracleCache(spec)
+    slots = rng.permutation(4 * 16)[:20]
+    oc.store(k, v, slots, k_scale=s, v_scale=s)
+    page, t = slots // 16, slots % 16
+    for h in range(3):
+        assert np.array_equal(oc.dequant(page, t, h, "k", s, s), k[:, h])
+        assert np.array_equal(oc.dequant(page, t, h, "v", s, s), v[:, h])

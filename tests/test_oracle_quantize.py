@@ -162,3 +162,34 @@ def test_nvfp4_error_bound():
     assert np.all(err <= 1.0 * mult + 1e-12)
     rel = np.linalg.norm(x - xh) / np.linalg.norm(x)
     assert 0.05 < rel < 0.15
+
+
+# ------------------------------------------------------ FP8 per KV head ----
+@pytest.mark.parametrize("fmt", [F.E4M3, F.E5M2])
+def test_fp8_head_scales_map_each_head_max_to_format_max(fmt):
+    """vLLM page, "Supported schemes": one scale per KV head. Each head's own
+    largest magnitude must land exactly on the format maximum."""
+    rng = np.random.default_rng(11)
+    x = bf16_to_f32(bf16_bits(rng.standard_normal((300, 4, 64)) * np.array([0.01, 1.0, 30.0, 500.0])[:, None]))
+    x = x.astype(np.float64)
+    s = Q.fp8_head_scales(x, fmt)
+    assert s.shape == (4,) and s.dtype == np.float32
+    for h in range(4):
+        i = np.unravel_index(np.abs(x[:, h]).argmax(), x[:, h].shape)
+        code = Q.quantize_fp8(np.array([abs(x[:, h][i])]), s[h], fmt)[0]
+        assert F.decode(np.array([code]), fmt)[0] == fmt.max_value
+        # head h alone, calibrated per tensor, is the same quantization
+        assert s[h] == Q.fp8_scale(np.abs(x[:, h]).max(), fmt)
+
+
+def test_fp8_head_scales_power_of_two_heads_share_codes():
+    """Heads that differ by exact powers of two get scales that differ by the
+    same factor and identical codes (a wrong axis or a shared amax breaks it)."""
+    rng = np.random.default_rng(12)
+    base = bf16_to_f32(bf16_bits(rng.standard_normal((200, 1, 32)))).astype(np.float64)
+    x = np.concatenate([base * 2.0 ** k for k in (-6, 0, 3, 9)], axis=1)
+    s = Q.fp8_head_scales(x, F.E4M3)
+    assert np.all(s[1:] / s[:-1] == np.array([2.0 ** 6, 2.0 ** 3, 2.0 ** 6], np.float32))
+    codes = [Q.quantize_fp8(x[:, h], s[h], F.E4M3) for h in range(4)]
+    for c in codes[1:]:
+        assert np.array_equal(c, codes[0])
