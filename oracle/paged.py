@@ -239,3 +239,34 @@ class OracleCache:
             return Q.dequantize_mx16(codes, sc)
         sc = self.k_scales[page[:, None], head, k_scale_pos(s, t[:, None], b)]
         return Q.dequantize_nvfp4(codes, sc, k_scale)
+
+
+# --------------------------------------------------------------------------
+# dequantize_prev_kv (PR #21954 analysis page, "code analysis"): the FP4
+# cache and its scales are turned into FP8 E4M3 (the dq_k_buffer /
+# dq_v_buffer workspaces that create_buffers allocates) so that an FP8
+# prefill kernel can read the quantized prefix; the review notes on the same
+# page explain the FP8 target by the absence of an FP4 prefill kernel.
+# Reading adopted (the page gives no formula): every token row of the listed
+# pages is dequantized exactly and rounded once to binary32 (MX16: e2m1 * 2^e,
+# exact; NVFP4: e2m1 * e4m3 * g), then re-encoded as E4M3 with a per-tensor
+# scale s: code = encode_E4M3(fl32(x^ / s)), round to nearest even,
+# saturating (s = None: 1.0). Output rows are token-major: GQA
+# [n_pages, Hkv, page_size, D] for K and V, MLA [n_pages, page_size, Dk].
+# --------------------------------------------------------------------------
+def dequantize_prev_kv(cache: "OracleCache", pages, k_scale_out=None, v_scale_out=None, g=None):
+    s = cache.spec
+    assert s.dtype in ("mx16", "nvfp4")
+    pages = np.asarray(pages, dtype=np.int64)
+    t = np.arange(s.page_size)
+    out = []
+    for which in (("k", "v") if s.kind == "gqa" else ("k",)):
+        sc = np.float32(1.0 if (k_scale_out if which == "k" else v_scale_out) is None
+                        else (k_scale_out if which == "k" else v_scale_out))
+        res = np.zeros((len(pages), s.num_kv_heads, s.page_size, s.head_dim), np.uint8)
+        for i, pg in enumerate(pages):
+            for h in range(s.num_kv_heads):
+                x_hat = Q.fl32(cache.dequant(np.full(s.page_size, pg), t, h, which, g))
+                res[i, h] = Q.quantize_fp8(x_hat, sc, E4M3)
+        out.append(res if s.kind == "gqa" else res[:, 0])
+    return out[0], (out[1] if s.kind == "gqa" else None)

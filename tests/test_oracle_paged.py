@@ -104,3 +104,71 @@ def test_per_head_scales_round_trip_on_grid():
     for h in range(3):
         assert np.array_equal(oc.dequant(page, t, h, "k", s, s), k[:, h])
         assert np.array_equal(oc.dequant(page, t, h, "v", s, s), v[:, h])
+
+
+# ------------------------------------------------------ dequantize_prev_kv ----
+from oracle.paged import dequantize_prev_kv  # noqa: E402
+
+
+def test_dequantize_prev_kv_identity_on_e4m3_grid():
+    """MX16 blocks whose values E2M1 * 2^e are all E4M3 numbers (e in
+    [-6, 6]) come back unchanged through FP4 -> FP8 with scale 1: every code
+    decodes to exactly the dequantized FP4 value."""
+    spec = CacheSpec("mx16", "gqa", 2, 128, 128, 16, 3)
+    rng = np.random.default_rng(41)
+    e2m1 = F.decode(np.arange(16), F.E2M1)
+    # 16-element blocks: E2M1 values with the block max 4 or 6 (so the store
+    # reproduces the exponent), times 2^e
+    blocks = rng.choice(e2m1, size=(40, 2, 8, 16))
+    blocks[..., 0] = rng.choice([4.0, 6.0, -4.0, -6.0], size=blocks.shape[:-1])
+    e = rng.integers(-6, 5, size=blocks.shape[:-1] + (1,))
+    x = (blocks * 2.0 ** e).reshape(40, 2, 128)
+    oc = OracleCache(spec)
+    slots = rng.permutation(48)[:40]
+    oc.store(x, -x, slots)
+    used = np.unique(slots // 16)
+    dk, dv = dequantize_prev_kv(oc, used)
+    for i, pg in enumerate(used):
+        for h in range(2):
+            xk = oc.dequant(np.full(16, pg), np.arange(16), h, "k")
+            xv = oc.dequant(np.full(16, pg), np.arange(16), h, "v")
+            assert np.array_equal(F.decode(dk[i, h], F.E4M3), xk)
+            assert np.array_equal(F.decode(dv[i, h], F.E4M3), xv)
+
+
+def test_dequantize_prev_kv_scale_and_saturation():
+    """code = RNE_sat(x^ / s): doubling s halves every decoded value exactly
+    (powers of two), and a scale small enough to overflow saturates at 448."""
+    spec = CacheSpec("mx16", "gqa", 1, 128, 128, 16, 1)
+    rng = np.random.default_rng(42)
+    x = rng.standard_normal((16, 1, 128))
+    oc = OracleCache(spec)
+    oc.store(x, x, np.arange(16))
+    d1, _ = dequantize_prev_kv(oc, [0], 1.0, 1.0)
+    d2, _ = dequantize_prev_kv(oc, [0], 2.0, 2.0)
+    f1, f2 = F.decode(d1, F.E4M3), F.decode(d2, F.E4M3)
+    normal = np.abs(f1) >= 2.0 ** -5            # both stay in E4M3's normal range
+    assert np.array_equal(f2[normal], f1[normal] / 2)
+    ds, _ = dequantize_prev_kv(oc, [0], 1e-6, 1e-6)
+    big = np.abs(oc.dequant(np.zeros(16, int), np.arange(16), 0, "k")) > 448e-6
+    assert np.all(np.abs(F.decode(ds[0, 0], F.E4M3))[big] == 448.0)
+
+
+def test_dequantize_prev_kv_nvfp4_error_bound():
+    """NVFP4 -> E4M3 with s = 6 g: |dec(code) * s - x^| <= 2^-4 |x^| in E4M3's
+    normal range (one RNE rounding to a 4-bit significand)."""
+    spec = CacheSpec("nvfp4", "mla", 1, 576, 512, 64, 2)
+    rng = np.random.default_rng(43)
+    x = rng.standard_normal((100, 576)) * np.where(rng.random(576) < 0.03, 8.0, 1.0)
+    g = Q.nvfp4_global_scale(np.abs(x).max())
+    oc = OracleCache(spec)
+    oc.store(x, None, np.arange(100), k_scale=g)
+    s = np.float32(np.float32(6.0) * g)
+    dk, dv = dequantize_prev_kv(oc, [0, 1], s, None, g)
+    assert dv is None and dk.shape == (2, 64, 576)
+    for i in range(2):
+        x_hat = oc.dequant(np.full(64, i), np.arange(64), 0, "k", g)
+        back = F.decode(dk[i], F.E4M3) * float(s)
+        normal = np.abs(x_hat) >= 2.0 ** -6 * float(s)
+        assert np.all(np.abs(back - x_hat)[normal] <= 2.0 ** -4 * np.abs(x_hat)[normal] * (1 + 1e-6))
+        assert np.all(np.abs(back) <= 448.0 * float(s))
