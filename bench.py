@@ -220,6 +220,93 @@ def cpu_baseline(w, seconds_hint=20.0):
             "decode_s": round(t_dec, 3), "codec_s": round(t_codec, 3)}
 
 
+def dequant_prev_cpu_baseline(w, n_pages=None):
+    """The oracle's dequantize_prev_kv, untuned, on the pages of sequence 0
+    of the same workload (at most 2,048 pages)."""
+    from oracle import quantize as Q
+    from oracle.paged import CacheSpec, OracleCache, dequantize_prev_kv
+    from quantized_paged_kv_store_amd import inputs as I
+
+    P = w.page_size
+    if n_pages is None:
+        n_pages = min(2048, int(I.seq_lens(w)[0]) // P)
+    L = n_pages * P
+    k, v = I.kv_rows(w, 0, 0, L)
+    kf = I.bf16_to_f32(k)
+    vf = None if v is None else I.bf16_to_f32(v)
+    g = Q.nvfp4_global_scale(np.abs(kf).max()) if w.dtype == "nvfp4" else None
+    oc = OracleCache(CacheSpec(w.dtype, w.kind, w.kv_heads, w.head_dim, w.v_dim, P, n_pages))
+    oc.store(kf, vf, np.arange(L), k_scale=g)
+    t0 = time.perf_counter()
+    dequantize_prev_kv(oc, np.arange(n_pages), 0.02, None if w.kind == "mla" else 0.01, g=g)
+    dt = time.perf_counter() - t0
+    rows = 2 * w.kv_heads if w.kind == "gqa" else 1
+    nbytes = L * rows * w.head_dim * (4.5 / 8 + 1.0)
+    return {"value": round(nbytes / dt / 1e9, 6), "unit": "GB/s", "cores": 1,
+            "host_cores_available": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{n_pages} pages ({L} tokens, all {w.kv_heads} KV heads) of sequence 0: "
+                      f"oracle dequantize_prev_kv {dt:.2f} s"}
+
+
+def bench_dequant_prev(w, args, dev):
+    """kvq_dequantize_prev_kv over every page of the workload's cache: the
+    FP4 prefix turned into E4M3 rows for an FP8 prefill kernel."""
+    import torch
+
+    import quantized_paged_kv_store_amd as K
+    t0 = time.time()
+    st = setup(w, dev, args.rotate)
+    log(f"setup {time.time() - t0:.1f} s")
+    caches = st["caches"]
+    d = caches[0].desc
+    npages = d.num_pages
+    pages = torch.arange(npages, dtype=torch.int32, device=dev)
+    g = st["ks"] if w.kind == "mla" else None
+    ks_out = torch.tensor([0.02], dtype=torch.float32, device=dev)
+    vs_out = None if w.kind == "mla" else torch.tensor([0.01], dtype=torch.float32, device=dev)
+    dk, dv = K.kvq_dequantize_prev_kv(caches[0], pages, ks_out, vs_out, g=g)
+
+    def loop(n, off=0):
+        for i in range(n):
+            K.kvq_dequantize_prev_kv(caches[(i + off) % len(caches)], pages, ks_out, vs_out, g=g, dq_k=dk, dq_v=dv)
+
+    loop(args.warmup)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    loop(args.steps)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    K.kvq_profile_enable(True)
+    loop(args.steps)
+    torch.cuda.synchronize()
+    tot, n = K.kvq_profile_read("dequant_prev")
+    K.kvq_profile_enable(False)
+    kern_ms = tot / max(n, 1)
+    rows = 2 * d.num_kv_heads if w.kind == "gqa" else 1
+    elems = float(npages) * d.page_size * rows * d.head_dim
+    read_b, write_b = elems * (0.5 + 1 / 16), elems * 1.0
+    value = (read_b + write_b) / (ms * 1e-3) / 1e9
+    ach = (read_b + write_b) / (kern_ms * 1e-3) / 1e9
+    res = {
+        "metric": "dequantize_prev_kv effective GB/s (FP4 pages read + E4M3 rows written)", "value": round(value, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{w.name}: every page of the cache ({npages} pages of {d.page_size} tokens, "
+                               f"{d.num_kv_heads} kv head(s), head_dim {d.head_dim}, {w.dtype}) -> E4M3",
+                   "cache_copies_rotated": args.rotate},
+        "roofline": {"bound": "hbm", "achieved": round(ach, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "kernel": f"dequant_prev_{'nvfp4' if w.kind == 'mla' else 'mx16'}_kernel",
+                     "kernel_ms": round(kern_ms, 5), "algorithmic_bytes_per_launch": read_b + write_b},
+        "pct_hbm_peak": round(100 * value / PEAK_HBM_GBPS, 2),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = dequant_prev_cpu_baseline(w)
+    print(json.dumps(res), flush=True)
+
+
 def copy_reference(nbytes=1 << 30, reps=10):
     """A plain device copy of known size (src -> dst), the reference the HBM
     traffic counters are scaled by."""
@@ -249,6 +336,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true", help="replay captured HIP graphs instead of eager launches")
     ap.add_argument("--copy-ref", action="store_true", help="only run the 1 GiB reference copy (for counters)")
+    ap.add_argument("--dequant-prev", action="store_true",
+                    help="FP4 workloads: time kvq_dequantize_prev_kv over every page instead of the decode step")
     ap.add_argument("--per-head-scales", action="store_true",
                     help="FP8 workloads: one calibrated k/v scale per KV head instead of per tensor")
     args = ap.parse_args()
@@ -269,6 +358,10 @@ def main():
         assert w.dtype in ("e4m3", "e5m2"), "per-head scales apply to FP8 caches"
         w = w.with_(scale_mode="amax_head")
     dev = torch.device("cuda:0")
+    if args.dequant_prev:
+        assert w.dtype in ("mx16", "nvfp4"), "dequantize_prev_kv reads FP4 caches"
+        bench_dequant_prev(w, args, dev)
+        return
     t0 = time.time()
     st = setup(w, dev, args.rotate)
     log(f"setup {time.time() - t0:.1f} s")

@@ -231,12 +231,35 @@ int kvq_decode_append(const kvq_cache* cache, const void* k_new, const void* v_n
                       float sm_scale, const float* k_scale, const float* v_scale, float* out,
                       float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* dequantize_prev_kv ([P4] "code analysis"): turn listed pages of an FP4
+ * cache into FP8 E4M3 rows, the dq_k / dq_v workspaces an FP8 prefill kernel
+ * reads when a new chunk attends to an already quantized prefix (the pages
+ * have no FP4 prefill kernel). Every element is dequantized exactly and
+ * rounded once to binary32 (MX16: e2m1 * 2^(c-127); NVFP4: e2m1 * e4m3 * g),
+ * then code = RNE_sat_E4M3(x^ / s) with the per-tensor output scale s
+ * (binary32 division, saturating at +-448).
+ *   pages:       [dev] int32 [n_pages] page ids; an id outside
+ *                [0, num_pages) yields all-zero rows.
+ *   g_scale:     [dev] fp32, NVFP4 global scale g (required); unused for MX16.
+ *   k_scale_out, v_scale_out: [dev] fp32 output scales s, NULL = 1.0; each
+ *                must be positive and finite. MLA: v_scale_out must be NULL.
+ *   dq_k, dq_v:  [dev] E4M3 bytes, 16-byte aligned, written token-major:
+ *                GQA [n_pages][num_kv_heads][page_size][head_dim] each;
+ *                MLA dq_k = [n_pages][page_size][head_dim] latent rows
+ *                (V is their first v_dim elements), dq_v must be NULL.
+ * Reads the cache only; n_pages = 0 launches nothing.
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED (FP8 caches), KVQ_ERR_HIP. */
+int kvq_dequantize_prev_kv(const kvq_cache* cache, const int32_t* pages, int32_t n_pages,
+                           const float* g_scale, const float* k_scale_out, const float* v_scale_out,
+                           void* dq_k, void* dq_v, void* stream);
+
 /* Instrumentation (off by default). While enabled, every kernel launched by
- * kvq_store / kvq_decode(_append) / kvq_compute_scale is bracketed by two HIP events
+ * kvq_store / kvq_decode(_append) / kvq_compute_scale / kvq_dequantize_prev_kv is
+ * bracketed by two HIP events
  * recorded on the call's stream (nothing else changes; do not enable while
  * capturing a HIP graph). Enabling or disabling clears the records.
  * kvq_profile_read synchronizes the recorded events and returns, for one
- * kernel family ("store", "decode", "merge", "amax"), the summed device
+ * kernel family ("store", "decode", "merge", "amax", "dequant_prev"), the summed device
  * time in milliseconds and the number of launches, then forgets them.
  * Errors: KVQ_ERR_ARG (unknown name, null outputs), KVQ_ERR_HIP. */
 int kvq_profile_enable(int on);

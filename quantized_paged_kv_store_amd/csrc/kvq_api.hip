@@ -153,10 +153,11 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 // ------------------------------------------------------------ instrumentation
 struct ProfRecord {
-  int family;  // 0 store, 1 decode, 2 merge, 3 amax
+  int family;  // 0 store, 1 decode, 2 merge, 3 amax, 4 dequant_prev
   hipEvent_t start, stop;
 };
-const char* const kFamilies[] = {"store", "decode", "merge", "amax"};
+const char* const kFamilies[] = {"store", "decode", "merge", "amax", "dequant_prev"};
+constexpr int kNumFamilies = 5;
 std::mutex g_prof_mu;
 bool g_prof_on = false;
 std::vector<ProfRecord> g_prof;
@@ -175,7 +176,7 @@ hipEvent_t take_event() {
 
 void clear_records_locked() {
   for (auto& r : g_prof) {
-    hipEventSynchronize(r.stop);
+    (void)hipEventSynchronize(r.stop);
     g_event_pool.push_back(r.start);
     g_event_pool.push_back(r.stop);
   }
@@ -192,11 +193,11 @@ struct Timed {
     if (!g_prof_on) return;
     start = take_event();
     stop = take_event();
-    if (start && stop) hipEventRecord(start, stream);
+    if (start && stop) (void)hipEventRecord(start, stream);
   }
   ~Timed() {
     if (!start || !stop) return;
-    hipEventRecord(stop, stream);
+    (void)hipEventRecord(stop, stream);
     std::lock_guard<std::mutex> lk(g_prof_mu);
     g_prof.push_back({family, start, stop});
   }
@@ -216,7 +217,7 @@ int kvq_profile_enable(int on) {
 int kvq_profile_read(const char* kernel, double* total_ms, int64_t* launches) {
   if (!kernel || !total_ms || !launches) return KVQ_ERR_ARG;
   int fam = -1;
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kNumFamilies; ++i)
     if (std::string(kernel) == kFamilies[i]) fam = i;
   if (fam < 0) return KVQ_ERR_ARG;
   std::lock_guard<std::mutex> lk(g_prof_mu);
@@ -510,6 +511,27 @@ int kvq_decode_append(const kvq_cache* c, const void* k_new, const void* v_new, 
   if (!k_new) return KVQ_ERR_ARG;
   return decode_impl(c, k_new, v_new, q, batch, hq, page_table, page_table_stride, seq_lens, max_len, sm_scale,
                      k_scale, v_scale, out, lse, ws, ws_bytes, stream);
+}
+
+int kvq_dequantize_prev_kv(const kvq_cache* c, const int32_t* pages, int32_t n_pages, const float* g_scale,
+                           const float* k_scale_out, const float* v_scale_out, void* dq_k, void* dq_v, void* stream) {
+  if (!c || n_pages < 0) return KVQ_ERR_ARG;
+  const kvq_cache_desc& d = c->desc;
+  if (d.dtype != KVQ_FP4_MX16 && d.dtype != KVQ_NVFP4) return KVQ_ERR_UNSUPPORTED;
+  if (d.kind == KVQ_GQA) {
+    if (n_pages > 0 && (!dq_v || !aligned16(dq_v))) return KVQ_ERR_ARG;
+  } else {
+    if (dq_v || v_scale_out || !g_scale) return KVQ_ERR_ARG;
+  }
+  if (n_pages == 0) return KVQ_OK;
+  if (!pages || !dq_k || !aligned16(dq_k)) return KVQ_ERR_ARG;
+  const int64_t threads = (int64_t)n_pages * d.num_kv_heads * d.page_size * (d.head_dim / 16);
+  if ((threads + 255) / 256 > INT32_MAX) return KVQ_ERR_UNSUPPORTED;
+  Timed timer(4, static_cast<hipStream_t>(stream));
+  const hipError_t e = kvq_launch_dequant_prev(c, pages, n_pages, g_scale, k_scale_out, v_scale_out,
+                                               static_cast<uint8_t*>(dq_k), static_cast<uint8_t*>(dq_v),
+                                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
 }  // extern "C"

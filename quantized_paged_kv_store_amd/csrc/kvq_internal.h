@@ -163,5 +163,8 @@ hipError_t kvq_launch_store(const kvq_cache* c, const uint16_t* k, const uint16_
 hipError_t kvq_launch_decode_gqa(const kvq_cache* c, const GqaDecodeArgs& a, hipStream_t s);
 hipError_t kvq_launch_decode_mla(const kvq_cache* c, const MlaDecodeArgs& a, hipStream_t s);
 hipError_t kvq_launch_combine(const CombineArgs& a, hipStream_t s);
+hipError_t kvq_launch_dequant_prev(const kvq_cache* c, const int32_t* pages, int32_t n_pages, const float* g_scale,
+                                   const float* ks_out, const float* vs_out, uint8_t* dq_k, uint8_t* dq_v,
+                                   hipStream_t s);
 hipError_t kvq_launch_amax_heads(const uint16_t* x0, int64_t rows0, const uint16_t* x1, int64_t rows1, int hkv,
                                  int dim, unsigned* scratch, float fmt_div, float* scale_out, hipStream_t s);

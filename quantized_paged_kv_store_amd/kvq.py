@@ -8,6 +8,7 @@ exception is raised.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from ctypes import POINTER, byref, c_char_p, c_double, c_float, c_int32, c_int64, c_size_t, c_void_p
 
@@ -70,6 +71,9 @@ def _lib():
                                         c_void_p, c_int32, c_float, c_void_p, c_void_p, c_void_p, c_void_p,
                                         c_void_p, c_size_t, c_void_p]
         L.kvq_decode_append.restype = c_int32
+        L.kvq_dequantize_prev_kv.argtypes = [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                             c_void_p, c_void_p]
+        L.kvq_dequantize_prev_kv.restype = c_int32
         L.kvq_profile_enable.argtypes = [c_int32]
         L.kvq_profile_enable.restype = c_int32
         L.kvq_profile_read.argtypes = [c_char_p, POINTER(c_double), POINTER(c_int64)]
@@ -248,6 +252,29 @@ def kvq_decode_append(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor | N
     return out, lse
 
 
+def kvq_dequantize_prev_kv(cache: Cache, pages: torch.Tensor, k_scale_out=None, v_scale_out=None, g=None,
+                           dq_k: torch.Tensor | None = None, dq_v: torch.Tensor | None = None):
+    """FP4 pages -> E4M3 rows (uint8). Returns (dq_k, dq_v): GQA
+    [n, Hkv, P, D] each; MLA (dq_k [n, P, Dk], None)."""
+    dev, d = cache.device, cache.desc
+    assert pages.dtype == torch.int32 and pages.is_contiguous() and pages.device == dev and pages.dim() == 1
+    n = pages.numel()
+    shape = (n, d.num_kv_heads, d.page_size, d.head_dim) if d.kind == KINDS["gqa"] else (n, d.page_size, d.head_dim)
+    if dq_k is None:
+        dq_k = torch.empty(shape, dtype=torch.uint8, device=dev)
+    if dq_v is None and d.kind == KINDS["gqa"]:
+        dq_v = torch.empty(shape, dtype=torch.uint8, device=dev)
+    for t in (dq_k, dq_v):
+        assert t is None or (t.dtype == torch.uint8 and t.is_contiguous() and t.device == dev
+                             and t.numel() >= math.prod(shape))
+    # the scale tensors stay referenced until the launch: a temporary freed
+    # inside the argument list would hand its block to the next one
+    gd, ksd, vsd = _dev_f32(g, dev), _dev_f32(k_scale_out, dev), _dev_f32(v_scale_out, dev)
+    _check(_lib().kvq_dequantize_prev_kv(cache.handle, _ptr(pages), n, _ptr(gd), _ptr(ksd), _ptr(vsd),
+                                         _ptr(dq_k), _ptr(dq_v), _stream(dev)), "kvq_dequantize_prev_kv")
+    return dq_k, dq_v
+
+
 def kvq_profile_enable(on: bool = True) -> None:
     """Bracket every library kernel launch with HIP events (instrumentation)."""
     _check(_lib().kvq_profile_enable(1 if on else 0), "kvq_profile_enable")
@@ -255,7 +282,7 @@ def kvq_profile_enable(on: bool = True) -> None:
 
 def kvq_profile_read(kernel: str) -> tuple[float, int]:
     """(summed device ms, launches) of one kernel family since the last read:
-    "store", "decode", "merge" or "amax"."""
+    "store", "decode", "merge", "amax" or "dequant_prev"."""
     ms, n = c_double(), c_int64()
     _check(_lib().kvq_profile_read(kernel.encode(), byref(ms), byref(n)), "kvq_profile_read")
     return ms.value, n.value

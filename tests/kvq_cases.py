@@ -46,9 +46,11 @@ def assert_close(got, want, what=""):
 
 
 class Case:
-    def __init__(self, w: I.Workload, device="cuda", identity=False, spare_pages=0, lens=None, data=None):
-        """data: the host inputs of another Case of the same seed/shape (reused)."""
+    def __init__(self, w: I.Workload, device="cuda", identity=False, spare_pages=0, lens=None, data=None, fill=None):
+        """data: the host inputs of another Case of the same seed/shape (reused);
+        fill: byte value of never-written slots (default FILL[dtype])."""
         self.w = w
+        self.fill = FILL[w.dtype] if fill is None else fill
         self.data = data
         self.dev = torch.device(device)
         self.lens = I.seq_lens(w) if lens is None else np.asarray(lens, np.int32)
@@ -87,7 +89,7 @@ class Case:
         w = self.w
         assert not append or w.new_tokens == 1
         self.cache = K.kvq_alloc_pages(w.dtype, w.kind, w.kv_heads, w.head_dim, w.v_dim, w.page_size,
-                                       self.npages, device=self.dev, fill=FILL[w.dtype],
+                                       self.npages, device=self.dev, fill=self.fill,
                                        scale_per_head=w.scale_mode == "amax_head")
         pre = [(b, 0, int(self.prefill[b])) for b in range(w.batch) if self.prefill[b] > 0]
         new = [(b, int(self.prefill[b]), int(self.lens[b])) for b in range(w.batch) if self.lens[b] > self.prefill[b]]
@@ -195,7 +197,7 @@ class Case:
             n = (int(self.lens[b]) + P - 1) // P
             otable[b, :n] = [remap[int(p)] for p in self.table[b, :n]]
         spec = CacheSpec(w.dtype, w.kind, w.kv_heads, w.head_dim, w.v_dim, P, max(len(pages), 1))
-        oc = OracleCache(spec, fill=FILL[w.dtype])
+        oc = OracleCache(spec, fill=self.fill)
         ks, vs = self.oracle_scales()
         for b in batch_ids:
             L = int(self.lens[b])

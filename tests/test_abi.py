@@ -231,3 +231,20 @@ def test_per_head_compute_scale_shape_errors():
     assert lib.kvq_compute_scale(h, P, 4 * 128 + 1, None, 0, P, None) == ARG          # not whole rows
     assert lib.kvq_compute_scale(h, c_void_p(FAKE_DEV + 2), 4 * 128, None, 0, P, None) == ARG  # unaligned
     lib.kvq_free_handle(h)
+
+
+def test_dequantize_prev_kv_argument_errors(handles):
+    lib, h = handles
+    P = c_void_p(FAKE_DEV)
+    f = lib.kvq_dequantize_prev_kv
+    assert f(h["fp8"], P, 4, None, None, None, P, P, None) == UNSUP               # FP4 caches only
+    assert f(h["mx"], P, 0, None, None, None, None, None, None) == OK              # no pages: no-op
+    assert f(h["mx"], P, -1, None, None, None, P, P, None) == ARG
+    assert f(h["mx"], None, 4, None, None, None, P, P, None) == ARG               # page list required
+    assert f(h["mx"], P, 4, None, None, None, None, P, None) == ARG               # dq_k required
+    assert f(h["mx"], P, 4, None, None, None, P, None, None) == ARG               # GQA needs dq_v
+    assert f(h["mx"], P, 4, None, None, None, c_void_p(FAKE_DEV + 8), P, None) == ARG  # 16-byte aligned
+    assert f(h["mla"], P, 4, None, None, None, P, None, None) == ARG              # NVFP4 needs g
+    assert f(h["mla"], P, 4, P, None, None, P, P, None) == ARG                    # MLA has no dq_v
+    assert f(h["mla"], P, 4, P, None, P, P, None, None) == ARG                    # nor a V output scale
+    assert f(None, P, 4, None, None, None, P, P, None) == ARG

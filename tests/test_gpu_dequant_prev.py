@@ -1,0 +1,147 @@
+"""GPU parity of kvq_dequantize_prev_kv (PR #21954 analysis page, "code
+analysis": FP4 pages turned into the FP8 E4M3 workspaces an FP8 prefill
+kernel reads) against the oracle's dequantize_prev_kv: every output byte
+bit-exact, on caches of seeded random bytes (every code and a wide range of
+scales, so saturation, signed zeros and E4M3 subnormals all occur) and on
+caches written by kvq_store from the workload inputs."""
+import numpy as np
+import pytest
+import torch
+
+import quantized_paged_kv_store_amd as K
+from oracle.paged import CacheSpec, OracleCache, dequantize_prev_kv
+from quantized_paged_kv_store_amd import inputs as I
+from tests.kvq_cases import Case
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _random_cache(dtype, kind, hkv, D, Dv, P, npages, seed, mx_codes=(0, 191)):
+    """The same seeded random bytes in a device cache and an oracle cache.
+    MX16 E8M0 codes are drawn from mx_codes (half of them near 127) and NVFP4
+    E4M3 block scales avoid the NaN codes, so that every dequantized value and
+    quotient is finite."""
+    spec = CacheSpec(dtype, kind, hkv, D, Dv, P, npages)
+    oc = OracleCache(spec)
+    cache = K.kvq_alloc_pages(dtype, kind, hkv, D, Dv, P, npages, device=DEV, fill=0)
+    rng = np.random.default_rng(seed)
+    for name in ("k_codes", "v_codes", "k_scales", "v_scales"):
+        arr = getattr(oc, name)
+        if arr is None:
+            continue
+        if name.endswith("codes"):
+            arr[...] = rng.integers(0, 256, arr.shape, dtype=np.uint8)
+        elif dtype == "mx16":     # half near the middle of the range, half over all of it
+            mid = (mx_codes[0] + mx_codes[1]) // 2
+            near = rng.integers(max(mx_codes[0], mid - 10), min(mx_codes[1], mid + 11), arr.shape)
+            wide = rng.integers(mx_codes[0], mx_codes[1], arr.shape)
+            arr[...] = np.where(rng.random(arr.shape) < 0.5, near, wide).astype(np.uint8)
+        else:                     # E4M3 magnitudes 0 .. 0x7E with a random sign
+            mag = rng.integers(0, 0x7F, arr.shape)
+            arr[...] = (mag | (rng.integers(0, 2, arr.shape) << 7)).astype(np.uint8)
+        cache.view(name).copy_(torch.from_numpy(arr.reshape(-1)))
+    return cache, oc
+
+
+def _dev_pages(pages):
+    return torch.from_numpy(np.asarray(pages, np.int32)).to(DEV)
+
+
+@pytest.mark.parametrize("P,scales", [(16, (None, None)), (16, (0.0123, 2.5)), (32, (0.37, 0.001953125)),
+                                      (48, (1e-3, 7.0))])
+def test_random_bytes_mx16(P, scales):
+    hkv, npages = 3, 11
+    cache, oc = _random_cache("mx16", "gqa", hkv, 128, 128, P, npages, seed=P)
+    pages = [7, 0, 10, 3, 3, 5]                       # any order, repeats allowed
+    ks, vs = scales
+    dk, dv = K.kvq_dequantize_prev_kv(cache, _dev_pages(pages), ks, vs)
+    wk, wv = dequantize_prev_kv(oc, pages, ks, vs)
+    assert dk.shape == (len(pages), hkv, P, 128)
+    assert np.array_equal(dk.cpu().numpy(), wk)
+    assert np.array_equal(dv.cpu().numpy(), wv)
+    # the random caches reach saturation, signed zeros and subnormal codes
+    got = dk.cpu().numpy()
+    assert np.any((got & 0x7F) == 0x7E) and np.any(got == 0x80) and np.any(((got & 0x78) == 0) & ((got & 7) != 0))
+
+
+@pytest.mark.parametrize("P,g,s", [(64, 0.0137, None), (64, 1.0, 0.25), (16, 3.5e-3, 0.03125), (32, 0.71, 5e-4)])
+def test_random_bytes_nvfp4_mla(P, g, s):
+    npages = 9
+    cache, oc = _random_cache("nvfp4", "mla", 1, 576, 512, P, npages, seed=100 + P)
+    pages = [8, 2, 0, 5]
+    dk, dv = K.kvq_dequantize_prev_kv(cache, _dev_pages(pages), s, None, g=g)
+    wk, wv = dequantize_prev_kv(oc, pages, s, None, g=g)
+    assert dv is None and wv is None
+    assert dk.shape == (len(pages), P, 576)
+    assert np.array_equal(dk.cpu().numpy(), wk)
+
+
+@pytest.mark.parametrize("ks,vs,codes", [(2.0 ** -110, 2.0 ** -105, (0, 143)), (2.0 ** 105, 2.0 ** 101, (200, 253)),
+                                         (0.5, 2.0 ** 102, (127, 225))])
+def test_random_bytes_mx16_scales_outside_fast_range(ks, vs, codes):
+    """Output scales outside [2^-100, 2^100]: the tables are built by direct
+    division; still bit-exact."""
+    cache, oc = _random_cache("mx16", "gqa", 2, 128, 128, 16, 6, seed=77, mx_codes=codes)
+    pages = [5, 1, 2]
+    dk, dv = K.kvq_dequantize_prev_kv(cache, _dev_pages(pages), ks, vs)
+    wk, wv = dequantize_prev_kv(oc, pages, ks, vs)
+    assert np.array_equal(dk.cpu().numpy(), wk) and np.array_equal(dv.cpu().numpy(), wv)
+    assert len(np.unique(wk)) > 16 and len(np.unique(wv)) > 16       # not all zero or saturated
+
+
+@pytest.mark.parametrize("g,s", [(2.0 ** -118, 2.0 ** -125), (0.6 * 2.0 ** -100, 2.0 ** -96),
+                                 (2.0 ** -103 * 1.37, 2.0 ** -110)])
+def test_random_bytes_nvfp4_scales_outside_fast_range(g, s):
+    """g or s outside [2^-100, 2^100]; with g = 2^-118 many x^ = e2m1 * e4m3 * g
+    round in the binary32 subnormal range before the division."""
+    cache, oc = _random_cache("nvfp4", "mla", 1, 576, 512, 16, 5, seed=78)
+    pages = [4, 0, 3]
+    dk, _ = K.kvq_dequantize_prev_kv(cache, _dev_pages(pages), s, None, g=g)
+    wk, _ = dequantize_prev_kv(oc, pages, s, None, g=g)
+    assert np.array_equal(dk.cpu().numpy(), wk)
+    assert len(np.unique(wk)) > 32
+
+
+def test_out_of_pool_pages_give_zero_rows_and_empty_list():
+    cache, oc = _random_cache("mx16", "gqa", 2, 128, 128, 16, 4, seed=5)
+    pages = [1, -1, 4, 2, 1 << 30]
+    dk, dv = K.kvq_dequantize_prev_kv(cache, _dev_pages(pages), 0.5, 0.5)
+    gk, gv = dk.cpu().numpy(), dv.cpu().numpy()
+    for i in (1, 2, 4):
+        assert not gk[i].any() and not gv[i].any()
+    wk, wv = dequantize_prev_kv(oc, [1, 2], 0.5, 0.5)
+    assert np.array_equal(gk[[0, 3]], wk) and np.array_equal(gv[[0, 3]], wv)
+    ek, ev = K.kvq_dequantize_prev_kv(cache, _dev_pages([]), 0.5, 0.5)
+    assert ek.numel() == 0 and ev.numel() == 0
+
+
+def _stored_check(c, ids, ks, vs):
+    """Dequantize every page of the pool in one call; compare the pages of
+    sequences `ids` with the oracle cache built from the same inputs (each
+    side with its own NVFP4 global scale: the oracle's from the host amax)."""
+    oc, _, pages, (g_oracle, _) = c.oracle(ids)
+    g_dev = c.k_scale if c.w.dtype == "nvfp4" else None
+    dk, dv = K.kvq_dequantize_prev_kv(c.cache, _dev_pages(np.arange(c.npages)), ks, vs, g=g_dev)
+    wk, wv = dequantize_prev_kv(oc, np.arange(len(pages)), ks, vs, g=g_oracle if c.w.dtype == "nvfp4" else None)
+    idx = torch.from_numpy(pages).to(DEV)
+    assert np.array_equal(dk.index_select(0, idx).cpu().numpy(), wk)
+    if wv is not None:
+        assert np.array_equal(dv.index_select(0, idx).cpu().numpy(), wv)
+    return dk, dv
+
+
+@pytest.mark.parametrize("P", [16, 32])
+def test_stored_mx16_ragged(P):
+    lens = [1, 15, 16, 17, 100, 1000]
+    w = I.Workload("dq-mx16", "mx16", "gqa", len(lens), 16, 4, 128, 128, P, max(lens), 0, 1, "qwen", seed=41)
+    c = Case(w, lens=lens, fill=0, spare_pages=3).run_gpu(decode=False)
+    _stored_check(c, [0, 2, 3, 5], 0.02, 0.01)
+
+
+@pytest.mark.parametrize("P", [64, 16])
+def test_stored_nvfp4_mla_ragged(P):
+    lens = [1, 63, 64, 65, 700]
+    w = I.Workload("dq-mla", "nvfp4", "mla", len(lens), 128, 1, 576, 512, P, max(lens), 0, 1, "mla", seed=42)
+    c = Case(w, lens=lens, fill=0).run_gpu(decode=False)
+    _stored_check(c, [0, 3, 4], 0.01, None)

@@ -5,7 +5,10 @@ float64 oracle. The quantization error against unquantized BF16 attention is
 printed as information."""
 import numpy as np
 import pytest
+import torch
 
+import quantized_paged_kv_store_amd as K
+from oracle.paged import dequantize_prev_kv
 from quantized_paged_kv_store_amd import inputs as I
 from tests.kvq_cases import Case, assert_close, rel_l2
 
@@ -24,6 +27,21 @@ def _check_case(c, ids, what):
     assert np.allclose(c.lse.cpu().numpy()[ids], wlse[ids], rtol=0, atol=1e-4), what
     q = rel_l2(got[ids[0]], c.unquantized(ids[0]))
     print(f"{what}: max-abs {mab:.2e} rel-L2 {r:.2e}; quantization error vs BF16 attention rel-L2 {q:.3e}")
+    return oc, pages
+
+
+def _check_dequant_prev(c, oc, pages, what, ks=0.02, vs=0.01, sample=96):
+    """kvq_dequantize_prev_kv over every page of the pool (the benchmark's
+    launch); a seeded sample of the oracle-covered pages compared byte for byte."""
+    mla = c.w.kind == "mla"
+    dk, dv = K.kvq_dequantize_prev_kv(c.cache, torch.arange(c.npages, dtype=torch.int32, device=c.dev), ks,
+                                      None if mla else vs, g=c.k_scale if mla else None)
+    pick = np.sort(np.random.default_rng(7).choice(len(pages), size=min(sample, len(pages)), replace=False))
+    wk, wv = dequantize_prev_kv(oc, pick, ks, None if mla else vs, g=c.oracle_scales()[0] if mla else None)
+    idx = torch.from_numpy(pages[pick]).to(c.dev)
+    assert np.array_equal(dk.index_select(0, idx).cpu().numpy(), wk), f"{what}: dq_k differ"
+    if not mla:
+        assert np.array_equal(dv.index_select(0, idx).cpu().numpy(), wv), f"{what}: dq_v differ"
 
 
 def test_llama3_70b_share_fp8_variants():
@@ -45,11 +63,13 @@ def test_qwen3_235b_fp4_chunk_store_and_decode():
     """Batch 64, 64/4 heads, context 32,768, FP4 block-16: the last 2,048
     tokens of every sequence go through the chunk store, then decode."""
     c = Case(I.WORKLOADS["qwen3_235b"]).run_gpu()
-    _check_case(c, [0, 63], "qwen3_235b mx16")
+    oc, pages = _check_case(c, [0, 63], "qwen3_235b mx16")
+    _check_dequant_prev(c, oc, pages, "qwen3_235b dequantize_prev_kv")
 
 
 def test_dsr1_mla_nvfp4_sampled():
     """Batch 64, 128 heads over one 576-element latent, context 65,536, page
     64, NVFP4 with a computed global scale; oracle on sequences 0 and 63."""
     c = Case(I.WORKLOADS["dsr1_mla"]).run_gpu()
-    _check_case(c, [0, 63], "dsr1_mla nvfp4")
+    oc, pages = _check_case(c, [0, 63], "dsr1_mla nvfp4")
+    _check_dequant_prev(c, oc, pages, "dsr1_mla dequantize_prev_kv")
