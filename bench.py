@@ -32,13 +32,17 @@ PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E, vendor figure
 PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, vendor figure
 
 
-def measured_traffic(w):
-    """HBM bytes per launch of the decode kernel from the committed rocprofv3
-    counter runs, or None when no measurement exists for this workload or the
-    kernel's sources changed since it was taken."""
+def measured_traffic(w, op="decode"):
+    """HBM bytes per launch of the decode (op "decode") or dequantize_prev_kv
+    (op "dequant_prev") kernel from the committed rocprofv3 counter runs, or
+    None when no measurement exists for this workload or the kernel's sources
+    changed since it was taken."""
     import hashlib
-    kind = "gqa" if w.kind == "gqa" else "mla"
-    path = os.path.join(ROOT, "profiles", f"kvq_decode_{kind}_{w.name}_{w.dtype}_traffic.json")
+    if op == "decode":
+        kind = "gqa" if w.kind == "gqa" else "mla"
+        path = os.path.join(ROOT, "profiles", f"kvq_decode_{kind}_{w.name}_{w.dtype}_traffic.json")
+    else:
+        path = os.path.join(ROOT, "profiles", f"kvq_dequant_prev_{w.dtype}_{w.name}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
@@ -297,7 +301,8 @@ def bench_dequant_prev(w, args, dev):
                                f"{d.num_kv_heads} kv head(s), head_dim {d.head_dim}, {w.dtype}) -> E4M3",
                    "cache_copies_rotated": args.rotate},
         "roofline": {"bound": "hbm", "achieved": round(ach, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(w, "dequant_prev"),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
                      "kernel": f"dequant_prev_{'nvfp4' if w.kind == 'mla' else 'mx16'}_kernel",
                      "kernel_ms": round(kern_ms, 5), "algorithmic_bytes_per_launch": read_b + write_b},
         "pct_hbm_peak": round(100 * value / PEAK_HBM_GBPS, 2),

@@ -181,3 +181,29 @@ def queries(w: Workload) -> np.ndarray:
 def sm_scale(w: Workload) -> float:
     """Softmax scale 1/sqrt(dot-product length) (the pages leave it open)."""
     return float(1.0 / np.sqrt(w.head_dim))
+
+
+def random_cache_bytes(shapes: dict, dtype: str, seed: int, mx_codes=(0, 191)) -> dict:
+    """Seeded random contents for the buffers of an FP4 cache, {name: shape}
+    -> {name: uint8 array}: code buffers uniform over all 256 byte values
+    (every E2M1 code in both nibbles); MX16 E8M0 scale codes from
+    [mx_codes[0], mx_codes[1]), half of them within 10 of the middle; NVFP4
+    E4M3 scale codes over every non-NaN magnitude with a random sign. Buffers
+    are drawn in the order k_codes, v_codes, k_scales, v_scales."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for name in ("k_codes", "v_codes", "k_scales", "v_scales"):
+        shape = shapes.get(name)
+        if shape is None:
+            continue
+        if name.endswith("codes"):
+            out[name] = rng.integers(0, 256, shape, dtype=np.uint8)
+        elif dtype == "mx16":
+            mid = (mx_codes[0] + mx_codes[1]) // 2
+            near = rng.integers(max(mx_codes[0], mid - 10), min(mx_codes[1], mid + 11), shape)
+            wide = rng.integers(mx_codes[0], mx_codes[1], shape)
+            out[name] = np.where(rng.random(shape) < 0.5, near, wide).astype(np.uint8)
+        else:
+            mag = rng.integers(0, 0x7F, shape)
+            out[name] = (mag | (rng.integers(0, 2, shape) << 7)).astype(np.uint8)
+    return out

@@ -19,27 +19,15 @@ DEV = "cuda"
 
 def _random_cache(dtype, kind, hkv, D, Dv, P, npages, seed, mx_codes=(0, 191)):
     """The same seeded random bytes in a device cache and an oracle cache.
-    MX16 E8M0 codes are drawn from mx_codes (half of them near 127) and NVFP4
-    E4M3 block scales avoid the NaN codes, so that every dequantized value and
-    quotient is finite."""
+    MX16 E8M0 codes are drawn from mx_codes and NVFP4 E4M3 block scales avoid
+    the NaN codes, so that every dequantized value and quotient is finite."""
     spec = CacheSpec(dtype, kind, hkv, D, Dv, P, npages)
     oc = OracleCache(spec)
     cache = K.kvq_alloc_pages(dtype, kind, hkv, D, Dv, P, npages, device=DEV, fill=0)
-    rng = np.random.default_rng(seed)
-    for name in ("k_codes", "v_codes", "k_scales", "v_scales"):
-        arr = getattr(oc, name)
-        if arr is None:
-            continue
-        if name.endswith("codes"):
-            arr[...] = rng.integers(0, 256, arr.shape, dtype=np.uint8)
-        elif dtype == "mx16":     # half near the middle of the range, half over all of it
-            mid = (mx_codes[0] + mx_codes[1]) // 2
-            near = rng.integers(max(mx_codes[0], mid - 10), min(mx_codes[1], mid + 11), arr.shape)
-            wide = rng.integers(mx_codes[0], mx_codes[1], arr.shape)
-            arr[...] = np.where(rng.random(arr.shape) < 0.5, near, wide).astype(np.uint8)
-        else:                     # E4M3 magnitudes 0 .. 0x7E with a random sign
-            mag = rng.integers(0, 0x7F, arr.shape)
-            arr[...] = (mag | (rng.integers(0, 2, arr.shape) << 7)).astype(np.uint8)
+    shapes = {n: getattr(oc, n).shape for n in ("k_codes", "v_codes", "k_scales", "v_scales")
+              if getattr(oc, n) is not None}
+    for name, arr in I.random_cache_bytes(shapes, dtype, seed, mx_codes).items():
+        getattr(oc, name)[...] = arr
         cache.view(name).copy_(torch.from_numpy(arr.reshape(-1)))
     return cache, oc
 
