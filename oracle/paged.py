@@ -15,6 +15,10 @@ page, t16 = t % 16, tile = t // 16, d = element index, b = d // 16):
   every buffer is [num_pages][num_kv_heads][block], block = page_size * row
   bytes, made of 16-token tiles laid one after the other.
 
+  KIVI-style FP8 caches (K scale per channel, V scale per token) add a V
+  scale buffer of one binary32 per token: float t of the (page, kv head)
+  block; the per-channel K scales are [Hkv, D] arrays held by the caller.
+
   GQA, FP8 (E4M3 / E5M2), row = D bytes, tile = 16 * D bytes:
     K: 256 * (d // 16) + 16 * t16 + d % 16
     V: 1024 * (d // 64) + 16 * (16 * (t16 // 4) + d % 16)
@@ -55,6 +59,7 @@ class CacheSpec:
     v_dim: int          # GQA D; MLA Dv (latent)
     page_size: int
     num_pages: int
+    kivi: bool = False  # FP8 GQA: K scales per channel, V scales per token (buffer below)
 
     def code_row_bytes(self) -> int:
         return self.head_dim if self.dtype in ("e4m3", "e5m2") else self.head_dim // 2
@@ -64,6 +69,10 @@ class CacheSpec:
 
     def block_bytes(self) -> tuple[int, int]:
         return (self.page_size * self.code_row_bytes(), self.page_size * self.scale_row_bytes())
+
+    def token_scale_block_bytes(self) -> int:
+        """KIVI: one binary32 V scale per token of a (page, kv head) block, token t at float t."""
+        return 4 * self.page_size if self.kivi else 0
 
 
 # ---------------------------- layout formulas -----------------------------
@@ -146,6 +155,15 @@ class OracleCache:
         self.k_scales = np.full(shape_s, fill, dtype=np.uint8) if sb else None
         self.v_scales = (np.full(shape_s, fill, dtype=np.uint8)
                          if sb and spec.kind != "mla" else None)
+        if spec.kivi:
+            assert spec.dtype in ("e4m3", "e5m2") and spec.kind == "gqa"
+            # V token scales [num_pages, Hkv, page_size] binary32, kept as bytes
+            # [num_pages, Hkv, 4 * page_size] like the device buffer
+            self.v_scales = np.full((spec.num_pages, spec.num_kv_heads, 4 * spec.page_size), fill, dtype=np.uint8)
+
+    def v_token_scales(self) -> np.ndarray:
+        """KIVI: the V scale buffer as binary32 [num_pages, Hkv, page_size] (a view)."""
+        return self.v_scales.view(np.float32)
 
     # -- writing codes for rows (page[i], head, t[i], all d) --
     def _put_codes(self, buf, pos_fn, page, head, t, codes):
@@ -175,7 +193,9 @@ class OracleCache:
         a negative slot skips the token. k_scale/v_scale: FP8 per-tensor
         scales (None = 1.0) or, per attention head (vLLM page, "Supported
         schemes"), sequences of Hkv scales, head h using element h; for NVFP4,
-        k_scale is the global scale g."""
+        k_scale is the global scale g. KIVI caches: k_scale [Hkv, D] channel
+        scales (None = 1.0), v_scale unused (each token's own scale is
+        computed here and written to the V scale buffer)."""
         s = self.spec
         slots = np.asarray(slots, dtype=np.int64)
         keep = slots >= 0
@@ -187,7 +207,15 @@ class OracleCache:
         page, t = slots[keep] // s.page_size, slots[keep] % s.page_size
         assert np.all(page < s.num_pages)
         for h in range(s.num_kv_heads):
-            if s.dtype in ("e4m3", "e5m2"):
+            if s.kivi:
+                fmt = E4M3 if s.dtype == "e4m3" else E5M2
+                ksc = np.ones(s.head_dim, np.float32) if k_scale is None else np.asarray(k_scale, np.float32)[h]
+                kc = Q.quantize_fp8(k[:, h], ksc[None, :], fmt)
+                vc, vsc = Q.quantize_fp8_per_token(v[:, h], fmt)
+                self._put_codes(self.k_codes, k_code_pos, page, h, t, kc)
+                self._put_codes(self.v_codes, v_code_pos, page, h, t, vc)
+                self.v_token_scales()[page, h, t] = vsc
+            elif s.dtype in ("e4m3", "e5m2"):
                 fmt = E4M3 if s.dtype == "e4m3" else E5M2
                 kc = Q.quantize_fp8(k[:, h], head_scale(k_scale, h), fmt)
                 vc = Q.quantize_fp8(v[:, h], head_scale(v_scale, h), fmt)
@@ -228,6 +256,13 @@ class OracleCache:
             if s.kind == "mla":
                 return self.dequant(page, t, head, "k", k_scale)[:, : s.v_dim]
             codes = self._get_codes(self.v_codes, v_code_pos, page, head, t, n)
+        if s.kivi:
+            fmt = E4M3 if s.dtype == "e4m3" else E5M2
+            if which == "k":
+                ksc = np.ones(n, np.float32) if k_scale is None else np.asarray(k_scale, np.float32)[head]
+                return decode(codes, fmt) * ksc.astype(np.float64)[None, :]
+            vsc = self.v_token_scales()[page, head, t].astype(np.float64)
+            return decode(codes, fmt) * vsc[:, None]
         if s.dtype in ("e4m3", "e5m2"):
             fmt = E4M3 if s.dtype == "e4m3" else E5M2
             sc = head_scale(k_scale if which == "k" else v_scale, head)

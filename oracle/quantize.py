@@ -1,4 +1,5 @@
-"""Quantizers for new K/V tokens: FP8 per-tensor, FP4 block-16 (E8M0), NVFP4 two-level.
+"""Quantizers for new K/V tokens: FP8 per-tensor / per-head / KIVI-style
+(per-channel K, per-token V), FP4 block-16 (E8M0), NVFP4 two-level.
 
 TEST INFRASTRUCTURE (CPU oracle; see ``oracle/formats.py``).
 
@@ -46,10 +47,38 @@ def fp8_head_scales(x, fmt: Format) -> np.ndarray:
     return np.array([fp8_scale(a, fmt) for a in amax], dtype=np.float32)
 
 
+# --------------------------------------------------------------------------
+# KIVI-style asymmetric scaling ("KV cache quantization mechanism and traps",
+# the section on why K and V distributions differ): Key outliers sit in fixed
+# channels, so K gets one scale per channel; Value varies from token to
+# token, so V gets one scale per token. The page reports KIVI with 2-bit
+# integers; reading adopted for this cache: the same FP8 codes as the
+# per-tensor path, K scale per (kv head, channel) = fl32(amax over the
+# calibration tokens / format max), fixed afterwards; V scale per (token, kv
+# head) = fl32(amax of that token's row / format max), computed when the
+# token is stored; an all-zero channel or row gets 1.0.
+# --------------------------------------------------------------------------
+def fp8_channel_scales(x, fmt: Format) -> np.ndarray:
+    """[tokens, Hkv, D] -> [Hkv, D]: fp8_scale of the amax of every channel."""
+    x = np.asarray(x, dtype=np.float64)
+    amax = np.abs(x).max(axis=0) if x.shape[0] else np.zeros(x.shape[1:])
+    return np.vectorize(lambda a: fp8_scale(a, fmt), otypes=[np.float32])(amax).astype(np.float32)
+
+
+def quantize_fp8_per_token(x, fmt: Format) -> tuple[np.ndarray, np.ndarray]:
+    """Rows [N, D] -> (codes [N, D], scales [N]): each row with its own
+    fp8_scale(amax of the row)."""
+    x = np.asarray(x, dtype=np.float64)
+    amax = np.abs(x).max(axis=-1) if x.shape[-1] else np.zeros(x.shape[:-1])
+    s = np.array([fp8_scale(a, fmt) for a in amax.reshape(-1)], dtype=np.float32).reshape(amax.shape)
+    return quantize_fp8(x, s[..., None], fmt), s
+
+
 def quantize_fp8(x, scale, fmt: Format) -> np.ndarray:
-    """codes = encode(fl32(x / scale)); x holds BF16 values (exact in fp32)."""
+    """codes = encode(fl32(x / scale)); x holds BF16 values (exact in fp32);
+    scale is a binary32 scalar or an array broadcast against x."""
     x32 = fl32(x)
-    q = x32 / np.float32(scale)
+    q = x32 / np.asarray(scale, dtype=np.float32)
     return encode(q.astype(np.float64), fmt)
 
 

@@ -172,3 +172,31 @@ def test_dequantize_prev_kv_nvfp4_error_bound():
         normal = np.abs(x_hat) >= 2.0 ** -6 * float(s)
         assert np.all(np.abs(back - x_hat)[normal] <= 2.0 ** -4 * np.abs(x_hat)[normal] * (1 + 1e-6))
         assert np.all(np.abs(back) <= 448.0 * float(s))
+
+
+def test_kivi_cache_round_trip_on_grid():
+    """KIVI-style cache: K rows on the E4M3 grid times power-of-two channel
+    scales and V rows on the grid whose per-token scale is exact come back
+    exactly; the V scale buffer holds each token's fl32(amax / 448) at float t
+    of its (page, head) block. A swapped channel or token index fails."""
+    rng = np.random.default_rng(31)
+    spec = CacheSpec("e4m3", "gqa", 2, 64, 64, 32, 3, kivi=True)
+    oc = OracleCache(spec)
+    grid = F.decode(np.arange(0x7F), F.E4M3)                    # every finite magnitude
+    T = 70
+    ks = (2.0 ** rng.integers(-8, 4, (2, 64))).astype(np.float32)
+    kc = rng.choice(grid, (T, 2, 64)) * np.where(rng.random((T, 2, 64)) < 0.5, -1, 1)
+    k = kc * ks[None].astype(np.float64)
+    vrow = rng.choice(grid, (T, 2, 64)) * np.where(rng.random((T, 2, 64)) < 0.5, -1, 1)
+    vrow[:, :, 7] = 448.0                                        # every row's amax is 448 * (its factor)
+    vfac = 2.0 ** rng.integers(-10, 6, (T, 2, 1))
+    v = vrow * vfac / 448.0 * 448.0
+    slots = rng.permutation(spec.num_pages * spec.page_size)[:T]
+    oc.store(k, v, slots, k_scale=ks)
+    page, t = slots // spec.page_size, slots % spec.page_size
+    for h in range(2):
+        assert np.array_equal(oc.dequant(page, t, h, "k", k_scale=ks), k[:, h])
+        assert np.array_equal(oc.dequant(page, t, h, "v"), v[:, h])
+        got = oc.v_token_scales()[page, h, t]
+        assert np.array_equal(got, (np.float32(448.0 * vfac[:, h, 0]) / np.float32(448.0)).astype(np.float32))
+    assert oc.v_scales.shape == (3, 2, 4 * 32) and spec.token_scale_block_bytes() == 128

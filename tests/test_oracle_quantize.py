@@ -193,3 +193,100 @@ def test_fp8_head_scales_power_of_two_heads_share_codes():
     codes = [Q.quantize_fp8(x[:, h], s[h], F.E4M3) for h in range(4)]
     for c in codes[1:]:
         assert np.array_equal(c, codes[0])
+
+
+# ------------------------------------------- KIVI-style per-channel / per-token
+@pytest.mark.parametrize("fmt", [F.E4M3, F.E5M2])
+def test_channel_scales_closed_form_and_zero_channel(fmt):
+    """One scale per (kv head, channel) = fl32(channel amax / format max);
+    an all-zero channel gets 1.0. The amax is planted at a random token."""
+    rng = np.random.default_rng(21)
+    T, H, D = 50, 3, 16
+    amax = bf16_to_f32(bf16_bits(10.0 ** rng.uniform(-3, 3, (H, D)))).astype(np.float64)
+    x = rng.uniform(-1, 1, (T, H, D)) * amax[None] * 0.99
+    x = bf16_to_f32(bf16_bits(x)).astype(np.float64)
+    at = rng.integers(0, T, (H, D))
+    sign = np.where(rng.random((H, D)) < 0.5, -1.0, 1.0)
+    for h in range(H):
+        for d in range(D):
+            x[at[h, d], h, d] = sign[h, d] * amax[h, d]
+    x[:, 1, 5] = 0.0
+    s = Q.fp8_channel_scales(x, fmt)
+    assert s.shape == (H, D) and s.dtype == np.float32
+    want = (np.float32(amax) / np.float32(fmt.max_value)).astype(np.float32)
+    want[1, 5] = 1.0
+    assert np.array_equal(s, want)
+
+
+def test_per_token_scales_put_each_row_max_on_the_format_max():
+    """Every row's largest magnitude encodes to +-448 (E4M3) and the row's
+    scale is fl32(row amax / 448); scaling a row by 2^k scales its scale by
+    2^k and leaves its codes unchanged (normal range)."""
+    rng = np.random.default_rng(22)
+    x = bf16_to_f32(bf16_bits(rng.standard_normal((40, 128)) * 10.0 ** rng.uniform(-2, 2, (40, 1))))
+    x = x.astype(np.float64)
+    codes, s = Q.quantize_fp8_per_token(x, F.E4M3)
+    assert s.shape == (40,) and s.dtype == np.float32
+    assert np.array_equal(s, (np.float32(np.abs(x).max(axis=1)) / np.float32(448.0)).astype(np.float32))
+    i = np.abs(x).argmax(axis=1)
+    assert np.all(np.abs(F.decode(codes[np.arange(40), i], F.E4M3)) == 448.0)
+    c2, s2 = Q.quantize_fp8_per_token(x * 2.0 ** 5, F.E4M3)
+    assert np.array_equal(c2, codes) and np.array_equal(s2, s * np.float32(32.0))
+    z, sz = Q.quantize_fp8_per_token(np.zeros((2, 8)), F.E4M3)
+    assert np.all(sz == 1.0) and np.all(z == 0)
+
+
+def test_kivi_reduces_to_per_tensor_when_all_amax_agree():
+    """When every channel (and every token) has the same amax A, the
+    per-channel and per-token quantizers give the per-tensor codes with
+    scale fl32(A / 448)."""
+    rng = np.random.default_rng(23)
+    x = bf16_to_f32(bf16_bits(rng.uniform(-3.0, 3.0, (16, 1, 16)))).astype(np.float64)
+    idx = np.arange(16)
+    x[idx, 0, idx] = 3.0          # a diagonal of 3s: every row and every column reaches amax 3
+    s_t = Q.fp8_scale(3.0, F.E4M3)
+    per_tensor = Q.quantize_fp8(x[:, 0], s_t, F.E4M3)
+    sc = Q.fp8_channel_scales(x, F.E4M3)
+    assert np.all(sc == s_t)
+    assert np.array_equal(Q.quantize_fp8(x[:, 0], sc[0][None, :], F.E4M3), per_tensor)
+    ct, st = Q.quantize_fp8_per_token(x[:, 0], F.E4M3)
+    assert np.all(st == s_t) and np.array_equal(ct, per_tensor)
+
+
+def test_kivi_scaling_fits_the_outlier_structure():
+    """The pages' rationale ("KV cache quantization mechanism and traps", K and
+    V distributions and the scale-reuse trap). Per-channel K codes of the
+    ordinary channels do not depend on the outlier channels at all; one scale
+    per tensor costs them nothing while the outliers stay within E4M3's wide
+    range (x100: the page's remark that E4M3 absorbs scale error) and doubles
+    their error once the outliers push them into E4M3's subnormals (x10^4).
+    V rows with per-token scales keep every error within half the widest
+    E4M3 step (32, between 256 and 448) times the row's scale."""
+    rng = np.random.default_rng(24)
+    base = rng.standard_normal((512, 1, 128))
+    out_ch = [3, 40, 77, 101]
+    normal = np.setdiff1d(np.arange(128), out_ch)
+    errs, codes = {}, {}
+    for fac in (100.0, 10000.0):
+        k = base.copy()
+        k[:, :, out_ch] *= fac
+        k = bf16_to_f32(bf16_bits(k)).astype(np.float64)
+        s_ch = Q.fp8_channel_scales(k, F.E4M3)
+        c_ch = Q.quantize_fp8(k[:, 0], s_ch[0][None, :], F.E4M3)
+        k_ch = F.decode(c_ch, F.E4M3) * s_ch[0][None, :]
+        s_t = Q.fp8_scale(np.abs(k).max(), F.E4M3)
+        k_t = F.decode(Q.quantize_fp8(k[:, 0], s_t, F.E4M3), F.E4M3) * float(s_t)
+        err = lambda a: np.linalg.norm(a[:, normal] - k[:, 0][:, normal]) / np.linalg.norm(k[:, 0][:, normal])
+        errs[fac] = (err(k_ch), err(k_t))
+        codes[fac] = c_ch[:, normal]
+    assert np.array_equal(codes[100.0], codes[10000.0])
+    assert errs[100.0][0] == errs[10000.0][0] and errs[100.0][0] < 0.03
+    assert abs(errs[100.0][1] / errs[100.0][0] - 1.0) < 0.05
+    assert errs[10000.0][1] > 1.5 * errs[10000.0][0]
+    v = rng.standard_normal((512, 128)) * np.exp(rng.normal(0.0, 2.0, (512, 1)))
+    v = bf16_to_f32(bf16_bits(v)).astype(np.float64)
+    cv, sv = Q.quantize_fp8_per_token(v, F.E4M3)
+    v_tok = F.decode(cv, F.E4M3) * sv.astype(np.float64)[:, None]
+    # (x / s is rounded to binary32 first: a quotient a hair above a tie lands on it)
+    assert np.all(np.abs(v_tok - v) <= 16.0 * (1 + 2.0 ** -20) * sv.astype(np.float64)[:, None])
+    assert np.abs(v_tok - v).max(axis=1).min() > 0          # not vacuous
