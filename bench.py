@@ -70,7 +70,8 @@ def setup(w, dev, rotate):
     max_len = int(lens.max())
     pre = np.maximum(lens - w.new_tokens, 0)
     cache = K.kvq_alloc_pages(w.dtype, w.kind, w.kv_heads, w.head_dim, w.v_dim, w.page_size, npages,
-                              device=dev, fill=0, scale_per_head=w.scale_mode == "amax_head")
+                              device=dev, fill=0,
+                              scale_mode={"amax_head": "head", "kivi": "kivi"}.get(w.scale_mode, "tensor"))
     # prefill, one sequence at a time (bounded host memory); scales first need the
     # whole prefill, so K (and V) are staged on the device
     n_pre = int(pre.sum())
@@ -90,7 +91,9 @@ def setup(w, dev, rotate):
         sd[off:off + n] = torch.from_numpy(I.slots_for(table[b], np.arange(n), w.page_size)).to(dev)
         off += n
     ks = vs = None
-    if w.dtype in ("e4m3", "e5m2") and w.scale_mode in ("amax", "amax_head"):
+    if w.dtype in ("e4m3", "e5m2") and w.scale_mode == "kivi":
+        ks = K.kvq_compute_scale(cache, kd)          # K channel scales; V scales per token at store
+    elif w.dtype in ("e4m3", "e5m2") and w.scale_mode in ("amax", "amax_head"):
         ks = K.kvq_compute_scale(cache, kd, vd) if w.dist == "tiny" else K.kvq_compute_scale(cache, kd)
         vs = ks if w.dist == "tiny" else K.kvq_compute_scale(cache, vd)
     elif w.dtype == "nvfp4":
@@ -198,9 +201,11 @@ def cpu_baseline(w, seconds_hint=20.0):
     elif w.dtype in ("e4m3", "e5m2") and w.scale_mode == "amax_head":
         fmt = E4M3 if w.dtype == "e4m3" else E5M2
         ks, vs = Q.fp8_head_scales(kf, fmt), Q.fp8_head_scales(vf, fmt)
+    elif w.dtype in ("e4m3", "e5m2") and w.scale_mode == "kivi":
+        ks = Q.fp8_channel_scales(kf, E4M3 if w.dtype == "e4m3" else E5M2)
     elif w.dtype == "nvfp4":
         ks = Q.nvfp4_global_scale(np.abs(kf).max())
-    oc = OracleCache(CacheSpec(w.dtype, w.kind, w.kv_heads, w.head_dim, w.v_dim, P, npg))
+    oc = OracleCache(CacheSpec(w.dtype, w.kind, w.kv_heads, w.head_dim, w.v_dim, P, npg, kivi=w.scale_mode == "kivi"))
     t0 = time.perf_counter()
     oc.store(kf, vf, I.slots_for(table[b], np.arange(L), P), k_scale=ks, v_scale=vs)
     t_codec = time.perf_counter() - t0
@@ -343,6 +348,8 @@ def main():
     ap.add_argument("--copy-ref", action="store_true", help="only run the 1 GiB reference copy (for counters)")
     ap.add_argument("--dequant-prev", action="store_true",
                     help="FP4 workloads: time kvq_dequantize_prev_kv over every page instead of the decode step")
+    ap.add_argument("--kivi", action="store_true",
+                    help="FP8 workloads: K scales per channel, V scales per token (KIVI-style)")
     ap.add_argument("--per-head-scales", action="store_true",
                     help="FP8 workloads: one calibrated k/v scale per KV head instead of per tensor")
     args = ap.parse_args()
@@ -362,6 +369,9 @@ def main():
     if args.per_head_scales:
         assert w.dtype in ("e4m3", "e5m2"), "per-head scales apply to FP8 caches"
         w = w.with_(scale_mode="amax_head")
+    if args.kivi:
+        assert w.dtype in ("e4m3", "e5m2") and w.kind == "gqa", "KIVI-style scales apply to FP8 GQA caches"
+        w = w.with_(scale_mode="kivi")
     dev = torch.device("cuda:0")
     if args.dequant_prev:
         assert w.dtype in ("mx16", "nvfp4"), "dequantize_prev_kv reads FP4 caches"

@@ -54,6 +54,17 @@ typedef enum kvq_kind {
                   K = the whole row (head_dim), V = its first v_dim elements   */
 } kvq_kind;
 
+/* How FP8 scales are kept (cache descriptor field scale_mode). */
+typedef enum kvq_scale_mode {
+  KVQ_SCALE_TENSOR = 0, /* one k_scale and one v_scale ([P1] "Scaling factors")           */
+  KVQ_SCALE_HEAD = 1,   /* one per KV head: k/v_scale = [num_kv_heads] ([P3] "Supported
+                           schemes", per-attention-head quantization)                    */
+  KVQ_SCALE_KIVI = 2    /* K: one scale per (KV head, channel), k_scale = [num_kv_heads]
+                           [head_dim]; V: one scale per (token, KV head), computed when
+                           the token is stored ([P2] "why K and V distributions differ":
+                           per-channel K, per-token V)                                    */
+} kvq_scale_mode;
+
 typedef enum kvq_status {
   KVQ_OK = 0,
   KVQ_ERR_ARG = -1,         /* null pointer, negative size, inconsistent shape */
@@ -71,15 +82,16 @@ typedef struct kvq_cache_desc {
   int32_t v_dim;        /* GQA: must equal head_dim; MLA: latent dims (Dv) */
   int32_t page_size;    /* tokens per page, a multiple of 16 */
   int64_t num_pages;    /* physical pages in the pool, >= 1 */
-  int32_t scale_per_head; /* FP8 GQA only: 0 = one k_scale / v_scale per tensor,
-                             1 = one per KV head ([P3] "Supported schemes":
-                             per-attention-head scales k/v_scale = [num_kv_heads]);
-                             every k_scale / v_scale argument is then an array
-                             of num_kv_heads floats. Must be 0 otherwise. */
+  int32_t scale_mode;   /* kvq_scale_mode; KVQ_SCALE_HEAD and KVQ_SCALE_KIVI are for
+                           FP8 GQA only, every other cache uses KVQ_SCALE_TENSOR.
+                           HEAD: every k_scale / v_scale argument is an array of
+                           num_kv_heads floats. KIVI: k_scale is [num_kv_heads]
+                           [head_dim] floats, v_scale is unused (NULL), and the
+                           cache holds one fp32 V scale per stored token. */
 } kvq_cache_desc;
 
 /* Supported combinations (others return KVQ_ERR_UNSUPPORTED):
- *   GQA x {E4M3, E5M2}: head_dim in {64, 128}, scale_per_head 0 or 1
+ *   GQA x {E4M3, E5M2}: head_dim in {64, 128}, any scale_mode
  *   GQA x FP4_MX16:     head_dim == 128
  *   MLA x NVFP4:        head_dim == 576, v_dim == 512
  *   decode, GQA:        G = Hq / Hkv in [1, 16], max_seq_len <= 2,097,152
@@ -105,6 +117,8 @@ typedef struct kvq_cache_desc {
  *     code,  d >= 512: 4096 + 2*((g4*16 + (d-512)/4)*4 + tt) + (d%4)/2
  *     scale, b < 32:   4*((b/4*4 + g4)*4 + b%4) + tt      (E4M3 code)
  *     scale, b >= 32:  512 + 4*(g4*4 + b-32) + tt
+ *   GQA FP8 with scale_mode KIVI adds the V scale buffer, one fp32 per token:
+ *     V scale of token t: float t of the (page, kv head) block (4*page_size B)
  * The K layouts put the 16 tokens of a tile at consecutive 16-byte lanes and
  * the V layouts put 4 consecutive tokens of one element (FP8) or of one
  * 4- or 8-element group (MLA, FP4) in one lane load, so each wave of the
@@ -156,9 +170,11 @@ void kvq_free_handle(kvq_cache* cache);
  *   x1[0..n1) (x1 may be NULL with n1 == 0); division is IEEE binary32.
  * x0, x1: [dev] BF16. scale_out: [dev] one float. Uses the cache's scratch
  * buffer: concurrent calls on one cache race.
- * With scale_per_head = 1, x0 and x1 are [tokens][num_kv_heads][head_dim]
+ * With scale_mode HEAD or KIVI, x0 and x1 are [tokens][num_kv_heads][head_dim]
  * (n0, n1 multiples of num_kv_heads*head_dim, both 16-byte aligned) and
- * scale_out[h] = amax over head h / format max, for h < num_kv_heads.
+ *   HEAD: scale_out[h] = amax over head h / format max, h < num_kv_heads;
+ *   KIVI: scale_out[h*head_dim + d] = amax over channel d of head h / format
+ *         max (the K channel scales; V needs none).
  * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED (FP4_MX16 has no tensor scale). */
 int kvq_compute_scale(const kvq_cache* cache, const void* x0, int64_t n0, const void* x1,
                       int64_t n1, float* scale_out, void* stream);
@@ -171,7 +187,11 @@ int kvq_compute_scale(const kvq_cache* cache, const void* x0, int64_t n0, const 
  *         a negative slot or one >= num_pages*page_size skips the token.
  *   k_scale, v_scale: [dev] fp32 scalars. FP8: per-tensor scales, NULL = 1.0
  *         ([P1]: default when no scale is given); code = RNE_sat(x / scale);
- *         with scale_per_head, [num_kv_heads] arrays indexed by KV head.
+ *         with scale_mode HEAD, [num_kv_heads] arrays indexed by KV head;
+ *         KIVI: k_scale = the [num_kv_heads][head_dim] channel scales
+ *         (required), v_scale unused; each token's V row gets its own scale
+ *         fl32(amax / format max) (1.0 for an all-zero row), stored in the
+ *         cache's V scale buffer.
  *         NVFP4: k_scale = global scale g (required), v_scale unused.
  *         FP4_MX16: both unused (block exponents are computed here from each
  *         16-element block's amax: e = floor(log2 amax) - 2).
@@ -197,7 +217,8 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t
  *   seq_lens:   [dev] int32 [batch], each in [0, max_seq_len]
  *   max_seq_len [host]: upper bound used to size the launch
  *   k_scale, v_scale: [dev] fp32 (FP8: per-tensor scales, NULL = 1.0, or
- *               [num_kv_heads] arrays with scale_per_head;
+ *               [num_kv_heads] arrays with scale_mode HEAD; KIVI: k_scale =
+ *               the channel scales (required), V scales from the cache;
  *               NVFP4: k_scale = global scale g, required; MX16: unused)
  *   out:        [dev] fp32 [batch][num_q_heads][v_dim]
  *   lse:        [dev] fp32 [batch][num_q_heads] (natural log) or NULL

@@ -26,6 +26,13 @@
 // The QK accumulator layout (lane = head column, 4 tokens per lane) is
 // exactly the PV B-operand layout once the 32 tokens of a pair are ordered
 // [tile A: 4g..4g+3, tile B: 4g..4g+3] along K, so scores never leave the lane.
+//
+// KIVI-style FP8 caches (K scale per channel, V scale per token; the "KV cache
+// quantization mechanism and traps" page, K and V distributions) fold the
+// scales into the other operand instead of the codes: Q^T[d][h] * ks[d] once
+// per workgroup (fp32, split into bf16 hi + lo, two QK MFMAs), and
+// P[t][h] * vs[t] per tile (fp32, bf16 hi + lo for the PV MFMAs, V codes
+// exact in bf16); the softmax sum keeps the unscaled P.
 #include "store_row.h"
 
 namespace kvq {
@@ -44,9 +51,10 @@ struct Tile {
   uint4 v[NK];
   uint32_t ks;  // FP4: K E8M0 codes of blocks (2g, 2g+1) for token lane%16
   uint32_t vs;  // FP4: V E8M0 codes of tokens 4g..4g+3, block (lane%16)/2
+  f32x4 vt;     // KIVI: V scales of tokens 4g..4g+3
 };
 
-template <int FMT, int D>
+template <int FMT, int D, bool KIVI = false>
 __device__ __forceinline__ void load_tile(Tile<FMT, D>& t, const uint8_t* __restrict__ kb,
                                           const uint8_t* __restrict__ vb, const uint8_t* __restrict__ ksb,
                                           const uint8_t* __restrict__ vsb, int lane) {
@@ -61,6 +69,7 @@ __device__ __forceinline__ void load_tile(Tile<FMT, D>& t, const uint8_t* __rest
     t.ks = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(ksb + 2 * lane));
     t.vs = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vsb + 4 * (8 * (lane >> 4) + ((lane & 15) >> 1))));
   }
+  if (KIVI) t.vt = *reinterpret_cast<const f32x4*>(vsb + 16 * (lane >> 4));  // the tile's 16 floats, 4 per group
 }
 
 template <int FMT, int D>
@@ -72,6 +81,7 @@ __device__ __forceinline__ void zero_tile(Tile<FMT, D>& t) {
   }
   t.ks = 0x7f7fu;
   t.vs = 0x7f7f7f7fu;
+  t.vt = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 // Zero the V codes (and neutralize scales) of this lane's tokens 4g+tt with
@@ -96,6 +106,10 @@ __device__ __forceinline__ void mask_tile_v(Tile<FMT, D>& t, int nvalid) {
       t.v[i].z &= keep;
       t.v[i].w &= keep;
     }
+    // KIVI: padding slots may hold NaN scale bytes; P * vs must be 0 there
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (i >= nvalid) t.vt[i] = 0.f;
   }
 }
 
@@ -104,8 +118,9 @@ __device__ __forceinline__ uint32_t u4_get(const uint4& v, int i) {
 }
 
 // S^T tile (16 tokens x 16 heads), lane holds tokens 4g..4g+3 of head lane%16.
-template <int FMT, int D>
-__device__ __forceinline__ f32x4 qk_tile(const Tile<FMT, D>& t, const bf16x8* qf) {
+// KIVI: qf holds the high and ql the low bf16 half of Q * ks.
+template <int FMT, int D, bool KIVI = false>
+__device__ __forceinline__ f32x4 qk_tile(const Tile<FMT, D>& t, const bf16x8* qf, const bf16x8* ql) {
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (FMT == KVQ_FP4_MX16) {
 #pragma unroll
@@ -125,16 +140,52 @@ __device__ __forceinline__ f32x4 qk_tile(const Tile<FMT, D>& t, const bf16x8* qf
       u32x4 a = {fp8x2_to_bf16x2<FMT, false>(w0), fp8x2_to_bf16x2<FMT, true>(w0),
                  fp8x2_to_bf16x2<FMT, false>(w1), fp8x2_to_bf16x2<FMT, true>(w1)};
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qf[c], acc, 0, 0, 0);
+      if (KIVI) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), ql[c], acc, 0, 0, 0);
     }
   }
   return acc;
 }
 
+// 8 floats -> bf16 hi (RNE) and lo = bf16(x - hi): 16 significant bits
+__device__ __forceinline__ void split_bf16x8(const float* p, bf16x8& bh, bf16x8& bl) {
+  float r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const __bf16 h = (__bf16)p[i];
+    r[i] = p[i] - (float)h;
+  }
+  const u32x4 phi = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                     pack_bf16x2(p[6], p[7])};
+  const u32x4 plo = {pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]),
+                     pack_bf16x2(r[6], r[7])};
+  bh = __builtin_bit_cast(bf16x8, phi);
+  bl = __builtin_bit_cast(bf16x8, plo);
+}
+
 // O^T += V^T P^T over the 32 tokens of a tile pair.
-template <int FMT, int D>
+template <int FMT, int D, bool KIVI = false>
 __device__ __forceinline__ void pv_pair(const Tile<FMT, D>& ta, const Tile<FMT, D>& tb, const float* p,
                                         f32x4* o) {
-  if (FMT == KVQ_FP4_MX16) {
+  if (KIVI) {
+    float pv[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = p[i] * ta.vt[i];
+      pv[4 + i] = p[4 + i] * tb.vt[i];
+    }
+    bf16x8 bh, bl;
+    split_bf16x8(pv, bh, bl);
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+      const uint32_t wa = u4_get(ta.v[j >> 2], j & 3);
+      const uint32_t wb = u4_get(tb.v[j >> 2], j & 3);
+      u32x4 a = {fp8x2_to_bf16x2<FMT, false>(wa), fp8x2_to_bf16x2<FMT, true>(wa), fp8x2_to_bf16x2<FMT, false>(wb),
+                 fp8x2_to_bf16x2<FMT, true>(wb)};
+      const bf16x8 av = __builtin_bit_cast(bf16x8, a);
+      o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, o[j], 0, 0, 0);
+      o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, o[j], 0, 0, 0);
+    }
+  } else if (FMT == KVQ_FP4_MX16) {
     // P in bf16 as hi + lo (16 significant bits)
     u32x4 phi, plo;
     float r[8];
@@ -195,7 +246,7 @@ __device__ __forceinline__ int out_dim(int j, int g, int r) {
   return (FMT == KVQ_FP4_MX16) ? 8 * (4 * g + r) + j : 16 * j + 4 * g + r;
 }
 
-template <int FMT, int D>
+template <int FMT, int D, bool KIVI>
 __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs a) {
   constexpr int NJ = D / 16;                       // output accumulator tiles
   constexpr int NC = (FMT == KVQ_FP4_MX16) ? 4 : D / 32;  // QK MFMAs per tile
@@ -221,20 +272,21 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
   const int G = a.group;
   const int tpp = a.page_size / kTile;
   const int64_t tile_code_bytes = (FMT == KVQ_FP4_MX16) ? 8 * D : 16 * D;
-  const int64_t tile_scale_bytes = (FMT == KVQ_FP4_MX16) ? D : 0;
+  const int64_t tile_scale_bytes = (FMT == KVQ_FP4_MX16) ? D : (KIVI ? 4 * kTile : 0);
   const int64_t head_code = (int64_t)kvh * a.code_block_bytes;
   const int64_t head_scale = (int64_t)kvh * a.scale_block_bytes;
   const int64_t page_code = (int64_t)a.hkv * a.code_block_bytes;
   const int64_t page_scale = (int64_t)a.hkv * a.scale_block_bytes;
   const int32_t* pt = a.page_table + (int64_t)b * a.page_table_stride;
 
-  const int si = a.scale_per_head ? kvh : 0;  // per-tensor or per-KV-head FP8 scales
-  const float kscale = a.k_scale ? a.k_scale[si] : 1.0f;
-  const float vscale = a.v_scale ? a.v_scale[si] : 1.0f;
+  const int si = a.scale_mode == KVQ_SCALE_HEAD ? kvh : 0;  // per-tensor or per-KV-head FP8 scales
+  const float kscale = (!KIVI && a.k_scale) ? a.k_scale[si] : 1.0f;
+  const float vscale = (!KIVI && a.v_scale) ? a.v_scale[si] : 1.0f;
   const float s_log2 = a.sm_scale_log2 * kscale;
 
-  // Q^T operand fragments for head hc (zero beyond the group)
-  bf16x8 qf[NC];
+  // Q^T operand fragments for head hc (zero beyond the group); KIVI: Q * ks
+  // as bf16 hi (qf) + lo (ql)
+  bf16x8 qf[NC], ql[KIVI ? NC : 1];
   {
     const bool hv = hc < G;
     const uint16_t* qrow = a.q + ((int64_t)b * a.hq + (int64_t)kvh * G + (hv ? hc : 0)) * D;
@@ -243,7 +295,20 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
       const int d0 = (FMT == KVQ_FP4_MX16) ? 32 * g + 8 * c : 64 * (c >> 1) + 16 * g + 8 * (c & 1);
       uint4 w = *reinterpret_cast<const uint4*>(qrow + d0);
       if (!hv) w = make_uint4(0, 0, 0, 0);
-      qf[c] = __builtin_bit_cast(bf16x8, w);
+      if constexpr (KIVI) {
+        const float* ksr = a.k_scale + (int64_t)kvh * D + d0;
+        const f32x4 s0 = *reinterpret_cast<const f32x4*>(ksr), s1 = *reinterpret_cast<const f32x4*>(ksr + 4);
+        const uint32_t wq[4] = {w.x, w.y, w.z, w.w};
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[2 * i] = bf16_bits_to_f32(wq[i] & 0xffffu) * (i < 2 ? s0[2 * i] : s1[2 * i - 4]);
+          x[2 * i + 1] = bf16_bits_to_f32(wq[i] >> 16) * (i < 2 ? s0[2 * i + 1] : s1[2 * i - 3]);
+        }
+        split_bf16x8(x, qf[c], ql[c]);
+      } else {
+        qf[c] = __builtin_bit_cast(bf16x8, w);
+      }
     }
   }
 
@@ -276,6 +341,12 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
         const int64_t sbase = (int64_t)page * page_scale + head_scale + (int64_t)(t >> 4) * tile_scale_bytes;
         put_mx16_block(a.new_k + row, a.new_v + row, tid, D / 16, D, t & 15, kc, vc, const_cast<uint8_t*>(a.k_scales),
                        const_cast<uint8_t*>(a.v_scales), cbase, sbase);
+      } else if constexpr (KIVI) {
+        const int64_t base = (int64_t)page * page_code + head_code + (int64_t)(t >> 4) * tile_code_bytes;
+        const float vs = put_fp8_chunk_kivi<FMT>(a.new_k + row, a.new_v + row, tid, D / 16, t & 15,
+                                                 a.k_scale + (int64_t)kvh * D, kc, vc, base);
+        if (tid == 0)
+          reinterpret_cast<float*>(const_cast<uint8_t*>(a.v_scales) + (int64_t)page * page_scale + head_scale)[t] = vs;
       } else {
         const int64_t base = (int64_t)page * page_code + head_code + (int64_t)(t >> 4) * tile_code_bytes;
         put_fp8_chunk<FMT>(a.new_k + row, a.new_v + row, tid, t & 15, kscale, vscale, kc, vc, base);
@@ -304,7 +375,7 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
       ok |= (int)v << s2;
       const int64_t pg = v ? page : 0;
       const int64_t sub = tile - (tile / tpp) * tpp;
-      load_tile<FMT, D>(P.t[s2], a.k_codes + pg * page_code + head_code + sub * tile_code_bytes,
+      load_tile<FMT, D, KIVI>(P.t[s2], a.k_codes + pg * page_code + head_code + sub * tile_code_bytes,
                         a.v_codes + pg * page_code + head_code + sub * tile_code_bytes,
                         a.k_scales + pg * page_scale + head_scale + sub * tile_scale_bytes,
                         a.v_scales + pg * page_scale + head_scale + sub * tile_scale_bytes, lane);
@@ -316,8 +387,8 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
     const int tA = P.tA;
     float s[8];
     {
-      const f32x4 sa = qk_tile<FMT, D>(P.t[0], qf);
-      const f32x4 sb = qk_tile<FMT, D>(P.t[1], qf);
+      const f32x4 sa = qk_tile<FMT, D, KIVI>(P.t[0], qf, ql);
+      const f32x4 sb = qk_tile<FMT, D, KIVI>(P.t[1], qf, ql);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         s[i] = sa[i] * s_log2;
@@ -355,7 +426,7 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
     m_run = m_new;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) o[j] *= alpha;
-    pv_pair<FMT, D>(P.t[0], P.t[1], p, o);
+    pv_pair<FMT, D, KIVI>(P.t[0], P.t[1], p, o);
   };
 
   // Tile pairs in flight per wave: two for FP8 at D = 128 (8 KB per wave in
@@ -433,19 +504,27 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
 
 using namespace kvq;
 
+template <int FMT, int D>
+void launch_fp8(const GqaDecodeArgs& a, dim3 grid, hipStream_t s) {
+  if (a.scale_mode == KVQ_SCALE_KIVI)
+    decode_gqa_kernel<FMT, D, true><<<grid, 256, 0, s>>>(a);
+  else
+    decode_gqa_kernel<FMT, D, false><<<grid, 256, 0, s>>>(a);
+}
+
 hipError_t kvq_launch_decode_gqa(const kvq_cache* c, const GqaDecodeArgs& a, hipStream_t s) {
   const dim3 grid(a.num_splits, a.hkv, a.batch);
   const int dt = c->desc.dtype, D = c->desc.head_dim;
   if (dt == KVQ_FP8_E4M3 && D == 128)
-    decode_gqa_kernel<KVQ_FP8_E4M3, 128><<<grid, 256, 0, s>>>(a);
+    launch_fp8<KVQ_FP8_E4M3, 128>(a, grid, s);
   else if (dt == KVQ_FP8_E4M3 && D == 64)
-    decode_gqa_kernel<KVQ_FP8_E4M3, 64><<<grid, 256, 0, s>>>(a);
+    launch_fp8<KVQ_FP8_E4M3, 64>(a, grid, s);
   else if (dt == KVQ_FP8_E5M2 && D == 128)
-    decode_gqa_kernel<KVQ_FP8_E5M2, 128><<<grid, 256, 0, s>>>(a);
+    launch_fp8<KVQ_FP8_E5M2, 128>(a, grid, s);
   else if (dt == KVQ_FP8_E5M2 && D == 64)
-    decode_gqa_kernel<KVQ_FP8_E5M2, 64><<<grid, 256, 0, s>>>(a);
+    launch_fp8<KVQ_FP8_E5M2, 64>(a, grid, s);
   else if (dt == KVQ_FP4_MX16 && D == 128)
-    decode_gqa_kernel<KVQ_FP4_MX16, 128><<<grid, 256, 0, s>>>(a);
+    decode_gqa_kernel<KVQ_FP4_MX16, 128, false><<<grid, 256, 0, s>>>(a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

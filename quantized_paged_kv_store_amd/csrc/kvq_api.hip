@@ -3,6 +3,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <new>
 #include <string>
@@ -29,8 +30,8 @@ int check_desc(const kvq_cache_desc* d) {
     return KVQ_ERR_ARG;
   if (d->page_size % kvq::kTile) return KVQ_ERR_ARG;
   if (d->head_dim % 16) return KVQ_ERR_ARG;
-  if (d->scale_per_head != 0 && d->scale_per_head != 1) return KVQ_ERR_ARG;
-  if (d->scale_per_head && !(d->kind == KVQ_GQA && is_fp8(d->dtype))) return KVQ_ERR_UNSUPPORTED;
+  if (d->scale_mode < KVQ_SCALE_TENSOR || d->scale_mode > KVQ_SCALE_KIVI) return KVQ_ERR_ARG;
+  if (d->scale_mode != KVQ_SCALE_TENSOR && !(d->kind == KVQ_GQA && is_fp8(d->dtype))) return KVQ_ERR_UNSUPPORTED;
   if (d->kind == KVQ_GQA) {
     if (d->v_dim != d->head_dim) return KVQ_ERR_ARG;
     if (is_fp8(d->dtype)) return (d->head_dim == 64 || d->head_dim == 128) ? KVQ_OK : KVQ_ERR_UNSUPPORTED;
@@ -42,13 +43,19 @@ int check_desc(const kvq_cache_desc* d) {
   return (d->head_dim == 576 && d->v_dim == 512) ? KVQ_OK : KVQ_ERR_UNSUPPORTED;
 }
 
+// Scale buffers: FP4 block scales for K and V (bytes per row = D/16), or for
+// KIVI caches only the V buffer of one fp32 per token (scale_block = 4*P).
 void compute_layout(const kvq_cache_desc* d, kvq_layout* L, int64_t* code_block, int64_t* scale_block) {
+  const bool kivi = d->scale_mode == KVQ_SCALE_KIVI;
   const int64_t row_code = is_fp8(d->dtype) ? d->head_dim : d->head_dim / 2;
-  const int64_t row_scale = is_fp8(d->dtype) ? 0 : d->head_dim / 16;
+  const int64_t row_scale = kivi ? 4 : (is_fp8(d->dtype) ? 0 : d->head_dim / 16);
   *code_block = row_code * d->page_size;
   *scale_block = row_scale * d->page_size;
   const size_t per_code = (size_t)d->num_pages * d->num_kv_heads * (size_t)*code_block;
   const size_t per_scale = (size_t)d->num_pages * d->num_kv_heads * (size_t)*scale_block;
+  const size_t per_k_scale = kivi ? 0 : per_scale;
+  // KIVI channel calibration keeps one running max per (kv head, channel)
+  const size_t scratch = std::max(kScratchBytes, (size_t)d->num_kv_heads * d->head_dim * sizeof(unsigned));
   const bool has_v = d->kind == KVQ_GQA;
   memset(L, 0, sizeof(*L));
   size_t off = 0;
@@ -59,14 +66,14 @@ void compute_layout(const kvq_cache_desc* d, kvq_layout* L, int64_t* code_block,
   L->v_codes_bytes = has_v ? per_code : 0;
   off = align_up(off + L->v_codes_bytes);
   L->k_scales_offset = off;
-  L->k_scales_bytes = per_scale;
-  off = align_up(off + per_scale);
+  L->k_scales_bytes = per_k_scale;
+  off = align_up(off + per_k_scale);
   L->v_scales_offset = off;
   L->v_scales_bytes = has_v ? per_scale : 0;
   off = align_up(off + L->v_scales_bytes);
   L->scratch_offset = off;
-  L->scratch_bytes = kScratchBytes;
-  off = align_up(off + kScratchBytes);
+  L->scratch_bytes = scratch;
+  off = align_up(off + scratch);
   L->total_bytes = off;
 }
 
@@ -262,6 +269,7 @@ int kvq_bytes_per_token(const kvq_cache_desc* d, double* bytes_out) {
   const double bits = is_fp8(d->dtype) ? 8.0 : 4.0 + 8.0 / 16.0;
   const double rows = d->kind == KVQ_GQA ? 2.0 * d->num_kv_heads : 1.0;
   *bytes_out = rows * d->head_dim * bits / 8.0;
+  if (d->scale_mode == KVQ_SCALE_KIVI) *bytes_out += 4.0 * d->num_kv_heads;  // one fp32 V scale per token-head
   return KVQ_OK;
 }
 
@@ -308,11 +316,17 @@ int kvq_compute_scale(const kvq_cache* c, const void* x0, int64_t n0, const void
     default: return KVQ_ERR_UNSUPPORTED;
   }
   unsigned* scratch = reinterpret_cast<unsigned*>(c->base + c->layout.scratch_offset);
-  if (c->desc.scale_per_head) {
+  if (c->desc.scale_mode != KVQ_SCALE_TENSOR) {
     const int64_t row = (int64_t)c->desc.num_kv_heads * c->desc.head_dim;
     if (n0 % row || n1 % row) return KVQ_ERR_ARG;
     if ((n0 && !aligned16(x0)) || (n1 && !aligned16(x1))) return KVQ_ERR_ARG;
     Timed timer(3, static_cast<hipStream_t>(stream));
+    if (c->desc.scale_mode == KVQ_SCALE_KIVI) {
+      const hipError_t e = kvq_launch_amax_channels(static_cast<const uint16_t*>(x0), n0 / row,
+                                                    static_cast<const uint16_t*>(x1), n1 / row, (int)row, scratch,
+                                                    div, scale_out, static_cast<hipStream_t>(stream));
+      return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+    }
     const hipError_t e = kvq_launch_amax_heads(static_cast<const uint16_t*>(x0), n0 / row,
                                                static_cast<const uint16_t*>(x1), n1 / row, c->desc.num_kv_heads,
                                                c->desc.head_dim, scratch, div, scale_out,
@@ -332,6 +346,7 @@ int kvq_store(const kvq_cache* c, const void* k, const void* v, const int64_t* s
   if (!k || !slots || !aligned16(k)) return KVQ_ERR_ARG;
   if (c->desc.kind == KVQ_GQA) {
     if (!v || !aligned16(v)) return KVQ_ERR_ARG;
+    if (c->desc.scale_mode == KVQ_SCALE_KIVI && (!k_scale || !aligned16(k_scale))) return KVQ_ERR_ARG;
   } else {
     if (v) return KVQ_ERR_ARG;
     if (!k_scale) return KVQ_ERR_ARG;  // NVFP4 needs its global scale
@@ -374,6 +389,7 @@ int decode_impl(const kvq_cache* c, const void* k_new, const void* v_new, const 
     if (hq % d.num_kv_heads) return KVQ_ERR_ARG;
     const int G = hq / d.num_kv_heads;
     if (G > 16) return KVQ_ERR_UNSUPPORTED;
+    if (d.scale_mode == KVQ_SCALE_KIVI && (!k_scale || !aligned16(k_scale))) return KVQ_ERR_ARG;
     const SplitPlan plan = plan_gqa(batch, d.num_kv_heads, max_len);
     const WsLayout wl = workspace_for(plan, batch, hq, d.v_dim);
     const size_t need = wl.total;
@@ -394,7 +410,8 @@ int decode_impl(const kvq_cache* c, const void* k_new, const void* v_new, const 
     const bool fp8 = is_fp8(d.dtype);
     a.k_scale = fp8 ? k_scale : nullptr;
     a.v_scale = fp8 ? v_scale : nullptr;
-    a.scale_per_head = d.scale_per_head;
+    a.scale_mode = d.scale_mode;
+    if (d.scale_mode == KVQ_SCALE_KIVI) a.v_scale = nullptr;  // V scales come from the cache
     a.sm_scale_log2 = sm_scale * 1.4426950408889634f;
     a.batch = batch;
     a.hq = hq;

@@ -111,7 +111,8 @@ struct GqaDecodeArgs {
   const int32_t* seq_lens;
   const float* k_scale;
   const float* v_scale;
-  int scale_per_head;   // FP8: k/v_scale are [hkv] arrays
+  int scale_mode;       // kvq_scale_mode (FP8): HEAD -> k/v_scale [hkv]; KIVI -> k_scale [hkv][D],
+                        // V scales per token in v_scales (fp32, scale_block_bytes = 4*P per page-head)
   float sm_scale_log2;  // sm_scale * log2(e)
   int batch, hq, hkv, group, page_size, max_len;
   int tiles_per_split, num_splits;
@@ -166,5 +167,7 @@ hipError_t kvq_launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t kvq_launch_dequant_prev(const kvq_cache* c, const int32_t* pages, int32_t n_pages, const float* g_scale,
                                    const float* ks_out, const float* vs_out, uint8_t* dq_k, uint8_t* dq_v,
                                    hipStream_t s);
+hipError_t kvq_launch_amax_channels(const uint16_t* x0, int64_t rows0, const uint16_t* x1, int64_t rows1, int cols,
+                                   unsigned* scratch, float fmt_div, float* scale_out, hipStream_t s);
 hipError_t kvq_launch_amax_heads(const uint16_t* x0, int64_t rows0, const uint16_t* x1, int64_t rows1, int hkv,
                                  int dim, unsigned* scratch, float fmt_div, float* scale_out, hipStream_t s);

@@ -106,13 +106,58 @@ __global__ void __launch_bounds__(256) amax_head_final_kernel(const unsigned* __
   }
 }
 
-// one thread per (token, kv head, 16-element chunk)
+// Per-(kv head, channel) amax of x[rows][ng * 8] BF16 for KIVI-style K
+// scales: each thread keeps the running max of its 8 columns over a stride of
+// rows, then one atomic max per column into acc (zeroed first by
+// zero_u32_kernel; a fill kernel rather than a memset keeps the calibration
+// capturable in a graph).
+__global__ void __launch_bounds__(256) zero_u32_kernel(unsigned* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+__global__ void __launch_bounds__(256) amax_chan_partial_kernel(const uint16_t* __restrict__ x0, int64_t rows0,
+                                                                const uint16_t* __restrict__ x1, int64_t rows1,
+                                                                int ng, unsigned* __restrict__ acc) {
+  const int q = blockIdx.y * blockDim.x + threadIdx.x;
+  if (q >= ng) return;
+  unsigned m[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+  for (int which = 0; which < 2; ++which) {
+    const uint16_t* x = which ? x1 : x0;
+    const int64_t rows = which ? rows1 : rows0;
+    if (x == nullptr || rows <= 0) continue;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+      const uint4 w = *reinterpret_cast<const uint4*>(x + (r * ng + q) * 8);
+      const uint32_t a4[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        m[2 * j] = max(m[2 * j], a4[j] & 0x7fffu);
+        m[2 * j + 1] = max(m[2 * j + 1], (a4[j] >> 16) & 0x7fffu);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (m[j]) atomicMax(acc + 8 * q + j, m[j]);
+}
+
+// out[i] = amax_i / fmt_div (1.0 for an all-zero column)
+__global__ void __launch_bounds__(256) amax_chan_final_kernel(const unsigned* __restrict__ acc, int n, float fmt_div,
+                                                              float* __restrict__ out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float amax = bf16_bits_to_f32(acc[i]);
+  out[i] = (amax == 0.f) ? 1.0f : amax / fmt_div;  // IEEE binary32 division
+}
+
+// one thread per (token, kv head, 16-element chunk); the D/16 chunks of a row
+// are consecutive lanes (the KIVI V row amax is reduced across them)
 template <int FMT>
 __global__ void __launch_bounds__(256) store_fp8_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const int64_t* __restrict__ slots,
     int32_t n_tok, int hkv, int dim, int page_size, int64_t capacity, const float* __restrict__ k_scale,
-    const float* __restrict__ v_scale, int scale_per_head, uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
-    int64_t block_bytes) {
+    const float* __restrict__ v_scale, int mode, uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+    int64_t block_bytes, uint8_t* __restrict__ vts, int64_t vts_block) {
   const int chunks = dim / 16;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (int64_t)n_tok * hkv * chunks) return;
@@ -125,11 +170,17 @@ __global__ void __launch_bounds__(256) store_fp8_kernel(
   const int64_t page = slot / page_size;
   const int t = (int)(slot % page_size);
   const int t16 = t & 15;
-  const int si = scale_per_head ? h : 0;
-  const float ks = k_scale ? k_scale[si] : 1.0f;
-  const float vs = v_scale ? v_scale[si] : 1.0f;
   const int64_t row = (tok * hkv + h) * dim;
   const int64_t base = (page * hkv + h) * block_bytes + (int64_t)(t >> 4) * 16 * dim;
+  if (mode == KVQ_SCALE_KIVI) {
+    const float vs = put_fp8_chunk_kivi<FMT>(k + row, v + row, c, chunks, t16, k_scale + (int64_t)h * dim, kc, vc,
+                                             base);
+    if (c == 0) reinterpret_cast<float*>(vts + (page * hkv + h) * vts_block)[t] = vs;
+    return;
+  }
+  const int si = mode == KVQ_SCALE_HEAD ? h : 0;
+  const float ks = k_scale ? k_scale[si] : 1.0f;
+  const float vs = v_scale ? v_scale[si] : 1.0f;
   put_fp8_chunk<FMT>(k + row, v + row, c, t16, ks, vs, kc, vc, base);
 }
 
@@ -209,6 +260,18 @@ hipError_t kvq_launch_amax_heads(const uint16_t* x0, int64_t rows0, const uint16
   return hipGetLastError();
 }
 
+hipError_t kvq_launch_amax_channels(const uint16_t* x0, int64_t rows0, const uint16_t* x1, int64_t rows1, int cols,
+                                   unsigned* scratch, float fmt_div, float* scale_out, hipStream_t s) {
+  const int ng = cols / 8;
+  const int64_t rows = rows0 + rows1;
+  int gx = (int)((rows + 63) / 64);
+  gx = gx < 1 ? 1 : (gx > 256 ? 256 : gx);
+  zero_u32_kernel<<<(cols + 255) / 256, 256, 0, s>>>(scratch, cols);
+  amax_chan_partial_kernel<<<dim3(gx, (ng + 255) / 256), 256, 0, s>>>(x0, rows0, x1, rows1, ng, scratch);
+  amax_chan_final_kernel<<<(cols + 255) / 256, 256, 0, s>>>(scratch, cols, fmt_div, scale_out);
+  return hipGetLastError();
+}
+
 hipError_t kvq_launch_store(const kvq_cache* c, const uint16_t* k, const uint16_t* v, const int64_t* slots,
                             int32_t n, const float* k_scale, const float* v_scale, hipStream_t s) {
   const kvq_cache_desc& d = c->desc;
@@ -220,14 +283,16 @@ hipError_t kvq_launch_store(const kvq_cache* c, const uint16_t* k, const uint16_
     const int grid = (int)((threads + 255) / 256);
     if (d.dtype == KVQ_FP8_E4M3)
       store_fp8_kernel<KVQ_FP8_E4M3><<<grid, 256, 0, s>>>(k, v, slots, n, d.num_kv_heads, d.head_dim, d.page_size,
-                                                         capacity, k_scale, v_scale, d.scale_per_head,
-                                                         base + L.k_codes_offset,
-                                                         base + L.v_codes_offset, c->code_block_bytes);
+                                                         capacity, k_scale, v_scale, d.scale_mode,
+                                                         base + L.k_codes_offset, base + L.v_codes_offset,
+                                                         c->code_block_bytes, base + L.v_scales_offset,
+                                                         c->scale_block_bytes);
     else
       store_fp8_kernel<KVQ_FP8_E5M2><<<grid, 256, 0, s>>>(k, v, slots, n, d.num_kv_heads, d.head_dim, d.page_size,
-                                                         capacity, k_scale, v_scale, d.scale_per_head,
-                                                         base + L.k_codes_offset,
-                                                         base + L.v_codes_offset, c->code_block_bytes);
+                                                         capacity, k_scale, v_scale, d.scale_mode,
+                                                         base + L.k_codes_offset, base + L.v_codes_offset,
+                                                         c->code_block_bytes, base + L.v_scales_offset,
+                                                         c->scale_block_bytes);
   } else if (d.dtype == KVQ_FP4_MX16) {
     const int64_t threads = (int64_t)n * d.num_kv_heads * (d.head_dim / 16);
     const int grid = (int)((threads + 255) / 256);

@@ -6,7 +6,9 @@
 // Quantization rules (the pages: SGLang "Quantized KV Cache" page, sections
 // "Supported formats" and "Scaling factors"; PR #21954 analysis page,
 // NVFP4KVMethod / BlockFP4KVMethod and quantize_and_store):
-//   FP8:   code = RNE(clamp(x / s, -max, max)) with x / s IEEE binary32
+//   FP8:   code = RNE(clamp(x / s, -max, max)) with x / s IEEE binary32; s per
+//          tensor, per KV head, or KIVI-style (per channel for K, per token
+//          for V: s = fl32(row amax / max))
 //   MX16:  per 16 elements e = floor(log2 amax) - 2 (clamped to [-127, 127]),
 //          element = RNE_sat_E2M1(x * 2^-e), scale byte = e + 127
 //   NVFP4: per 16 elements s = amax / fl32(6 g) -> E4M3 (saturating),
@@ -69,6 +71,71 @@ __device__ __forceinline__ void put_fp8_chunk(const uint16_t* krow, const uint16
   const uint32_t vw[4] = {vq.x, vq.y, vq.z, vq.w};
 #pragma unroll
   for (int r = 0; r < 16; ++r) vb[16 * r] = (uint8_t)(vw[r >> 2] >> (8 * (r & 3)));
+}
+
+// ------------------------------------------------ FP8, KIVI-style scaling --
+// K: one scale per (kv head, channel); V: one scale per (token, kv head),
+// fl32(row amax / format max) (1.0 for an all-zero row), computed here.
+// The "KV cache quantization mechanism and traps" page, K and V distributions.
+
+// 16 BF16 / 16 per-element scales -> 16 FP8 codes.
+template <int FMT>
+__device__ __forceinline__ uint4 quant_fp8_16_vec(const uint4 lo, const uint4 hi, const float* s) {
+  const uint32_t in[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  uint32_t out[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w0 = in[2 * i], w1 = in[2 * i + 1];
+    out[i] = encode_fp8x4<FMT>(bf16_bits_to_f32(w0 & 0xffffu) / s[4 * i], bf16_bits_to_f32(w0 >> 16) / s[4 * i + 1],
+                               bf16_bits_to_f32(w1 & 0xffffu) / s[4 * i + 2],
+                               bf16_bits_to_f32(w1 >> 16) / s[4 * i + 3]);
+  }
+  return make_uint4(out[0], out[1], out[2], out[3]);
+}
+
+// Largest BF16 magnitude bits (finite values order like bits & 0x7fff).
+__device__ __forceinline__ uint32_t amax16_bits(const uint4 lo, const uint4 hi) {
+  const uint32_t in[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = max(m, max(in[i] & 0x7fffu, (in[i] >> 16) & 0x7fffu));
+  return m;
+}
+
+// Chunk c of one (token, kv head) row pair, called by the `chunks` = D/16
+// consecutive lanes of a row together (lane c holds chunk c; the lanes form
+// an aligned group of the wave, all active). ks = the head's D channel
+// scales. Returns the row's V scale (every lane gets it).
+template <int FMT>
+__device__ __forceinline__ float put_fp8_chunk_kivi(const uint16_t* krow, const uint16_t* vrow, int c, int chunks,
+                                                    int t16, const float* ks, uint8_t* kc, uint8_t* vc,
+                                                    int64_t base) {
+  constexpr float MX = (FMT == KVQ_FP8_E4M3) ? 448.0f : 57344.0f;
+  const uint4* kp = reinterpret_cast<const uint4*>(krow + 16 * c);
+  const uint4* vp = reinterpret_cast<const uint4*>(vrow + 16 * c);
+  const uint4 v0 = vp[0], v1 = vp[1];
+  uint32_t m = amax16_bits(v0, v1);
+  for (int off = 1; off < chunks; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  const float amax = bf16_bits_to_f32(m);
+  const float vs = amax == 0.f ? 1.0f : amax / MX;  // IEEE binary32 division
+  float kss[16];
+  const float4* kq4 = reinterpret_cast<const float4*>(ks + 16 * c);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 q = kq4[i];
+    kss[4 * i] = q.x;
+    kss[4 * i + 1] = q.y;
+    kss[4 * i + 2] = q.z;
+    kss[4 * i + 3] = q.w;
+  }
+  const uint4 kq = quant_fp8_16_vec<FMT>(kp[0], kp[1], kss);
+  const uint4 vq = quant_fp8_16<FMT>(v0, v1, vs);
+  *reinterpret_cast<uint4*>(kc + base + 256 * c + 16 * t16) = kq;
+  uint8_t* vb = vc + base + 1024 * (c >> 2) + 16 * (16 * (t16 >> 2)) + 4 * (c & 3) + (t16 & 3);
+  const uint32_t vw[4] = {vq.x, vq.y, vq.z, vq.w};
+#pragma unroll
+  for (int r = 0; r < 16; ++r) vb[16 * r] = (uint8_t)(vw[r >> 2] >> (8 * (r & 3)));
+  return vs;
 }
 
 // ------------------------------------------------------------- FP4 (E2M1) --

@@ -42,6 +42,7 @@ class Workload:
     new_tokens: int            # tokens stored per sequence by the timed step
     dist: str                  # "tiny" | "llama" | "qwen" | "mla"
     scale_mode: str = "amax"   # FP8: "amax" (calibrated per tensor) | "amax_head" (per KV head) | "one"
+    #                            | "kivi" (K per channel, calibrated; V per token at store)
     seed: int = 1
     extra: dict = field(default_factory=dict)
 

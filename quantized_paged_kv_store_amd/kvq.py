@@ -12,11 +12,13 @@ import math
 import os
 from ctypes import POINTER, byref, c_char_p, c_double, c_float, c_int32, c_int64, c_size_t, c_void_p
 
+import numpy as np
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
 
 DTYPES = {"e4m3": 1, "e5m2": 2, "mx16": 3, "nvfp4": 4}
+SCALE_MODES = {"tensor": 0, "head": 1, "kivi": 2}
 KINDS = {"gqa": 0, "mla": 1}
 STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_ARG", -2: "KVQ_ERR_UNSUPPORTED", -3: "KVQ_ERR_SIZE", -4: "KVQ_ERR_HIP"}
 
@@ -29,7 +31,7 @@ class KVQError(RuntimeError):
 
 class CacheDesc(ctypes.Structure):
     _fields_ = [("dtype", c_int32), ("kind", c_int32), ("num_kv_heads", c_int32), ("head_dim", c_int32),
-                ("v_dim", c_int32), ("page_size", c_int32), ("num_pages", c_int64), ("scale_per_head", c_int32)]
+                ("v_dim", c_int32), ("page_size", c_int32), ("num_pages", c_int64), ("scale_mode", c_int32)]
 
 
 class Layout(ctypes.Structure):
@@ -101,9 +103,12 @@ def _stream(device) -> c_void_p:
 
 
 def make_desc(dtype: str, kind: str, num_kv_heads: int, head_dim: int, v_dim: int, page_size: int,
-              num_pages: int, scale_per_head: bool = False) -> CacheDesc:
+              num_pages: int, scale_per_head: bool = False, scale_mode: str | None = None) -> CacheDesc:
+    """scale_mode: "tensor", "head" (same as scale_per_head=True) or "kivi"
+    (FP8 K scales per channel, V scales per token)."""
+    mode = SCALE_MODES[scale_mode] if scale_mode is not None else (1 if scale_per_head else 0)
     return CacheDesc(DTYPES[dtype], KINDS[kind], num_kv_heads, head_dim, v_dim, page_size, num_pages,
-                     1 if scale_per_head else 0)
+                     mode)
 
 
 def kvq_bytes_per_token(desc: CacheDesc) -> float:
@@ -145,8 +150,9 @@ class Cache:
 
 
 def kvq_alloc_pages(dtype: str, kind: str, num_kv_heads: int, head_dim: int, v_dim: int, page_size: int,
-                    num_pages: int, device="cuda", fill: int | None = None, scale_per_head: bool = False) -> Cache:
-    desc = make_desc(dtype, kind, num_kv_heads, head_dim, v_dim, page_size, num_pages, scale_per_head)
+                    num_pages: int, device="cuda", fill: int | None = None, scale_per_head: bool = False,
+                    scale_mode: str | None = None) -> Cache:
+    desc = make_desc(dtype, kind, num_kv_heads, head_dim, v_dim, page_size, num_pages, scale_per_head, scale_mode)
     need = c_size_t()
     _check(_lib().kvq_alloc_pages(byref(desc), None, 0, byref(need), None), "kvq_alloc_pages(query)")
     mem = torch.empty(need.value, dtype=torch.uint8, device=device)
@@ -156,18 +162,23 @@ def kvq_alloc_pages(dtype: str, kind: str, num_kv_heads: int, head_dim: int, v_d
 
 
 def _dev_f32(x, device, n=1):
-    """A device fp32 scale: n >= 1 values (n = num_kv_heads for per-head FP8 scales)."""
+    """A device fp32 scale array of at least n values (1 per tensor, Hkv per
+    head, Hkv * D KIVI channel scales); host values are flattened."""
     if x is None:
         return None
     if not isinstance(x, torch.Tensor):
-        x = torch.tensor([float(v) for v in (x if hasattr(x, "__len__") else [x])], dtype=torch.float32,
-                         device=device)
+        x = torch.tensor(np.asarray(x, dtype=np.float32).reshape(-1).tolist(), dtype=torch.float32, device=device)
     assert x.dtype == torch.float32 and x.device == device and x.is_contiguous() and x.numel() >= n
     return x
 
 
-def _n_scales(cache: "Cache") -> int:
-    return cache.desc.num_kv_heads if cache.desc.scale_per_head else 1
+def _n_scales(cache: "Cache", which: str = "k") -> int:
+    """Floats of a k_scale / v_scale argument: 1, Hkv (per head), Hkv * D
+    (KIVI K channel scales; KIVI V scales live in the cache, none passed)."""
+    d = cache.desc
+    if d.scale_mode == SCALE_MODES["kivi"]:
+        return d.num_kv_heads * d.head_dim if which == "k" else 0
+    return d.num_kv_heads if d.scale_mode == SCALE_MODES["head"] else 1
 
 
 def kvq_compute_scale(cache: Cache, x0: torch.Tensor, x1: torch.Tensor | None = None,
@@ -190,7 +201,7 @@ def kvq_store(cache: Cache, k: torch.Tensor, v: torch.Tensor | None, slot_mappin
     if v is not None:
         assert v.dtype == torch.bfloat16 and v.is_contiguous() and v.device == dev
     assert slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous() and slot_mapping.device == dev
-    ks, vs = _dev_f32(k_scale, dev, _n_scales(cache)), _dev_f32(v_scale, dev, _n_scales(cache))
+    ks, vs = _dev_f32(k_scale, dev, _n_scales(cache)), _dev_f32(v_scale, dev, _n_scales(cache, "v"))
     _check(_lib().kvq_store(cache.handle, _ptr(k), _ptr(v), _ptr(slot_mapping), slot_mapping.numel(), _ptr(ks),
                             _ptr(vs), _stream(dev)), "kvq_store")
 
@@ -214,7 +225,7 @@ def kvq_decode(cache: Cache, q: torch.Tensor, page_table: torch.Tensor, seq_lens
     need = kvq_decode_workspace_bytes(cache, B, Hq, max_seq_len)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ks, vs = _dev_f32(k_scale, dev, _n_scales(cache)), _dev_f32(v_scale, dev, _n_scales(cache))
+    ks, vs = _dev_f32(k_scale, dev, _n_scales(cache)), _dev_f32(v_scale, dev, _n_scales(cache, "v"))
     _check(_lib().kvq_decode(cache.handle, _ptr(q), B, Hq, _ptr(page_table), page_table.shape[1], _ptr(seq_lens),
                              max_seq_len, float(sm_scale), _ptr(ks), _ptr(vs), _ptr(out), _ptr(lse),
                              _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(dev)),
@@ -243,7 +254,7 @@ def kvq_decode_append(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor | N
     need = kvq_decode_workspace_bytes(cache, B, Hq, max_seq_len)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ks, vs = _dev_f32(k_scale, dev, _n_scales(cache)), _dev_f32(v_scale, dev, _n_scales(cache))
+    ks, vs = _dev_f32(k_scale, dev, _n_scales(cache)), _dev_f32(v_scale, dev, _n_scales(cache, "v"))
     _check(_lib().kvq_decode_append(cache.handle, _ptr(k_new), _ptr(v_new), _ptr(q), B, Hq, _ptr(page_table),
                                     page_table.shape[1], _ptr(seq_lens), max_seq_len, float(sm_scale), _ptr(ks),
                                     _ptr(vs), _ptr(out), _ptr(lse), _ptr(workspace),

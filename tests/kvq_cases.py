@@ -23,6 +23,14 @@ from quantized_paged_kv_store_amd import inputs as I
 # padding bytes of never-written slots: NaN codes for FP8 and E8M0 scales
 FILL = {"e4m3": 0x7F, "e5m2": 0x7F, "mx16": 0xFF, "nvfp4": 0xFF}
 TOL_MAX_ABS = 4e-3
+CACHE_SCALE_MODE = {"amax_head": "head", "kivi": "kivi"}
+
+
+def cache_scale_mode(w) -> str:
+    """The cache descriptor's scale mode for a workload's scale_mode."""
+    return CACHE_SCALE_MODE.get(w.scale_mode, "tensor")
+
+
 TOL_REL_L2 = 1e-3
 _THREADS = min(16, os.cpu_count() or 4)
 
@@ -90,7 +98,7 @@ class Case:
         assert not append or w.new_tokens == 1
         self.cache = K.kvq_alloc_pages(w.dtype, w.kind, w.kv_heads, w.head_dim, w.v_dim, w.page_size,
                                        self.npages, device=self.dev, fill=self.fill,
-                                       scale_per_head=w.scale_mode == "amax_head")
+                                       scale_mode=cache_scale_mode(w))
         pre = [(b, 0, int(self.prefill[b])) for b in range(w.batch) if self.prefill[b] > 0]
         new = [(b, int(self.prefill[b]), int(self.lens[b])) for b in range(w.batch) if self.lens[b] > self.prefill[b]]
         if self.data is None:
@@ -100,7 +108,9 @@ class Case:
         if kp is not None and len(kp):
             kd, sd = self._bf16(kp), self._to_dev(sp)
             vd = None if vp is None else self._bf16(vp)
-            if w.dtype in ("e4m3", "e5m2") and w.scale_mode in ("amax", "amax_head"):
+            if w.dtype in ("e4m3", "e5m2") and w.scale_mode == "kivi":
+                self.k_scale = K.kvq_compute_scale(self.cache, kd)      # K channel scales; V per token
+            elif w.dtype in ("e4m3", "e5m2") and w.scale_mode in ("amax", "amax_head"):
                 if w.dist == "tiny":   # one scale for K and V jointly
                     self.k_scale = K.kvq_compute_scale(self.cache, kd, vd)
                     self.v_scale = self.k_scale
@@ -118,6 +128,9 @@ class Case:
             if w.scale_mode == "amax_head":     # [Hkv] magnitudes per head (BF16 bits order like values)
                 mag = lambda a: I.bf16_to_f32((a.reshape(len(a), w.kv_heads, -1) & 0x7FFF).max(axis=(0, 2)).astype(np.uint16))
                 self.host_amax = (mag(kp), None if vp is None else mag(vp))
+            elif w.scale_mode == "kivi":        # [Hkv, D] K magnitudes per channel
+                mag = I.bf16_to_f32((kp.reshape(len(kp), w.kv_heads, -1) & 0x7FFF).max(axis=0).astype(np.uint16))
+                self.host_amax = (mag, None)
             else:
                 ak = float(np.abs(I.bf16_to_f32(kp)).max())
                 av = None if vp is None else float(np.abs(I.bf16_to_f32(vp)).max())
@@ -154,6 +167,8 @@ class Case:
         return self
 
     def gpu_scales(self):
+        if self.w.scale_mode == "kivi":
+            return self.k_scale.cpu().numpy().astype(np.float32).reshape(self.w.kv_heads, -1), None
         if self.w.scale_mode == "amax_head":
             f = lambda t: None if t is None else t.cpu().numpy().astype(np.float32)
         else:
@@ -166,6 +181,9 @@ class Case:
         if self.host_amax is None:
             return (np.float32(1.0) if w.dtype == "nvfp4" else None), None
         ak, av = self.host_amax
+        if w.dtype in ("e4m3", "e5m2") and w.scale_mode == "kivi":
+            fmt = E4M3 if w.dtype == "e4m3" else E5M2
+            return Q.fp8_channel_scales(np.asarray(ak, np.float64)[None], fmt), None
         if w.dtype in ("e4m3", "e5m2") and w.scale_mode == "amax_head":
             fmt = E4M3 if w.dtype == "e4m3" else E5M2
             per_head = lambda a: Q.fp8_head_scales(np.asarray(a, np.float64)[None, :, None], fmt)
@@ -196,7 +214,8 @@ class Case:
         for b in batch_ids:
             n = (int(self.lens[b]) + P - 1) // P
             otable[b, :n] = [remap[int(p)] for p in self.table[b, :n]]
-        spec = CacheSpec(w.dtype, w.kind, w.kv_heads, w.head_dim, w.v_dim, P, max(len(pages), 1))
+        spec = CacheSpec(w.dtype, w.kind, w.kv_heads, w.head_dim, w.v_dim, P, max(len(pages), 1),
+                         kivi=w.scale_mode == "kivi")
         oc = OracleCache(spec, fill=self.fill)
         ks, vs = self.oracle_scales()
         for b in batch_ids:

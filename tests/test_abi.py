@@ -208,21 +208,21 @@ def test_per_head_scale_descriptor_rules():
     lib = _lib()
     need = c_size_t()
     d = _desc("e4m3")
-    d.scale_per_head = 1
+    d.scale_mode = 1
     assert lib.kvq_alloc_pages(byref(d), None, 0, byref(need), None) == OK
     for dtype, kind, args in (("mx16", "gqa", ()), ("nvfp4", "mla", (1, 576, 512, 64))):
         d = _desc(dtype, kind, *args)
-        d.scale_per_head = 1
+        d.scale_mode = 1
         assert lib.kvq_alloc_pages(byref(d), None, 0, byref(need), None) == UNSUP
     d = _desc("e4m3")
-    d.scale_per_head = 2
+    d.scale_mode = -1
     assert lib.kvq_alloc_pages(byref(d), None, 0, byref(need), None) == ARG
 
 
 def test_per_head_compute_scale_shape_errors():
     lib = _lib()
     d = _desc("e4m3", hkv=4)
-    d.scale_per_head = 1
+    d.scale_mode = 1
     need = c_size_t()
     h = c_void_p()
     assert lib.kvq_alloc_pages(byref(d), None, 0, byref(need), None) == OK
@@ -248,3 +248,36 @@ def test_dequantize_prev_kv_argument_errors(handles):
     assert f(h["mla"], P, 4, P, None, None, P, P, None) == ARG                    # MLA has no dq_v
     assert f(h["mla"], P, 4, P, None, P, P, None, None) == ARG                    # nor a V output scale
     assert f(None, P, 4, None, None, None, P, P, None) == ARG
+
+
+def test_kivi_descriptor_layout_and_accounting():
+    """KIVI-style caches: FP8 GQA only; no K scale buffer, one fp32 V scale
+    per (page, kv head, token); 4 bytes per token-head in the accounting;
+    the scratch holds one running max per (kv head, channel)."""
+    lib = _lib()
+    need = c_size_t()
+    for dtype, kind, args in (("mx16", "gqa", ()), ("nvfp4", "mla", (1, 576, 512, 64))):
+        d = _desc(dtype, kind, *args)
+        d.scale_mode = 2
+        assert lib.kvq_alloc_pages(byref(d), None, 0, byref(need), None) == UNSUP
+    d = _desc("e4m3", hkv=4, d=128, p=32, n=10)
+    d.scale_mode = 3
+    assert lib.kvq_alloc_pages(byref(d), None, 0, byref(need), None) == ARG
+    d.scale_mode = 2
+    assert lib.kvq_alloc_pages(byref(d), None, 0, byref(need), None) == OK
+    h = c_void_p()
+    assert lib.kvq_alloc_pages(byref(d), c_void_p(FAKE_DEV), need.value, byref(need), byref(h)) == OK
+    L = Layout()
+    assert lib.kvq_cache_layout(h, byref(L)) == OK
+    assert L.k_scales_bytes == 0 and L.v_scales_bytes == 10 * 4 * 32 * 4
+    assert L.scratch_bytes >= 4 * 128 * 4
+    bpt = ctypes.c_double()
+    assert lib.kvq_bytes_per_token(byref(d), byref(bpt)) == OK and bpt.value == 2 * 4 * 128 + 4 * 4
+    P = c_void_p(FAKE_DEV)
+    # K channel scales are required (and 16-byte aligned) for store and decode
+    assert lib.kvq_store(h, P, P, P, 4, None, None, None) == ARG
+    assert lib.kvq_store(h, P, P, P, 4, c_void_p(FAKE_DEV + 4), None, None) == ARG
+    dec = lambda ks: lib.kvq_decode(h, P, 2, 8, P, 4, P, 64, 0.1, ks, None, P, None, None, 0, None)
+    assert dec(None) == ARG and dec(c_void_p(FAKE_DEV + 4)) == ARG
+    assert lib.kvq_compute_scale(h, P, 4 * 128 + 8, None, 0, P, None) == ARG     # whole rows only
+    lib.kvq_free_handle(h)
