@@ -40,7 +40,8 @@ def measured_traffic(w, op="decode"):
     import hashlib
     if op == "decode":
         kind = "gqa" if w.kind == "gqa" else "mla"
-        path = os.path.join(ROOT, "profiles", f"kvq_decode_{kind}_{w.name}_{w.dtype}_traffic.json")
+        mode = {"amax_head": "_head", "kivi": "_kivi"}.get(w.scale_mode, "")
+        path = os.path.join(ROOT, "profiles", f"kvq_decode_{kind}_{w.name}_{w.dtype}{mode}_traffic.json")
     else:
         path = os.path.join(ROOT, "profiles", f"kvq_dequant_prev_{w.dtype}_{w.name}_traffic.json")
     if not os.path.exists(path):
