@@ -72,3 +72,53 @@ def decode_attention(cache: OracleCache, q, page_table, seq_lens, sm_scale,
             out[b, hs] = o
             lse[b, hs] = l
     return out, lse
+
+
+# --------------------------------------------------------------------------
+# Extend (chunked prefill) attention over a quantized prefix. The PR #21954
+# analysis page ("code analysis") has dequantize_prev_kv turn the FP4 prefix
+# into FP8 E4M3 workspaces (dq_k_buffer / dq_v_buffer) because only FP8
+# prefill kernels exist; reading adopted for the attention that reads them:
+# the C_b new tokens of sequence b attend to its L0_b prefix tokens through
+# those E4M3 rows (value = decode(code) * s_k or s_v, the workspace's
+# per-tensor scales) and to the chunk's own BF16 K/V causally (chunk token i
+# sees chunk tokens 0..i), all query heads of a KV head sharing it (GQA).
+# Prefix token t of sequence b is row t % P of page page_off[b] + t // P of
+# the [n_pages, Hkv, P, D] workspace.
+# --------------------------------------------------------------------------
+def extend_attention(q, k_new, v_new, cu_q, prefix_len, dq_k, dq_v, page_off, s_k, s_v, sm_scale,
+                     rows=None):
+    """q [Nq, Hq, D], k_new / v_new [Nq, Hkv, D] (float), cu_q [B+1] chunk
+    offsets, prefix_len / page_off [B], dq_k / dq_v uint8 E4M3 [n_pages, Hkv,
+    P, D], s_k / s_v binary32 (None = 1.0) -> (out [Nq, Hq, D], lse [Nq, Hq])
+    float64; ``rows`` restricts the work to some chunk rows (others nan)."""
+    from .formats import E4M3, decode
+    q = np.asarray(q, dtype=np.float64)
+    k_new = np.asarray(k_new, dtype=np.float64)
+    v_new = np.asarray(v_new, dtype=np.float64)
+    Nq, Hq, D = q.shape
+    Hkv = k_new.shape[1]
+    G = Hq // Hkv
+    P = dq_k.shape[2]
+    sk = 1.0 if s_k is None else float(np.float32(s_k))
+    sv = 1.0 if s_v is None else float(np.float32(s_v))
+    out = np.full((Nq, Hq, D), np.nan)
+    lse = np.full((Nq, Hq), np.nan)
+    want = None if rows is None else set(int(r) for r in rows)
+    for b in range(len(prefix_len)):
+        L0 = int(prefix_len[b])
+        t = np.arange(L0)
+        pg = int(page_off[b]) + t // P
+        for kvh in range(Hkv):
+            kp = decode(dq_k[pg, kvh, t % P].astype(np.int64), E4M3) * sk
+            vp = decode(dq_v[pg, kvh, t % P].astype(np.int64), E4M3) * sv
+            hs = slice(kvh * G, (kvh + 1) * G)
+            for r in range(int(cu_q[b]), int(cu_q[b + 1])):
+                if want is not None and r not in want:
+                    continue
+                keys = np.concatenate([kp, k_new[int(cu_q[b]):r + 1, kvh]])
+                vals = np.concatenate([vp, v_new[int(cu_q[b]):r + 1, kvh]])
+                o, l = softmax_attention(q[r, hs], keys, vals, sm_scale)
+                out[r, hs] = o
+                lse[r, hs] = l
+    return out, lse
