@@ -318,6 +318,122 @@ def bench_dequant_prev(w, args, dev):
     print(json.dumps(res), flush=True)
 
 
+def extend_flops(prefix, chunk, hq, d):
+    """Algorithmic flops of extend attention: chunk token i of a sequence with
+    prefix L0 scores and weighs L0 + i + 1 keys, 2 * d flops each for QK and PV
+    per query head."""
+    c = np.asarray(chunk, np.float64)
+    return float(np.sum(c * np.asarray(prefix, np.float64) + c * (c + 1) / 2) * hq * 4 * d)
+
+
+def extend_cpu_baseline(w, rows=48):
+    """The oracle's extend_attention, untuned, on a few chunk rows of one
+    sequence of the same shape (all query heads, full prefix)."""
+    from oracle.attention import extend_attention
+    from quantized_paged_kv_store_amd import inputs as I
+    L0 = w.max_len - w.new_tokens
+    inp = I.extend_inputs(9, [L0], [rows], w.kv_heads, w.group, w.head_dim, w.page_size)
+    f = lambda a: I.bf16_to_f32(a).astype(np.float64)
+    t0 = time.perf_counter()
+    extend_attention(f(inp["q"]), f(inp["k_new"]), f(inp["v_new"]), inp["cu_q"], inp["prefix_len"], inp["dq_k"],
+                     inp["dq_v"], inp["page_off"], 0.05, 0.05, I.sm_scale(w))
+    dt = time.perf_counter() - t0
+    fl = extend_flops([L0], [rows], w.q_heads, w.head_dim)
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas = 1
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas),
+            "host_cores_available": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{rows} chunk rows x {w.q_heads} heads over a {L0}-token prefix: float64 oracle "
+                      f"extend_attention {dt:.2f} s (E4M3 workspace decode included)"}
+
+
+def bench_extend(w, args, dev):
+    """One chunked-prefill step of the FP4 workload: kvq_store of the chunk
+    (new_tokens per sequence), kvq_dequantize_prev_kv of every prefix page to
+    E4M3, then kvq_extend_attention of the chunk over prefix + chunk."""
+    import torch
+
+    import quantized_paged_kv_store_amd as K
+    from quantized_paged_kv_store_amd import inputs as I
+    t0 = time.time()
+    st = setup(w, dev, 1)
+    log(f"setup {time.time() - t0:.1f} s")
+    cache = st["caches"][0]
+    lens = st["lens_h"]
+    C = w.new_tokens
+    prefix = (lens - C).astype(np.int32)
+    assert np.all(prefix >= 0)
+    table, _ = I.page_table(w, lens)
+    P = w.page_size
+    npg = (prefix + P - 1) // P
+    pages = np.concatenate([table[b, :npg[b]] for b in range(w.batch)]).astype(np.int32)
+    page_off = np.concatenate([[0], np.cumsum(npg)[:-1]]).astype(np.int32)
+    pages_d = torch.from_numpy(pages).to(dev)
+    s_k = torch.tensor([0.05], dtype=torch.float32, device=dev)
+    s_v = torch.tensor([0.05], dtype=torch.float32, device=dev)
+    dk, dv = K.kvq_dequantize_prev_kv(cache, pages_d, s_k, s_v)
+    k_new, v_new, slots = st["new"]
+    nq = w.batch * C
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(w.seed)
+    q = torch.randn((nq, w.q_heads, w.head_dim), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    cu = torch.arange(0, nq + 1, C, dtype=torch.int32, device=dev)
+    prefix_d = torch.from_numpy(prefix).to(dev)
+    off_d = torch.from_numpy(page_off).to(dev)
+    out = torch.empty((nq, w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    lse = torch.empty((nq, w.q_heads), dtype=torch.float32, device=dev)
+    sm = I.sm_scale(w)
+
+    def step():
+        K.kvq_store(cache, k_new, v_new, slots)
+        K.kvq_dequantize_prev_kv(cache, pages_d, s_k, s_v, dq_k=dk, dq_v=dv)
+        K.kvq_extend_attention(q, k_new, v_new, cu, prefix_d, dk, dv, off_d, s_k, s_v, C, sm, out=out, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    K.kvq_profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ext_ms = K.kvq_profile_read("extend")[0] / args.steps
+    dq_ms = K.kvq_profile_read("dequant_prev")[0] / args.steps
+    sto_ms = K.kvq_profile_read("store")[0] / args.steps
+    K.kvq_profile_enable(False)
+    fl = extend_flops(prefix, [C] * w.batch, w.q_heads, w.head_dim)
+    value = fl / (ms * 1e-3) / 1e12
+    ach = fl / (ext_ms * 1e-3) / 1e12
+    log(f"step {ms:.2f} ms: store {sto_ms:.3f} ms, dequantize_prev_kv {dq_ms:.3f} ms, extend {ext_ms:.2f} ms")
+    res = {
+        "metric": "extend attention TFLOP/s over an FP4 prefix (store chunk + dequantize_prev_kv + extend)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{w.name}: batch {w.batch}, {C}-token chunk per sequence over a "
+                               f"{int(prefix[0])}-token {w.dtype} prefix, {w.q_heads} q / {w.kv_heads} kv heads, "
+                               f"head_dim {w.head_dim}, page {P}; prefix read through E4M3 workspaces "
+                               f"(scales 0.05), chunk K/V BF16, causal within the chunk",
+                   "algorithmic_flops_per_step": fl},
+        "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / PEAK_F16_TFLOPS, 4), "traffic": None,
+                     "kernel": "extend_attn_kernel (bf16 / fp16 MFMA)", "kernel_ms": round(ext_ms, 4)},
+        "kernel_ms": {"extend": round(ext_ms, 4), "dequant_prev": round(dq_ms, 4), "store": round(sto_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = extend_cpu_baseline(w)
+    print(json.dumps(res), flush=True)
+
+
 def copy_reference(nbytes=1 << 30, reps=10):
     """A plain device copy of known size (src -> dst), the reference the HBM
     traffic counters are scaled by."""
@@ -349,6 +465,8 @@ def main():
     ap.add_argument("--copy-ref", action="store_true", help="only run the 1 GiB reference copy (for counters)")
     ap.add_argument("--dequant-prev", action="store_true",
                     help="FP4 workloads: time kvq_dequantize_prev_kv over every page instead of the decode step")
+    ap.add_argument("--extend", action="store_true",
+                    help="FP4 GQA workload with a chunk: store + dequantize_prev_kv + extend attention per step")
     ap.add_argument("--kivi", action="store_true",
                     help="FP8 workloads: K scales per channel, V scales per token (KIVI-style)")
     ap.add_argument("--per-head-scales", action="store_true",
@@ -377,6 +495,10 @@ def main():
     if args.dequant_prev:
         assert w.dtype in ("mx16", "nvfp4"), "dequantize_prev_kv reads FP4 caches"
         bench_dequant_prev(w, args, dev)
+        return
+    if args.extend:
+        assert w.dtype == "mx16" and w.kind == "gqa" and w.new_tokens > 1, "extend runs on the FP4 chunk workload"
+        bench_extend(w, args, dev)
         return
     t0 = time.time()
     st = setup(w, dev, args.rotate)

@@ -274,13 +274,46 @@ int kvq_dequantize_prev_kv(const kvq_cache* cache, const int32_t* pages, int32_t
                            const float* g_scale, const float* k_scale_out, const float* v_scale_out,
                            void* dq_k, void* dq_v, void* stream);
 
+/* Extend (chunked prefill) attention over a quantized prefix ([P4] "code
+ * analysis": dequantize_prev_kv turns the FP4 prefix into E4M3 workspaces for
+ * an FP8 prefill kernel; this is that kernel). For sequence b with chunk rows
+ * cu_q[b] .. cu_q[b+1]-1 (C_b tokens) and prefix length L0 = prefix_len[b],
+ * chunk token i and query head h (kv head = h / G) attend to
+ *   prefix tokens t < L0: K^ = E4M3(dq_k row) * s_k, V^ = E4M3(dq_v row) * s_v,
+ *     token t at row t % page_size of workspace page page_off[b] + t / page_size
+ *     (the [n_pages][num_kv_heads][page_size][head_dim] layout that
+ *     kvq_dequantize_prev_kv writes), and
+ *   chunk tokens 0..i (causal): the BF16 rows k_new / v_new,
+ * with scores sm_scale * q . K^ and a softmax over all of them:
+ *   out[row][h][:] = sum softmax * V^,  lse[row][h] = log sum exp(score).
+ *   q:            [dev] BF16 [total_q][num_q_heads][head_dim]
+ *   k_new, v_new: [dev] BF16 [total_q][num_kv_heads][head_dim]
+ *   cu_q:         [dev] int32 [batch + 1] chunk offsets (clamped to [0, total_q])
+ *   prefix_len, page_off: [dev] int32 [batch]; prefix tokens whose page falls
+ *                 outside [0, n_pages) are dropped
+ *   dq_k, dq_v:   [dev] E4M3 workspaces of n_pages pages (may be NULL when n_pages is 0)
+ *   s_k, s_v:     [dev] fp32 workspace scales, NULL = 1.0
+ *   max_chunk:    [host] upper bound of every chunk length (sizes the launch)
+ *   out:          [dev] fp32 [total_q][num_q_heads][head_dim]; lse [dev] fp32
+ *                 [total_q][num_q_heads] (natural log) or NULL
+ * Supported: head_dim 128, G = num_q_heads / num_kv_heads in {1, 2, 4, 8, 16}
+ * (KVQ_ERR_UNSUPPORTED otherwise). q, k_new, v_new, dq_k, dq_v and out must be
+ * 16-byte aligned. Allocates nothing; batch, total_q or max_chunk 0 is a no-op.
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_HIP. */
+int kvq_extend_attention(const void* q, const void* k_new, const void* v_new, const int32_t* cu_q,
+                         int32_t total_q, const int32_t* prefix_len, const void* dq_k,
+                         const void* dq_v, const int32_t* page_off, int32_t n_pages,
+                         const float* s_k, const float* s_v, int32_t batch, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                         int32_t max_chunk, float sm_scale, float* out, float* lse, void* stream);
+
 /* Instrumentation (off by default). While enabled, every kernel launched by
- * kvq_store / kvq_decode(_append) / kvq_compute_scale / kvq_dequantize_prev_kv is
- * bracketed by two HIP events
+ * kvq_store / kvq_decode(_append) / kvq_compute_scale / kvq_dequantize_prev_kv /
+ * kvq_extend_attention is bracketed by two HIP events
  * recorded on the call's stream (nothing else changes; do not enable while
  * capturing a HIP graph). Enabling or disabling clears the records.
  * kvq_profile_read synchronizes the recorded events and returns, for one
- * kernel family ("store", "decode", "merge", "amax", "dequant_prev"), the summed device
+ * kernel family ("store", "decode", "merge", "amax", "dequant_prev", "extend"), the summed device
  * time in milliseconds and the number of launches, then forgets them.
  * Errors: KVQ_ERR_ARG (unknown name, null outputs), KVQ_ERR_HIP. */
 int kvq_profile_enable(int on);

@@ -106,6 +106,8 @@ def extend_attention(q, k_new, v_new, cu_q, prefix_len, dq_k, dq_v, page_off, s_
     lse = np.full((Nq, Hq), np.nan)
     want = None if rows is None else set(int(r) for r in rows)
     for b in range(len(prefix_len)):
+        if want is not None and not any(int(cu_q[b]) <= r < int(cu_q[b + 1]) for r in want):
+            continue
         L0 = int(prefix_len[b])
         t = np.arange(L0)
         pg = int(page_off[b]) + t // P

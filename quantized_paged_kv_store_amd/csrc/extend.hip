@@ -1,0 +1,326 @@
+// Extend (chunked prefill) attention over a quantized prefix, gfx950.
+//
+// The PR #21954 analysis page ("code analysis") has dequantize_prev_kv turn
+// the FP4 prefix of a sequence into FP8 E4M3 workspaces because only FP8
+// prefill kernels exist; this is that prefill kernel. The C new tokens of a
+// sequence attend to its L0 prefix tokens through the E4M3 rows (value =
+// code * s_k or s_v, the workspace's per-tensor scales) and to their own BF16
+// K/V causally; the G query heads of a KV head share its K/V (GQA).
+//
+// Work split: one workgroup (4 waves) per (sequence, KV head, tile of
+// 128 / G chunk tokens): 128 query rows (token, head), 32 per wave. Block ids
+// are remapped so that all tiles of one (sequence, KV head) run on one XCD
+// (the 8 XCDs take block ids round robin): they stream the same prefix, which
+// then stays in that XCD's L2.
+//
+// Per 64-key block, staged in LDS (K and V row-major, K as bf16, V as fp16
+// codes for the prefix and bf16 values for the chunk; two buffers, the next
+// block converted and stored while the current one is used):
+//   S^T[key][row]  = K[key][:] . Q^T[:][row]   v_mfma_f32_32x32x16_bf16
+//                    (E4M3 codes and BF16 values are exact in bf16; s_k and
+//                    sm_scale multiply the scores)
+//   online softmax per query row: the row is one lane column, so the block
+//   maximum takes one cross-lane step (the two halves of the wave)
+//   O^T[d][row]   += V^T[d][key] . P^T[key][row]
+//                    prefix: v_mfma_f32_32x32x16_f16 (E4M3 exact in fp16, P
+//                    carries 2^15); s_v multiplies O once after the prefix
+//                    chunk: bf16 MFMAs with P split hi + lo (BF16 values are
+//                    not all representable in fp16)
+// P^T goes from the score registers straight into the B operand: within each
+// 16-key step, lane half h holds keys {4h..4h+3, 8+4h..8+4h+3}; the V^T
+// operand reads the same keys with transposing LDS reads (ds_read_b64_tr_b16).
+// The softmax reference maximum moves only when a score exceeds it by more
+// than 2^8 (P = 2^(s - ref + 7) <= 2^15 stays in fp16 range), so the
+// accumulator rescale is rare.
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+constexpr int XD = 128;             // head dim
+constexpr int XKB = 64;             // keys per block
+constexpr int XROWS = 128;          // query rows per workgroup
+constexpr int XK_STRIDE = XD + 8;   // 16-bit elements per LDS K row: 272 B, rows 4 banks apart
+constexpr int XV_STRIDE = XD + 32;  // per LDS V row: 320 B, rows 16 banks apart (transposed reads)
+constexpr float kXNegInf = -__builtin_huge_valf();
+constexpr float kXPBias = 7.0f;     // P = 2^(s - ref + 7)
+constexpr float kXLazy = 8.0f;      // the reference moves when a score exceeds it by this
+constexpr float kXLog2e = 1.4426950408889634f;
+constexpr float kXLn2 = 0.6931471805599453f;
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+
+__device__ __forceinline__ void split_bf16(const float* p, bf16x8& hi, bf16x8& lo) {
+  float r[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = p[i] - (float)(__bf16)p[i];
+  const u32x4 h = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+  const u32x4 l = {pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]), pack_bf16x2(r[6], r[7])};
+  hi = __builtin_bit_cast(bf16x8, h);
+  lo = __builtin_bit_cast(bf16x8, l);
+}
+
+// transposed 4 x 16-bit LDS read: in each 16-lane group, lane i receives
+// element i%4 of the 8-byte reads of lanes i/4 + 4e (e = 0..3)
+__device__ __forceinline__ u32x2 lds_tr16(const uint16_t* p) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+__global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a) {
+  const int nwg = gridDim.x;  // a multiple of 8
+  const int work = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+  if (work >= a.n_work) return;
+  const int qt = work % a.q_tiles;
+  const int kvh = (work / a.q_tiles) % a.hkv;
+  const int b = work / (a.q_tiles * a.hkv);
+  const int G = a.group, TT = XROWS / G, P = a.page_size;
+
+  // device data is clamped, never trusted
+  const int q0 = min(max(a.cu_q[b], 0), a.total_q);
+  const int q1 = min(max(a.cu_q[b + 1], q0), a.total_q);
+  const int C = min(q1 - q0, a.max_chunk);
+  const int t0 = qt * TT;
+  if (t0 >= C) return;
+  const int po = a.page_off[b];
+  int L0 = max(a.prefix_len[b], 0);
+  L0 = (po < 0 || po >= a.n_pages) ? 0 : (int)min((int64_t)L0, (int64_t)(a.n_pages - po) * P);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = lane & 31, hh = lane >> 5;
+  const int row = 32 * wave + j;  // this lane's query row
+  const int tok = t0 + row / G;
+  const int head = kvh * G + row % G;
+  const bool rv = tok < C;
+
+  // Q^T operand: lane (row, half hh) holds d = 16 ks + 8 hh .. + 7 (zero for
+  // rows past the chunk: their scores are 0 and their outputs not written)
+  bf16x8 qf[XD / 16];
+  {
+    const uint16_t* qp = a.q + ((int64_t)(q0 + (rv ? tok : 0)) * a.hq + head) * XD + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < XD / 16; ++ks) {
+      uint4 w = rv ? *reinterpret_cast<const uint4*>(qp + 16 * ks) : make_uint4(0, 0, 0, 0);
+      qf[ks] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  const int nb0 = (L0 + XKB - 1) / XKB;
+  const int tl = min(t0 + TT, C) - 1;  // last chunk token of this tile
+  const int nb = nb0 + tl / XKB + 1;
+
+  __shared__ __attribute__((aligned(16))) uint16_t sk[2][XKB * XK_STRIDE];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[2][XKB * XV_STRIDE];
+
+  // global -> registers: a prefix block is 2 + 2 E4M3 chunks of 16 bytes
+  // (16 elements) per thread, a chunk block 4 + 4 BF16 chunks (8 elements);
+  // keys past the prefix or the chunk read zeros. Every register is written
+  // on both paths.
+  uint4 rk[4], rvv[4];
+  auto load_block = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool prefix = kb < nb0;
+      const int c = tid + 256 * i;
+      const int key = prefix ? (c >> 3) : (c >> 4);
+      const int t = prefix ? kb * XKB + key : (kb - nb0) * XKB + key;
+      const bool ok = prefix ? (i < 2 && t < L0) : (t < C);
+      const uint8_t* kp;
+      const uint8_t* vp;
+      if (prefix) {
+        const int64_t r = ((int64_t)(po + t / P) * a.hkv + kvh) * P + t % P;
+        kp = a.dq_k + r * XD + 16 * (c & 7);
+        vp = a.dq_v + r * XD + 16 * (c & 7);
+      } else {
+        const int64_t r = ((int64_t)(q0 + t) * a.hkv + kvh) * XD + 8 * (c & 15);
+        kp = reinterpret_cast<const uint8_t*>(a.k_new + r);
+        vp = reinterpret_cast<const uint8_t*>(a.v_new + r);
+      }
+      rk[i] = ok ? *reinterpret_cast<const uint4*>(kp) : make_uint4(0, 0, 0, 0);
+      rvv[i] = ok ? *reinterpret_cast<const uint4*>(vp) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  // registers -> LDS buffer: K rows as bf16; V rows as fp16 codes (prefix) or
+  // bf16 values (chunk)
+  auto store_block = [&](int kb, uint16_t* kd, uint16_t* vd) {
+    if (kb < nb0) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int c = tid + 256 * i, key = c >> 3, dc = c & 7;
+        const uint4 k = rk[i], v = rvv[i];
+        const uint4 k0 = {fp8x2_to_bf16x2<KVQ_FP8_E4M3, false>(k.x), fp8x2_to_bf16x2<KVQ_FP8_E4M3, true>(k.x),
+                          fp8x2_to_bf16x2<KVQ_FP8_E4M3, false>(k.y), fp8x2_to_bf16x2<KVQ_FP8_E4M3, true>(k.y)};
+        const uint4 k1 = {fp8x2_to_bf16x2<KVQ_FP8_E4M3, false>(k.z), fp8x2_to_bf16x2<KVQ_FP8_E4M3, true>(k.z),
+                          fp8x2_to_bf16x2<KVQ_FP8_E4M3, false>(k.w), fp8x2_to_bf16x2<KVQ_FP8_E4M3, true>(k.w)};
+        const uint4 v0 = {fp8x2_to_f16x2<KVQ_FP8_E4M3, false>(v.x), fp8x2_to_f16x2<KVQ_FP8_E4M3, true>(v.x),
+                          fp8x2_to_f16x2<KVQ_FP8_E4M3, false>(v.y), fp8x2_to_f16x2<KVQ_FP8_E4M3, true>(v.y)};
+        const uint4 v1 = {fp8x2_to_f16x2<KVQ_FP8_E4M3, false>(v.z), fp8x2_to_f16x2<KVQ_FP8_E4M3, true>(v.z),
+                          fp8x2_to_f16x2<KVQ_FP8_E4M3, false>(v.w), fp8x2_to_f16x2<KVQ_FP8_E4M3, true>(v.w)};
+        *reinterpret_cast<uint4*>(kd + key * XK_STRIDE + 16 * dc) = k0;
+        *reinterpret_cast<uint4*>(kd + key * XK_STRIDE + 16 * dc + 8) = k1;
+        *reinterpret_cast<uint4*>(vd + key * XV_STRIDE + 16 * dc) = v0;
+        *reinterpret_cast<uint4*>(vd + key * XV_STRIDE + 16 * dc + 8) = v1;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = tid + 256 * i, key = c >> 4, dc = c & 15;
+        *reinterpret_cast<uint4*>(kd + key * XK_STRIDE + 8 * dc) = rk[i];
+        *reinterpret_cast<uint4*>(vd + key * XV_STRIDE + 8 * dc) = rvv[i];
+      }
+    }
+  };
+
+  const float sm2 = a.sm_scale * kXLog2e;
+  const float skv = a.s_k ? a.s_k[0] : 1.0f;
+  const float svv = a.s_v ? a.s_v[0] : 1.0f;
+  f32x16 o[XD / 32];
+#pragma unroll
+  for (int dt = 0; dt < XD / 32; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) o[dt][v] = 0.f;
+  float m_ref = kXNegInf, l_run = 0.f;
+  // transposed-read lane address: lane 4e + c of each 16-lane group reads key
+  // row 4 hh + e, elements 16 ((lane >> 4) & 1) + 4 c (+ 32 dt)
+  const int v_lane = (4 * hh + ((lane & 15) >> 2)) * XV_STRIDE + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  load_block(0);
+  store_block(0, sk[0], sv[0]);
+  if (nb > 1) load_block(1);
+  __syncthreads();
+  for (int kb = 0; kb < nb; ++kb) {
+    const uint16_t* kd = sk[kb & 1];
+    const uint16_t* vd = sv[kb & 1];
+    const bool pre = kb < nb0;
+
+    // scores for the 64 keys: tile kt holds keys 32 kt + 8 (v/4) + 4 hh + v%4
+    float s[2][16];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x16 acc;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < XD / 16; ++ks) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kd + (32 * kt + j) * XK_STRIDE + 16 * ks + 8 * hh);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[kt][v] = acc[v];
+    }
+    const float scl = pre ? sm2 * skv : sm2;
+    // only blocks that reach past the prefix end, the chunk end or the
+    // diagonal of this tile need masking
+    const int kc0 = (kb - nb0) * XKB;
+    const bool edge = pre ? (kb * XKB + XKB > L0) : (kc0 + XKB - 1 > t0 || kc0 + XKB > C);
+    float mx = kXNegInf;
+    if (edge) {
+      const int lim = pre ? L0 - kb * XKB : tok - kc0 + 1;  // keys below lim are visible
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = 32 * kt + 8 * (v >> 2) + 4 * hh + (v & 3);
+          s[kt][v] = key < lim ? s[kt][v] * scl : kXNegInf;
+          mx = fmaxf(mx, s[kt][v]);
+        }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          s[kt][v] *= scl;
+          mx = fmaxf(mx, s[kt][v]);
+        }
+    }
+    mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+    // lazy reference: move (and rescale) only when a score exceeds it by 2^8
+    if (__builtin_amdgcn_ballot_w64(mx > m_ref + kXLazy) != 0ull) {
+      const float m_new = fmaxf(m_ref, mx);
+      const float alpha = (m_ref == kXNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < XD / 32; ++dt) o[dt] *= alpha;
+      m_ref = m_new;
+    }
+    const float mb = (m_ref == kXNegInf) ? 0.f : m_ref - kXPBias;
+    float psum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        s[kt][v] = __builtin_amdgcn_exp2f(s[kt][v] - mb);
+        psum += s[kt][v];
+      }
+    l_run += psum;
+
+    // O^T += V^T P^T, 16 keys per step
+#pragma unroll
+    for (int stp = 0; stp < 4; ++stp) {
+      const int kt = stp >> 1, sub = stp & 1;
+      const float* pv = &s[kt][8 * sub];
+      const uint16_t* vb = vd + v_lane + (32 * kt + 16 * sub) * XV_STRIDE;
+      if (pre) {
+        const u32x4 pp = {pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]), pack_f16x2(pv[4], pv[5]),
+                          pack_f16x2(pv[6], pv[7])};
+        const f16x8 pb = __builtin_bit_cast(f16x8, pp);
+#pragma unroll
+        for (int dt = 0; dt < XD / 32; ++dt) {
+          const u32x2 lo = lds_tr16(vb + 32 * dt), hi = lds_tr16(vb + 32 * dt + 8 * XV_STRIDE);
+          const f16x8 av = __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb, o[dt], 0, 0, 0);
+        }
+      } else {
+        bf16x8 ph, pl;
+        split_bf16(pv, ph, pl);
+#pragma unroll
+        for (int dt = 0; dt < XD / 32; ++dt) {
+          const u32x2 lo = lds_tr16(vb + 32 * dt), hi = lds_tr16(vb + 32 * dt + 8 * XV_STRIDE);
+          const bf16x8 ab = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, ph, o[dt], 0, 0, 0);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, pl, o[dt], 0, 0, 0);
+        }
+      }
+    }
+    if (pre && kb == nb0 - 1) {  // the prefix values carry the workspace V scale
+#pragma unroll
+      for (int dt = 0; dt < XD / 32; ++dt) o[dt] *= svv;
+    }
+    // the next block into the other buffer (last read by the previous
+    // block's math, which every wave finished before the last barrier)
+    if (kb + 1 < nb) {
+      store_block(kb + 1, sk[(kb + 1) & 1], sv[(kb + 1) & 1]);
+      if (kb + 2 < nb) load_block(kb + 2);
+    }
+    __syncthreads();
+  }
+
+  l_run += shfl_xor_f32(l_run, 32);
+  if (rv) {
+    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
+    float* op = a.out + ((int64_t)(q0 + tok) * a.hq + head) * XD;
+#pragma unroll
+    for (int dt = 0; dt < XD / 32; ++dt)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const float4 val = make_float4(o[dt][4 * a4] * inv, o[dt][4 * a4 + 1] * inv, o[dt][4 * a4 + 2] * inv,
+                                       o[dt][4 * a4 + 3] * inv);
+        *reinterpret_cast<float4*>(op + 32 * dt + 8 * a4 + 4 * hh) = val;
+      }
+    if (a.lse && hh == 0)
+      a.lse[(int64_t)(q0 + tok) * a.hq + head] =
+          l_run > 0.f ? (m_ref + __log2f(l_run) - kXPBias) * kXLn2 : kXNegInf;
+  }
+}
+
+}  // namespace
+}  // namespace kvq
+
+hipError_t kvq_launch_extend(const ExtendArgs& a, hipStream_t s) {
+  const int64_t nwg = (a.n_work + 7) / 8 * 8;
+  kvq::extend_attn_kernel<<<(unsigned)nwg, 256, 0, s>>>(a);
+  return hipGetLastError();
+}

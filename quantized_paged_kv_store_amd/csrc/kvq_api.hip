@@ -160,11 +160,11 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 // ------------------------------------------------------------ instrumentation
 struct ProfRecord {
-  int family;  // 0 store, 1 decode, 2 merge, 3 amax, 4 dequant_prev
+  int family;  // 0 store, 1 decode, 2 merge, 3 amax, 4 dequant_prev, 5 extend
   hipEvent_t start, stop;
 };
-const char* const kFamilies[] = {"store", "decode", "merge", "amax", "dequant_prev"};
-constexpr int kNumFamilies = 5;
+const char* const kFamilies[] = {"store", "decode", "merge", "amax", "dequant_prev", "extend"};
+constexpr int kNumFamilies = 6;
 std::mutex g_prof_mu;
 bool g_prof_on = false;
 std::vector<ProfRecord> g_prof;
@@ -548,6 +548,54 @@ int kvq_dequantize_prev_kv(const kvq_cache* c, const int32_t* pages, int32_t n_p
   const hipError_t e = kvq_launch_dequant_prev(c, pages, n_pages, g_scale, k_scale_out, v_scale_out,
                                                static_cast<uint8_t*>(dq_k), static_cast<uint8_t*>(dq_v),
                                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+int kvq_extend_attention(const void* q, const void* k_new, const void* v_new, const int32_t* cu_q, int32_t total_q,
+                         const int32_t* prefix_len, const void* dq_k, const void* dq_v, const int32_t* page_off,
+                         int32_t n_pages, const float* s_k, const float* s_v, int32_t batch, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t max_chunk,
+                         float sm_scale, float* out, float* lse, void* stream) {
+  if (batch < 0 || total_q < 0 || n_pages < 0 || max_chunk < 0 || page_size < 1) return KVQ_ERR_ARG;
+  if (num_kv_heads < 1 || num_q_heads < 1 || num_q_heads % num_kv_heads) return KVQ_ERR_ARG;
+  if (head_dim != 128) return KVQ_ERR_UNSUPPORTED;
+  const int G = num_q_heads / num_kv_heads;
+  if (G > 16 || (G & (G - 1))) return KVQ_ERR_UNSUPPORTED;  // 128 query rows per workgroup = 128/G tokens
+  if (batch == 0 || total_q == 0 || max_chunk == 0) return KVQ_OK;
+  if (!q || !k_new || !v_new || !cu_q || !prefix_len || !page_off || !out) return KVQ_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out)) return KVQ_ERR_ARG;
+  if (n_pages > 0 && (!dq_k || !dq_v || !aligned16(dq_k) || !aligned16(dq_v))) return KVQ_ERR_ARG;
+  const int TT = 128 / G;
+  const int64_t q_tiles = ((int64_t)max_chunk + TT - 1) / TT;
+  const int64_t n_work = (int64_t)batch * num_kv_heads * q_tiles;
+  if (n_work > INT32_MAX - 8) return KVQ_ERR_UNSUPPORTED;
+  ExtendArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.cu_q = cu_q;
+  a.prefix_len = prefix_len;
+  a.page_off = page_off;
+  a.dq_k = static_cast<const uint8_t*>(dq_k);
+  a.dq_v = static_cast<const uint8_t*>(dq_v);
+  a.s_k = s_k;
+  a.s_v = s_v;
+  a.out = out;
+  a.lse = lse;
+  a.total_q = total_q;
+  a.n_pages = n_pages;
+  a.batch = batch;
+  a.hq = num_q_heads;
+  a.hkv = num_kv_heads;
+  a.group = G;
+  a.page_size = page_size;
+  a.max_chunk = max_chunk;
+  a.q_tiles = (int)q_tiles;
+  a.n_work = (int)n_work;
+  a.sm_scale = sm_scale;
+  Timed timer(5, static_cast<hipStream_t>(stream));
+  const hipError_t e = kvq_launch_extend(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 

@@ -156,6 +156,26 @@ struct CombineArgs {
   int batch, hq, dv, num_splits, tokens_per_split, max_len;
 };
 
+// Extend attention over an E4M3 prefix workspace (kvq_extend_attention).
+struct ExtendArgs {
+  const uint16_t* q;       // BF16 [total_q][hq][128]
+  const uint16_t* k_new;   // BF16 [total_q][hkv][128]
+  const uint16_t* v_new;
+  const int32_t* cu_q;     // [batch + 1]
+  const int32_t* prefix_len;
+  const int32_t* page_off;
+  const uint8_t* dq_k;     // E4M3 [n_pages][hkv][page_size][128]
+  const uint8_t* dq_v;
+  const float* s_k;        // workspace scales (null = 1.0)
+  const float* s_v;
+  float* out;              // fp32 [total_q][hq][128]
+  float* lse;              // fp32 [total_q][hq] or null (natural log)
+  int total_q, n_pages, batch, hq, hkv, group, page_size, max_chunk;
+  int q_tiles, n_work;     // tiles of 128/group chunk tokens per sequence; batch * hkv * q_tiles
+  float sm_scale;
+};
+
+hipError_t kvq_launch_extend(const ExtendArgs& a, hipStream_t s);
 hipError_t kvq_launch_amax(const uint16_t* x0, int64_t n0, const uint16_t* x1, int64_t n1,
                            unsigned* scratch, float fmt_div, float* scale_out, hipStream_t s);
 hipError_t kvq_launch_store(const kvq_cache* c, const uint16_t* k, const uint16_t* v,

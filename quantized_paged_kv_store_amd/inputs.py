@@ -208,3 +208,34 @@ def random_cache_bytes(shapes: dict, dtype: str, seed: int, mx_codes=(0, 191)) -
             mag = rng.integers(0, 0x7F, shape)
             out[name] = (mag | (rng.integers(0, 2, shape) << 7)).astype(np.uint8)
     return out
+
+
+def extend_inputs(seed: int, prefix_lens, chunk_lens, hkv: int, group: int, head_dim: int, page_size: int,
+                  max_code: int = 0x58) -> dict:
+    """Seeded inputs of one extend-attention call: BF16 bits of Q [Nq, Hq, D]
+    and of the chunk K/V [Nq, Hkv, D] (N(0,1)), chunk offsets cu_q [B+1],
+    prefix_len [B], and E4M3 prefix workspaces dq_k / dq_v [n_pages, Hkv, P, D]
+    of random codes with magnitude code <= max_code (0x58: |value| <= 30, no
+    NaN) and a random sign; sequence b's prefix pages are consecutive from
+    page_off[b], the sequences' page ranges in a shuffled order."""
+    rng = np.random.default_rng([seed, 77])
+    prefix_lens = np.asarray(prefix_lens, np.int32)
+    chunk_lens = np.asarray(chunk_lens, np.int32)
+    B = len(prefix_lens)
+    npg = (prefix_lens + page_size - 1) // page_size
+    order = rng.permutation(B)
+    page_off = np.zeros(B, np.int32)
+    off = 0
+    for b in order:
+        page_off[b] = off
+        off += int(npg[b])
+    n_pages = max(off, 1)
+    shape = (n_pages, hkv, page_size, head_dim)
+    codes = lambda: (rng.integers(0, max_code + 1, shape) | (rng.integers(0, 2, shape) << 7)).astype(np.uint8)
+    dq_k, dq_v = codes(), codes()
+    cu = np.concatenate([[0], np.cumsum(chunk_lens)]).astype(np.int32)
+    nq = int(cu[-1])
+    q = bf16_bits(rng.standard_normal((nq, hkv * group, head_dim), dtype=np.float32))
+    k = bf16_bits(rng.standard_normal((nq, hkv, head_dim), dtype=np.float32))
+    v = bf16_bits(rng.standard_normal((nq, hkv, head_dim), dtype=np.float32))
+    return dict(q=q, k_new=k, v_new=v, cu_q=cu, prefix_len=prefix_lens, page_off=page_off, dq_k=dq_k, dq_v=dq_v)

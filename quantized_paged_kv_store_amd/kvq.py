@@ -76,6 +76,10 @@ def _lib():
         L.kvq_dequantize_prev_kv.argtypes = [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                              c_void_p, c_void_p]
         L.kvq_dequantize_prev_kv.restype = c_int32
+        L.kvq_extend_attention.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p, c_void_p,
+                                           c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_int32, c_int32,
+                                           c_int32, c_int32, c_int32, c_int32, c_float, c_void_p, c_void_p, c_void_p]
+        L.kvq_extend_attention.restype = c_int32
         L.kvq_profile_enable.argtypes = [c_int32]
         L.kvq_profile_enable.restype = c_int32
         L.kvq_profile_read.argtypes = [c_char_p, POINTER(c_double), POINTER(c_int64)]
@@ -286,6 +290,33 @@ def kvq_dequantize_prev_kv(cache: Cache, pages: torch.Tensor, k_scale_out=None, 
     return dq_k, dq_v
 
 
+def kvq_extend_attention(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, cu_q: torch.Tensor,
+                         prefix_len: torch.Tensor, dq_k: torch.Tensor | None, dq_v: torch.Tensor | None,
+                         page_off: torch.Tensor, s_k, s_v, max_chunk: int, sm_scale: float, out=None, lse=None):
+    """Chunk rows attend to their E4M3 prefix workspace rows and causally to
+    the chunk's BF16 K/V. Returns (out fp32 [Nq, Hq, D], lse fp32 [Nq, Hq])."""
+    dev = q.device
+    nq, hq, d = q.shape
+    hkv = k_new.shape[1]
+    for t in (q, k_new, v_new):
+        assert t.dtype == torch.bfloat16 and t.is_contiguous() and t.device == dev
+    for t in (cu_q, prefix_len, page_off):
+        assert t.dtype == torch.int32 and t.is_contiguous() and t.device == dev
+    n_pages, page_size = (0, 16) if dq_k is None else (dq_k.shape[0], dq_k.shape[2])
+    if dq_k is not None:
+        assert dq_k.dtype == torch.uint8 and dq_k.shape == dq_v.shape and dq_k.dim() == 4 and dq_k.shape[1] == hkv
+    if out is None:
+        out = torch.empty((nq, hq, d), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((nq, hq), dtype=torch.float32, device=dev)
+    skd, svd = _dev_f32(s_k, dev), _dev_f32(s_v, dev)
+    _check(_lib().kvq_extend_attention(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(cu_q), nq, _ptr(prefix_len),
+                                       _ptr(dq_k), _ptr(dq_v), _ptr(page_off), n_pages, _ptr(skd), _ptr(svd),
+                                       prefix_len.numel(), hq, hkv, d, page_size, int(max_chunk), float(sm_scale),
+                                       _ptr(out), _ptr(lse), _stream(dev)), "kvq_extend_attention")
+    return out, lse
+
+
 def kvq_profile_enable(on: bool = True) -> None:
     """Bracket every library kernel launch with HIP events (instrumentation)."""
     _check(_lib().kvq_profile_enable(1 if on else 0), "kvq_profile_enable")
@@ -293,7 +324,7 @@ def kvq_profile_enable(on: bool = True) -> None:
 
 def kvq_profile_read(kernel: str) -> tuple[float, int]:
     """(summed device ms, launches) of one kernel family since the last read:
-    "store", "decode", "merge", "amax" or "dequant_prev"."""
+    "store", "decode", "merge", "amax", "dequant_prev" or "extend"."""
     ms, n = c_double(), c_int64()
     _check(_lib().kvq_profile_read(kernel.encode(), byref(ms), byref(n)), "kvq_profile_read")
     return ms.value, n.value

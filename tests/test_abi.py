@@ -281,3 +281,22 @@ def test_kivi_descriptor_layout_and_accounting():
     assert dec(None) == ARG and dec(c_void_p(FAKE_DEV + 4)) == ARG
     assert lib.kvq_compute_scale(h, P, 4 * 128 + 8, None, 0, P, None) == ARG     # whole rows only
     lib.kvq_free_handle(h)
+
+
+def test_extend_attention_argument_errors():
+    lib = _lib()
+    P = c_void_p(FAKE_DEV)
+    f = lib.kvq_extend_attention
+
+    def call(q=P, total_q=64, batch=2, hq=32, hkv=2, d=128, page=16, max_chunk=32, npg=10, dq=P, out=P):
+        return f(q, P, P, P, total_q, P, dq, dq, P, npg, None, None, batch, hq, hkv, d, page, max_chunk, 0.1,
+                 out, None, None)
+    assert call(batch=0) == OK and call(total_q=0) == OK and call(max_chunk=0) == OK      # no-ops
+    assert call(d=64) == UNSUP                                   # head_dim 128 only
+    assert call(hq=48, hkv=2) == UNSUP                           # G = 24
+    assert call(hq=6, hkv=2) == UNSUP                            # G = 3: 128 rows / G not whole tokens
+    assert call(hq=33, hkv=2) == ARG                             # Hq % Hkv
+    assert call(q=None) == ARG and call(out=None) == ARG
+    assert call(q=c_void_p(FAKE_DEV + 2)) == ARG                 # 16-byte alignment
+    assert call(dq=None) == ARG                                  # pages but no workspace
+    assert call(batch=-1) == ARG and call(page=0) == ARG and call(max_chunk=-1) == ARG
