@@ -32,6 +32,8 @@
 // The softmax reference maximum moves only when a score exceeds it by more
 // than 2^8 (P = 2^(s - ref + 7) <= 2^15 stays in fp16 range), so the
 // accumulator rescale is rare.
+#include <type_traits>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -187,44 +189,55 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
   // row 4 hh + e, elements 16 ((lane >> 4) & 1) + 4 c (+ 32 dt)
   const int v_lane = (4 * hh + ((lane & 15) >> 2)) * XV_STRIDE + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  load_block(0);
-  store_block(0, sk[0], sv[0]);
-  if (nb > 1) load_block(1);
-  __syncthreads();
-  for (int kb = 0; kb < nb; ++kb) {
+  // One 64-key block. PRE: prefix (fp16 PV on E4M3 codes) or chunk (bf16 hi +
+  // lo PV); MASK: the block reaches past the prefix end, the chunk end or the
+  // tile's diagonal. The four variants are separate code, so the accumulators
+  // never cross a branch.
+  auto block = [&](auto pre_tag, auto mask_tag, int kb) {
+    constexpr bool PRE = decltype(pre_tag)::value;
+    constexpr bool MASK = decltype(mask_tag)::value;
     const uint16_t* kd = sk[kb & 1];
     const uint16_t* vd = sv[kb & 1];
-    const bool pre = kb < nb0;
-
-    // scores for the 64 keys: tile kt holds keys 32 kt + 8 (v/4) + 4 hh + v%4
-    float s[2][16];
+    // every LDS operand of the block is read up front (K for the scores, V^T
+    // for PV, which does not depend on the scores)
+    bf16x8 ka[2][XD / 16];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      f32x16 acc;
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+      for (int ks = 0; ks < XD / 16; ++ks)
+        ka[kt][ks] = *reinterpret_cast<const bf16x8*>(kd + (32 * kt + j) * XK_STRIDE + 16 * ks + 8 * hh);
+    u32x4 va[4][XD / 32];
 #pragma unroll
-      for (int ks = 0; ks < XD / 16; ++ks) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kd + (32 * kt + j) * XK_STRIDE + 16 * ks + 8 * hh);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], acc, 0, 0, 0);
+    for (int stp = 0; stp < 4; ++stp) {
+      const uint16_t* vb = vd + v_lane + (32 * (stp >> 1) + 16 * (stp & 1)) * XV_STRIDE;
+#pragma unroll
+      for (int dt = 0; dt < XD / 32; ++dt) {
+        const u32x2 lo = lds_tr16(vb + 32 * dt), hi = lds_tr16(vb + 32 * dt + 8 * XV_STRIDE);
+        va[stp][dt] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[kt][v] = acc[v];
     }
-    const float scl = pre ? sm2 * skv : sm2;
-    // only blocks that reach past the prefix end, the chunk end or the
-    // diagonal of this tile need masking
-    const int kc0 = (kb - nb0) * XKB;
-    const bool edge = pre ? (kb * XKB + XKB > L0) : (kc0 + XKB - 1 > t0 || kc0 + XKB > C);
+    // scores for the 64 keys: tile kt holds keys 32 kt + 8 (v/4) + 4 hh + v%4
+    f32x16 acc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[kt][v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < XD / 16; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+        acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kt][ks], qf[ks], acc[kt], 0, 0, 0);
+    const float scl = PRE ? sm2 * skv : sm2;  // > 0: the maximum commutes with it
+    float s[2][16];
     float mx = kXNegInf;
-    if (edge) {
-      const int lim = pre ? L0 - kb * XKB : tok - kc0 + 1;  // keys below lim are visible
+    if constexpr (MASK) {
+      const int lim = PRE ? L0 - kb * XKB : tok - (kb - nb0) * XKB + 1;  // keys below lim are visible
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = 32 * kt + 8 * (v >> 2) + 4 * hh + (v & 3);
-          s[kt][v] = key < lim ? s[kt][v] * scl : kXNegInf;
+          s[kt][v] = key < lim ? acc[kt][v] : kXNegInf;
           mx = fmaxf(mx, s[kt][v]);
         }
     } else {
@@ -232,11 +245,11 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          s[kt][v] *= scl;
+          s[kt][v] = acc[kt][v];
           mx = fmaxf(mx, s[kt][v]);
         }
     }
-    mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+    mx = fmaxf(mx, shfl_xor_f32(mx, 32)) * scl;
     // lazy reference: move (and rescale) only when a score exceeds it by 2^8
     if (__builtin_amdgcn_ballot_w64(mx > m_ref + kXLazy) != 0ull) {
       const float m_new = fmaxf(m_ref, mx);
@@ -252,42 +265,31 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        s[kt][v] = __builtin_amdgcn_exp2f(s[kt][v] - mb);
+        s[kt][v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][v], scl, -mb));
         psum += s[kt][v];
       }
     l_run += psum;
-
     // O^T += V^T P^T, 16 keys per step
 #pragma unroll
     for (int stp = 0; stp < 4; ++stp) {
-      const int kt = stp >> 1, sub = stp & 1;
-      const float* pv = &s[kt][8 * sub];
-      const uint16_t* vb = vd + v_lane + (32 * kt + 16 * sub) * XV_STRIDE;
-      if (pre) {
+      const float* pv = &s[stp >> 1][8 * (stp & 1)];
+      if constexpr (PRE) {
         const u32x4 pp = {pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]), pack_f16x2(pv[4], pv[5]),
                           pack_f16x2(pv[6], pv[7])};
         const f16x8 pb = __builtin_bit_cast(f16x8, pp);
 #pragma unroll
-        for (int dt = 0; dt < XD / 32; ++dt) {
-          const u32x2 lo = lds_tr16(vb + 32 * dt), hi = lds_tr16(vb + 32 * dt + 8 * XV_STRIDE);
-          const f16x8 av = __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb, o[dt], 0, 0, 0);
-        }
+        for (int dt = 0; dt < XD / 32; ++dt)
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va[stp][dt]), pb, o[dt], 0, 0, 0);
       } else {
         bf16x8 ph, pl;
         split_bf16(pv, ph, pl);
 #pragma unroll
         for (int dt = 0; dt < XD / 32; ++dt) {
-          const u32x2 lo = lds_tr16(vb + 32 * dt), hi = lds_tr16(vb + 32 * dt + 8 * XV_STRIDE);
-          const bf16x8 ab = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          const bf16x8 ab = __builtin_bit_cast(bf16x8, va[stp][dt]);
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, ph, o[dt], 0, 0, 0);
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, pl, o[dt], 0, 0, 0);
         }
       }
-    }
-    if (pre && kb == nb0 - 1) {  // the prefix values carry the workspace V scale
-#pragma unroll
-      for (int dt = 0; dt < XD / 32; ++dt) o[dt] *= svv;
     }
     // the next block into the other buffer (last read by the previous
     // block's math, which every wave finished before the last barrier)
@@ -296,7 +298,28 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
       if (kb + 2 < nb) load_block(kb + 2);
     }
     __syncthreads();
+  };
+
+  load_block(0);
+  store_block(0, sk[0], sv[0]);
+  if (nb > 1) load_block(1);
+  __syncthreads();
+  using T = std::true_type;
+  using F = std::false_type;
+  // prefix: whole blocks, then the last one if it is partial
+  const int nfull0 = L0 / XKB;
+  for (int kb = 0; kb < nfull0; ++kb) block(T{}, F{}, kb);
+  if (nb0 > nfull0) block(T{}, T{}, nb0 - 1);
+  if (nb0 > 0) {  // the prefix values carry the workspace V scale
+#pragma unroll
+    for (int dt = 0; dt < XD / 32; ++dt) o[dt] *= svv;
   }
+  // chunk: blocks whose keys all precede the tile's first token and lie in
+  // the chunk need no mask, the rest (the diagonal) do
+  int nfree = t0 / XKB;                      // keys [0, 64 * nfree) <= t0
+  nfree = min(nfree, C / XKB);
+  for (int kb = nb0; kb < nb0 + nfree; ++kb) block(F{}, F{}, kb);
+  for (int kb = nb0 + nfree; kb < nb; ++kb) block(F{}, T{}, kb);
 
   l_run += shfl_xor_f32(l_run, 32);
   if (rv) {
