@@ -326,7 +326,7 @@ def extend_flops(prefix, chunk, hq, d):
     return float(np.sum(c * np.asarray(prefix, np.float64) + c * (c + 1) / 2) * hq * 4 * d)
 
 
-def extend_cpu_baseline(w, rows=48):
+def extend_cpu_baseline(w, rows=256):
     """The oracle's extend_attention, untuned, on a few chunk rows of one
     sequence of the same shape (all query heads, full prefix)."""
     from oracle.attention import extend_attention
