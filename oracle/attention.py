@@ -74,6 +74,42 @@ def decode_attention(cache: OracleCache, q, page_table, seq_lens, sm_scale,
     return out, lse
 
 
+
+# --------------------------------------------------------------------------
+# FP8-domain decode (vLLM "Quantized KV Cache" page, overview: with an FP8 KV
+# cache, the Flash Attention 3 backend computes attention itself in FP8, the
+# query being quantized to FP8 like the keys and values; its "Supported
+# schemes" give the query its own scale, q_scale = [num_heads] per attention
+# head or [1] per tensor, defaulting like k/v_scale to 1.0). Reading adopted:
+# every query element is encoded to E4M3 as the cache's elements are,
+# codes = encode(fl32(q / q_scale)) with saturation, whatever the cache's FP8
+# format; the scores are then the exact products of those codes' values with
+# the cached codes' values, times q_scale * k_scale * sm_scale; the weights
+# and the value side are those of decode_attention. Equivalently: the
+# attention of decode_attention with q replaced by decode(codes) * q_scale.
+# --------------------------------------------------------------------------
+def quantize_query_fp8(q, q_scale=None):
+    """q [B, Hq, D] (BF16 values) -> (codes uint8 [B, Hq, D], per-head scales
+    float32 [Hq]); q_scale None (1.0), a scalar, or one value per query head."""
+    from .formats import E4M3
+    from .quantize import quantize_fp8
+    q = np.asarray(q, dtype=np.float64)
+    hq = q.shape[1]
+    s = np.full(hq, 1.0, np.float32) if q_scale is None else np.asarray(q_scale, np.float32)
+    s = np.broadcast_to(s.reshape(-1), (hq,)).astype(np.float32) if s.size == 1 else s.reshape(hq)
+    return quantize_fp8(q, s[None, :, None], E4M3), s
+
+
+def decode_attention_fp8q(cache: OracleCache, q, page_table, seq_lens, sm_scale, q_scale=None,
+                          k_scale=None, v_scale=None, batch_ids=None):
+    """decode_attention in the FP8 domain: Q rounded to E4M3 with q_scale
+    first (see quantize_query_fp8). Same arguments and results as
+    decode_attention, plus q_scale."""
+    from .formats import E4M3, decode
+    codes, s = quantize_query_fp8(q, q_scale)
+    q_hat = decode(codes.astype(np.int64), E4M3) * s[None, :, None].astype(np.float64)
+    return decode_attention(cache, q_hat, page_table, seq_lens, sm_scale, k_scale, v_scale, batch_ids)
+
 # --------------------------------------------------------------------------
 # Extend (chunked prefill) attention over a quantized prefix. The PR #21954
 # analysis page ("code analysis") has dequantize_prev_kv turn the FP4 prefix

@@ -47,6 +47,18 @@ def fp8_head_scales(x, fmt: Format) -> np.ndarray:
     return np.array([fp8_scale(a, fmt) for a in amax], dtype=np.float32)
 
 
+
+def fp8_query_scales(q, per_head: bool) -> np.ndarray:
+    """Calibrated E4M3 query scales for FP8-domain attention (vLLM page,
+    "Supported schemes": q_scale = [num_heads] or [1]; "Scale calibration":
+    estimated once from a batch of tokens): fp8_scale(amax / 448) of every
+    query head h = q[..., h, :] of a [tokens, Hq, D] tensor, or of the whole
+    tensor -> float32 [Hq] or [1]."""
+    if per_head:
+        return fp8_head_scales(q, E4M3)
+    x = np.asarray(q, dtype=np.float64)
+    return np.array([fp8_scale(np.abs(x).max() if x.size else 0.0, E4M3)], dtype=np.float32)
+
 # --------------------------------------------------------------------------
 # KIVI-style asymmetric scaling ("KV cache quantization mechanism and traps",
 # the section on why K and V distributions differ): Key outliers sit in fixed
