@@ -32,7 +32,7 @@ PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E, vendor figure
 PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, vendor figure
 
 
-def measured_traffic(w, op="decode"):
+def measured_traffic(w, op="decode", fp8q=False):
     """HBM bytes per launch of the decode (op "decode") or dequantize_prev_kv
     (op "dequant_prev") kernel from the committed rocprofv3 counter runs, or
     None when no measurement exists for this workload or the kernel's sources
@@ -40,7 +40,7 @@ def measured_traffic(w, op="decode"):
     import hashlib
     if op == "decode":
         kind = "gqa" if w.kind == "gqa" else "mla"
-        mode = {"amax_head": "_head", "kivi": "_kivi"}.get(w.scale_mode, "")
+        mode = {"amax_head": "_head", "kivi": "_kivi"}.get(w.scale_mode, "") + ("_fp8q" if fp8q else "")
         path = os.path.join(ROOT, "profiles", f"kvq_decode_{kind}_{w.name}_{w.dtype}{mode}_traffic.json")
     else:
         path = os.path.join(ROOT, "profiles", f"kvq_dequant_prev_{w.dtype}_{w.name}_traffic.json")
@@ -60,7 +60,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def setup(w, dev, rotate):
+def setup(w, dev, rotate, fp8q=False):
     import torch
 
     import quantized_paged_kv_store_amd as K
@@ -125,9 +125,11 @@ def setup(w, dev, rotate):
     new_rows = None
     if w.new_tokens == 1 and int((lens >= 1).sum()) == w.batch:
         new_rows = (new_k.view(w.batch, *row), None if new_v is None else new_v.view(w.batch, *row))
+    # FP8-domain attention: query scales calibrated once on the step's queries
+    qs = K.kvq_compute_q_scale(cache, q) if fp8q else None
     return dict(caches=caches, new=(new_k, new_v, new_s), new_rows=new_rows, q=q, table=table_d, lens=lens_d, lens_h=lens,
                 max_len=max_len, ks=ks, vs=vs, out=out, lse=lse, ws=ws, sm=I.sm_scale(w),
-                bpt=K.kvq_bytes_per_token(cache.desc))
+                bpt=K.kvq_bytes_per_token(cache.desc), fp8q=fp8q, qs=qs)
 
 
 def run_loop(st, steps, do_store, do_decode, offset=0, fused=False):
@@ -136,6 +138,11 @@ def run_loop(st, steps, do_store, do_decode, offset=0, fused=False):
     caches = st["caches"]
     for i in range(steps):
         c = caches[(i + offset) % len(caches)]
+        if fused and st["fp8q"]:
+            K.kvq_decode_append_fp8q(c, st["new_rows"][0], st["new_rows"][1], st["q"], st["table"], st["lens"],
+                                     st["max_len"], st["sm"], st["qs"], st["ks"], st["vs"], out=st["out"],
+                                     lse=st["lse"], workspace=st["ws"])
+            continue
         if fused:
             K.kvq_decode_append(c, st["new_rows"][0], st["new_rows"][1], st["q"], st["table"], st["lens"],
                                 st["max_len"], st["sm"], st["ks"], st["vs"], out=st["out"], lse=st["lse"],
@@ -143,7 +150,10 @@ def run_loop(st, steps, do_store, do_decode, offset=0, fused=False):
             continue
         if do_store:
             K.kvq_store(c, *st["new"], st["ks"], st["vs"])
-        if do_decode:
+        if do_decode and st["fp8q"]:
+            K.kvq_decode_fp8q(c, st["q"], st["table"], st["lens"], st["max_len"], st["sm"], st["qs"], st["ks"],
+                              st["vs"], out=st["out"], lse=st["lse"], workspace=st["ws"])
+        elif do_decode:
             K.kvq_decode(c, st["q"], st["table"], st["lens"], st["max_len"], st["sm"], st["ks"], st["vs"],
                          out=st["out"], lse=st["lse"], workspace=st["ws"])
 
@@ -177,9 +187,10 @@ def timed(st, steps, do_store, do_decode, graphs=None, fused=False):
     return start.elapsed_time(end) / steps     # ms per iteration
 
 
-def cpu_baseline(w, seconds_hint=20.0):
-    """The float64 oracle, untuned, on a bounded sample of the same workload."""
-    from oracle.attention import decode_attention
+def cpu_baseline(w, seconds_hint=20.0, fp8q=False):
+    """The float64 oracle, untuned, on a bounded sample of the same workload
+    (fp8q: the FP8-domain oracle, query scales calibrated on the step's queries)."""
+    from oracle.attention import decode_attention, decode_attention_fp8q
     from oracle.formats import E4M3, E5M2
     from oracle import quantize as Q
     from oracle.paged import CacheSpec, OracleCache
@@ -212,7 +223,11 @@ def cpu_baseline(w, seconds_hint=20.0):
     t_codec = time.perf_counter() - t0
     q = I.bf16_to_f32(I.queries(w)).astype(np.float64)
     t0 = time.perf_counter()
-    decode_attention(oc, q, table, lens, I.sm_scale(w), ks, vs, batch_ids=[b])
+    if fp8q:
+        qs = Q.fp8_query_scales(q, per_head=w.scale_mode == "amax_head")
+        decode_attention_fp8q(oc, q, table, lens, I.sm_scale(w), qs, ks, vs, batch_ids=[b])
+    else:
+        decode_attention(oc, q, table, lens, I.sm_scale(w), ks, vs, batch_ids=[b])
     t_dec = time.perf_counter() - t0
     rows = 2 * w.kv_heads if w.kind == "gqa" else 1
     bits = 8.0 if w.dtype in ("e4m3", "e5m2") else 4.5
@@ -265,7 +280,7 @@ def bench_dequant_prev(w, args, dev):
 
     import quantized_paged_kv_store_amd as K
     t0 = time.time()
-    st = setup(w, dev, args.rotate)
+    st = setup(w, dev, args.rotate, args.fp8q)
     log(f"setup {time.time() - t0:.1f} s")
     caches = st["caches"]
     d = caches[0].desc
@@ -471,6 +486,8 @@ def main():
                     help="FP8 workloads: K scales per channel, V scales per token (KIVI-style)")
     ap.add_argument("--per-head-scales", action="store_true",
                     help="FP8 workloads: one calibrated k/v scale per KV head instead of per tensor")
+    ap.add_argument("--fp8q", action="store_true",
+                    help="FP8 GQA workloads: FP8-domain attention (query rounded to E4M3, QK on FP8 MFMA)")
     args = ap.parse_args()
     if args.copy_ref:
         copy_reference()
@@ -491,6 +508,9 @@ def main():
     if args.kivi:
         assert w.dtype in ("e4m3", "e5m2") and w.kind == "gqa", "KIVI-style scales apply to FP8 GQA caches"
         w = w.with_(scale_mode="kivi")
+    if args.fp8q:
+        assert w.dtype in ("e4m3", "e5m2") and w.kind == "gqa" and w.scale_mode != "kivi", \
+            "FP8-domain attention applies to FP8 GQA caches with tensor or per-head scales"
     dev = torch.device("cuda:0")
     if args.dequant_prev:
         assert w.dtype in ("mx16", "nvfp4"), "dequantize_prev_kv reads FP4 caches"
@@ -544,16 +564,20 @@ def main():
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "vs_baseline": None, "dtype": "fp8" if args.fp8q else "bf16", "data": "synthetic",
         "config": {
             "workload": f"{w.name}: {w.q_heads} q heads / {w.kv_heads} kv heads, head_dim {w.head_dim}, "
                         f"batch {w.batch}, context {w.max_len}, page {w.page_size}, {w.dtype} KV "
                         f"({w.scale_mode} scales); step = "
                         + ("append 1 new token/sequence + decode in one kvq_decode_append launch (+ split merge)"
-                           if fused else f"store {w.new_tokens} new token(s)/sequence, then decode (+ split merge)"),
+                           if fused else f"store {w.new_tokens} new token(s)/sequence, then decode (+ split merge)")
+                        + ("; FP8-domain attention: query rounded to E4M3 with calibrated q_scale, QK^T on "
+                           "fp8 MFMA from the cached codes (kvq_decode_append_fp8q)" if args.fp8q else ""),
             "global_batch": w.batch, "seq_len": w.max_len, "kv_dtype": w.dtype,
             "compute": ("latent codes dequantized to fp16 (E2M1 x E4M3 exact) for QK and PV MFMAs, f32 accumulate"
                         if w.kind == "mla" else
+                        "E4M3 query x cached FP8 codes on fp8 MFMA (QK); V codes to f16 MFMA operands (PV); f32 "
+                        "accumulate" if args.fp8q else
                         "KV codes dequantized in registers to bf16 (QK) / f16 (PV) MFMA operands, f32 accumulate"),
             "cache_copies_rotated": args.rotate,
             "launch": "HIP graph replay per step" if use_graph else "eager launches",
@@ -564,7 +588,7 @@ def main():
         "context_tokens_per_s": round(float(st["lens_h"].sum()) / (ms_step * 1e-3), 1),
         "decode_tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),
     }
-    traffic = measured_traffic(w)
+    traffic = measured_traffic(w, fp8q=args.fp8q)
     if w.kind == "mla":
         flops = float(st["lens_h"].astype(np.int64).sum()) * w.q_heads * (w.head_dim + w.v_dim) * 2
         ach = flops / (kern_ms * 1e-3) / 1e12
@@ -577,12 +601,13 @@ def main():
         ach = kv_bytes / (kern_ms * 1e-3) / 1e9
         res["roofline"] = {"bound": "hbm", "achieved": round(ach, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                            "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                           "kernel": f"decode_gqa_kernel ({w.dtype}, head_dim {w.head_dim})",
+                           "kernel": f"decode_gqa_kernel ({w.dtype}, head_dim {w.head_dim}"
+                                     + (", FP8-domain QK)" if args.fp8q else ")"),
                            "kernel_ms": round(kern_ms, 5), "algorithmic_bytes_per_launch": kv_bytes}
     res["roofline"]["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)"
     res["kernel_ms"] = {"decode": round(kern_ms, 5), "merge": round(merge_ms, 5), "store": round(store_kern_ms, 5)}
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w)
+        res["cpu_baseline"] = cpu_baseline(w, fp8q=args.fp8q)
     print(json.dumps(res), flush=True)
 
 

@@ -252,6 +252,50 @@ int kvq_decode_append(const kvq_cache* cache, const void* k_new, const void* v_n
                       float sm_scale, const float* k_scale, const float* v_scale, float* out,
                       float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
+/* FP8-domain decode ([P3] overview: with an FP8 KV cache, the Flash
+ * Attention 3 backend runs attention itself in FP8, the query quantized to
+ * FP8 like K and V; [P3] "Supported schemes": q_scale = [num_q_heads] per
+ * attention head or [1] per tensor). kvq_decode with the query first rounded
+ * to E4M3 codes, code = RNE_sat(q / q_scale) (binary32 division, saturating
+ * at +-448, E4M3 whatever the cache's FP8 format), and the scores
+ *   sm_scale * q_scale * k_scale * (E4M3(code) . K codes)
+ * taken on FP8 matrix cores from the cached codes as they are; the softmax,
+ * the value side and every other argument are kvq_decode's.
+ *   q_scale: [dev] fp32, one value (cache scale_mode TENSOR) or
+ *            [num_q_heads] (scale_mode HEAD), 4-byte aligned; NULL = 1.0.
+ *            Queries beyond 448 * q_scale saturate.
+ * Caches: GQA, E4M3 or E5M2, scale_mode TENSOR or HEAD (KVQ_ERR_UNSUPPORTED
+ * otherwise: MX16 / NVFP4 codes are not FP8, KIVI folds a channel scale into
+ * the query). Errors as kvq_decode. */
+int kvq_decode_fp8q(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,
+                    const int32_t* page_table, int32_t page_table_stride, const int32_t* seq_lens,
+                    int32_t max_seq_len, float sm_scale, const float* q_scale, const float* k_scale,
+                    const float* v_scale, float* out, float* lse, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* kvq_decode_append in the FP8 domain: the append of kvq_decode_append, then
+ * kvq_decode_fp8q, in one launch. Arguments as those two; a NULL k_new (or
+ * v_new) is KVQ_ERR_ARG. */
+int kvq_decode_append_fp8q(const kvq_cache* cache, const void* k_new, const void* v_new,
+                           const void* q, int32_t batch, int32_t num_q_heads,
+                           const int32_t* page_table, int32_t page_table_stride,
+                           const int32_t* seq_lens, int32_t max_seq_len, float sm_scale,
+                           const float* q_scale, const float* k_scale, const float* v_scale,
+                           float* out, float* lse, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Query scales for kvq_decode_fp8q from a calibration batch of queries ([P3]
+ * "Scale calibration": estimated once, then kept fixed):
+ *   scale_mode TENSOR: q_scale_out[0] = amax(q) / 448
+ *   scale_mode HEAD:   q_scale_out[h] = amax over query head h / 448
+ * (binary32 division; an all-zero tensor or head gives 1.0).
+ *   q: [dev] BF16 [n_tokens][num_q_heads][head_dim], 16-byte aligned.
+ * Uses the cache's scratch buffer: concurrent calls on one cache race.
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED (caches kvq_decode_fp8q rejects),
+ * KVQ_ERR_HIP. n_tokens = 0 gives 1.0. */
+int kvq_compute_q_scale(const kvq_cache* cache, const void* q, int64_t n_tokens,
+                        int32_t num_q_heads, float* q_scale_out, void* stream);
+
 /* dequantize_prev_kv ([P4] "code analysis"): turn listed pages of an FP4
  * cache into FP8 E4M3 rows, the dq_k / dq_v workspaces an FP8 prefill kernel
  * reads when a new chunk attends to an already quantized prefix (the pages
@@ -308,8 +352,8 @@ int kvq_extend_attention(const void* q, const void* k_new, const void* v_new, co
                          int32_t max_chunk, float sm_scale, float* out, float* lse, void* stream);
 
 /* Instrumentation (off by default). While enabled, every kernel launched by
- * kvq_store / kvq_decode(_append) / kvq_compute_scale / kvq_dequantize_prev_kv /
- * kvq_extend_attention is bracketed by two HIP events
+ * kvq_store / kvq_decode(_append)(_fp8q) / kvq_compute_scale / kvq_compute_q_scale /
+ * kvq_dequantize_prev_kv / kvq_extend_attention is bracketed by two HIP events
  * recorded on the call's stream (nothing else changes; do not enable while
  * capturing a HIP graph). Enabling or disabling clears the records.
  * kvq_profile_read synchronizes the recorded events and returns, for one

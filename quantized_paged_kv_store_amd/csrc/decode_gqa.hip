@@ -33,6 +33,14 @@
 // per workgroup (fp32, split into bf16 hi + lo, two QK MFMAs), and
 // P[t][h] * vs[t] per tile (fp32, bf16 hi + lo for the PV MFMAs, V codes
 // exact in bf16); the softmax sum keeps the unscaled P.
+//
+// FP8-domain attention (vLLM "Quantized KV Cache" page, overview: with an
+// FP8 cache the attention itself runs in FP8, the query quantized like K and
+// V; "Supported schemes": q_scale per tensor or per query head): each
+// workgroup rounds its Q rows to E4M3 codes, RNE_sat(q / q_scale), once, and
+// S^T = K . Q^T runs on v_mfma_f32_16x16x32_{fp8,bf8}_fp8 with the cached
+// codes as the A operand exactly as loaded (no conversion at all); q_scale
+// joins k_scale and sm_scale on the scores. The PV side is unchanged.
 #include "store_row.h"
 
 namespace kvq {
@@ -146,6 +154,27 @@ __device__ __forceinline__ f32x4 qk_tile(const Tile<FMT, D>& t, const bf16x8* qf
   return acc;
 }
 
+// FP8-domain S^T tile: the 8 codes a lane holds per 32-element step are the
+// A operand as they are; q8[c] holds the E4M3 codes of the same 8 elements
+// of head lane%16 (the MFMA sums over k, so any common order of the 8
+// elements on both sides gives the same dot product).
+template <int FMT, int D>
+__device__ __forceinline__ f32x4 qk_tile_q8(const Tile<FMT, D>& t, const long* q8) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    const uint4& kk = t.k[c >> 1];
+    const uint32_t w0 = (c & 1) ? kk.z : kk.x;
+    const uint32_t w1 = (c & 1) ? kk.w : kk.y;
+    const long a = (long)(((uint64_t)w1 << 32) | w0);
+    if constexpr (FMT == KVQ_FP8_E4M3)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a, q8[c], acc, 0, 0, 0);
+    else
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf8_fp8(a, q8[c], acc, 0, 0, 0);
+  }
+  return acc;
+}
+
 // 8 floats -> bf16 hi (RNE) and lo = bf16(x - hi): 16 significant bits
 __device__ __forceinline__ void split_bf16x8(const float* p, bf16x8& bh, bf16x8& bl) {
   float r[8];
@@ -246,8 +275,9 @@ __device__ __forceinline__ int out_dim(int j, int g, int r) {
   return (FMT == KVQ_FP4_MX16) ? 8 * (4 * g + r) + j : 16 * j + 4 * g + r;
 }
 
-template <int FMT, int D, bool KIVI>
+template <int FMT, int D, bool KIVI, bool Q8 = false>
 __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs a) {
+  static_assert(!Q8 || (!KIVI && FMT != KVQ_FP4_MX16), "FP8-domain QK needs FP8 codes with tensor/head scales");
   constexpr int NJ = D / 16;                       // output accumulator tiles
   constexpr int NC = (FMT == KVQ_FP4_MX16) ? 4 : D / 32;  // QK MFMAs per tile
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -282,20 +312,35 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
   const int si = a.scale_mode == KVQ_SCALE_HEAD ? kvh : 0;  // per-tensor or per-KV-head FP8 scales
   const float kscale = (!KIVI && a.k_scale) ? a.k_scale[si] : 1.0f;
   const float vscale = (!KIVI && a.v_scale) ? a.v_scale[si] : 1.0f;
-  const float s_log2 = a.sm_scale_log2 * kscale;
+  float s_log2 = a.sm_scale_log2 * kscale;
 
   // Q^T operand fragments for head hc (zero beyond the group); KIVI: Q * ks
-  // as bf16 hi (qf) + lo (ql)
-  bf16x8 qf[NC], ql[KIVI ? NC : 1];
+  // as bf16 hi (qf) + lo (ql); FP8 domain: E4M3 codes of Q / q_scale (q8)
+  bf16x8 qf[Q8 ? 1 : NC], ql[KIVI ? NC : 1];
+  long q8[Q8 ? NC : 1];
   {
     const bool hv = hc < G;
     const uint16_t* qrow = a.q + ((int64_t)b * a.hq + (int64_t)kvh * G + (hv ? hc : 0)) * D;
+    float qs = 1.0f;
+    if constexpr (Q8) {
+      if (a.q_scale) qs = a.q_scale[a.scale_mode == KVQ_SCALE_HEAD ? kvh * G + (hv ? hc : 0) : 0];
+      s_log2 *= qs;
+    }
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int d0 = (FMT == KVQ_FP4_MX16) ? 32 * g + 8 * c : 64 * (c >> 1) + 16 * g + 8 * (c & 1);
       uint4 w = *reinterpret_cast<const uint4*>(qrow + d0);
       if (!hv) w = make_uint4(0, 0, 0, 0);
-      if constexpr (KIVI) {
+      if constexpr (Q8) {
+        // the same binary32 division and saturating RNE as the FP8 store
+        const uint32_t lo = encode_fp8x4<KVQ_FP8_E4M3>(
+            bf16_bits_to_f32(w.x & 0xffffu) / qs, bf16_bits_to_f32(w.x >> 16) / qs,
+            bf16_bits_to_f32(w.y & 0xffffu) / qs, bf16_bits_to_f32(w.y >> 16) / qs);
+        const uint32_t hi = encode_fp8x4<KVQ_FP8_E4M3>(
+            bf16_bits_to_f32(w.z & 0xffffu) / qs, bf16_bits_to_f32(w.z >> 16) / qs,
+            bf16_bits_to_f32(w.w & 0xffffu) / qs, bf16_bits_to_f32(w.w >> 16) / qs);
+        q8[c] = (long)(((uint64_t)hi << 32) | lo);
+      } else if constexpr (KIVI) {
         const float* ksr = a.k_scale + (int64_t)kvh * D + d0;
         const f32x4 s0 = *reinterpret_cast<const f32x4*>(ksr), s1 = *reinterpret_cast<const f32x4*>(ksr + 4);
         const uint32_t wq[4] = {w.x, w.y, w.z, w.w};
@@ -387,8 +432,14 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
     const int tA = P.tA;
     float s[8];
     {
-      const f32x4 sa = qk_tile<FMT, D, KIVI>(P.t[0], qf, ql);
-      const f32x4 sb = qk_tile<FMT, D, KIVI>(P.t[1], qf, ql);
+      f32x4 sa, sb;
+      if constexpr (Q8) {
+        sa = qk_tile_q8<FMT, D>(P.t[0], q8);
+        sb = qk_tile_q8<FMT, D>(P.t[1], q8);
+      } else {
+        sa = qk_tile<FMT, D, KIVI>(P.t[0], qf, ql);
+        sb = qk_tile<FMT, D, KIVI>(P.t[1], qf, ql);
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         s[i] = sa[i] * s_log2;
@@ -508,6 +559,8 @@ template <int FMT, int D>
 void launch_fp8(const GqaDecodeArgs& a, dim3 grid, hipStream_t s) {
   if (a.scale_mode == KVQ_SCALE_KIVI)
     decode_gqa_kernel<FMT, D, true><<<grid, 256, 0, s>>>(a);
+  else if (a.q8)
+    decode_gqa_kernel<FMT, D, false, true><<<grid, 256, 0, s>>>(a);
   else
     decode_gqa_kernel<FMT, D, false><<<grid, 256, 0, s>>>(a);
 }
@@ -523,7 +576,7 @@ hipError_t kvq_launch_decode_gqa(const kvq_cache* c, const GqaDecodeArgs& a, hip
     launch_fp8<KVQ_FP8_E5M2, 128>(a, grid, s);
   else if (dt == KVQ_FP8_E5M2 && D == 64)
     launch_fp8<KVQ_FP8_E5M2, 64>(a, grid, s);
-  else if (dt == KVQ_FP4_MX16 && D == 128)
+  else if (dt == KVQ_FP4_MX16 && D == 128 && !a.q8)
     decode_gqa_kernel<KVQ_FP4_MX16, 128, false><<<grid, 256, 0, s>>>(a);
   else
     return hipErrorInvalidValue;

@@ -369,11 +369,17 @@ namespace {
 
 // kvq_decode, optionally appending the token at position seq_lens[b] - 1 of
 // every sequence first (k_new / v_new non-null: kvq_decode_append)
+// (q8: FP8-domain attention, kvq_decode_fp8q / kvq_decode_append_fp8q)
 int decode_impl(const kvq_cache* c, const void* k_new, const void* v_new, const void* q, int32_t batch, int32_t hq,
                 const int32_t* page_table, int32_t page_table_stride, const int32_t* seq_lens, int32_t max_len,
                 float sm_scale, const float* k_scale, const float* v_scale, float* out, float* lse, void* ws,
-                size_t ws_bytes, void* stream) {
+                size_t ws_bytes, void* stream, bool q8 = false, const float* q_scale = nullptr) {
   if (!c || batch < 0 || hq < 1 || max_len < 0) return KVQ_ERR_ARG;
+  if (q8) {
+    const kvq_cache_desc& d = c->desc;
+    if (d.kind != KVQ_GQA || !is_fp8(d.dtype) || d.scale_mode == KVQ_SCALE_KIVI) return KVQ_ERR_UNSUPPORTED;
+    if (q_scale && reinterpret_cast<uintptr_t>(q_scale) % 4) return KVQ_ERR_ARG;
+  }
   if (batch == 0) return KVQ_OK;
   if (!q || !page_table || !seq_lens || !out || !aligned16(q)) return KVQ_ERR_ARG;
   const kvq_cache_desc& d = c->desc;
@@ -428,6 +434,8 @@ int decode_impl(const kvq_cache* c, const void* k_new, const void* v_new, const 
     a.lse = lse;
     a.new_k = static_cast<const uint16_t*>(k_new);
     a.new_v = static_cast<const uint16_t*>(v_new);
+    a.q8 = q8 ? 1 : 0;
+    a.q_scale = q_scale;
     hipError_t e;
     {
       Timed timer(1, s);
@@ -528,6 +536,44 @@ int kvq_decode_append(const kvq_cache* c, const void* k_new, const void* v_new, 
   if (!k_new) return KVQ_ERR_ARG;
   return decode_impl(c, k_new, v_new, q, batch, hq, page_table, page_table_stride, seq_lens, max_len, sm_scale,
                      k_scale, v_scale, out, lse, ws, ws_bytes, stream);
+}
+
+int kvq_decode_fp8q(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, const int32_t* page_table,
+                    int32_t page_table_stride, const int32_t* seq_lens, int32_t max_len, float sm_scale,
+                    const float* q_scale, const float* k_scale, const float* v_scale, float* out, float* lse,
+                    void* ws, size_t ws_bytes, void* stream) {
+  return decode_impl(c, nullptr, nullptr, q, batch, hq, page_table, page_table_stride, seq_lens, max_len, sm_scale,
+                     k_scale, v_scale, out, lse, ws, ws_bytes, stream, true, q_scale);
+}
+
+int kvq_decode_append_fp8q(const kvq_cache* c, const void* k_new, const void* v_new, const void* q, int32_t batch,
+                           int32_t hq, const int32_t* page_table, int32_t page_table_stride, const int32_t* seq_lens,
+                           int32_t max_len, float sm_scale, const float* q_scale, const float* k_scale,
+                           const float* v_scale, float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (!k_new) return KVQ_ERR_ARG;
+  return decode_impl(c, k_new, v_new, q, batch, hq, page_table, page_table_stride, seq_lens, max_len, sm_scale,
+                     k_scale, v_scale, out, lse, ws, ws_bytes, stream, true, q_scale);
+}
+
+int kvq_compute_q_scale(const kvq_cache* c, const void* q, int64_t n_tokens, int32_t num_q_heads, float* q_scale_out,
+                        void* stream) {
+  if (!c || !q_scale_out || n_tokens < 0 || num_q_heads < 1) return KVQ_ERR_ARG;
+  const kvq_cache_desc& d = c->desc;
+  if (d.kind != KVQ_GQA || !is_fp8(d.dtype) || d.scale_mode == KVQ_SCALE_KIVI) return KVQ_ERR_UNSUPPORTED;
+  if (num_q_heads % d.num_kv_heads) return KVQ_ERR_ARG;
+  if (n_tokens > 0 && (!q || !aligned16(q))) return KVQ_ERR_ARG;
+  if (d.scale_mode == KVQ_SCALE_HEAD && num_q_heads > kvq::kAmaxBlocks) return KVQ_ERR_UNSUPPORTED;
+  unsigned* scratch = reinterpret_cast<unsigned*>(c->base + c->layout.scratch_offset);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  Timed timer(3, s);
+  hipError_t e;
+  if (d.scale_mode == KVQ_SCALE_HEAD)
+    e = kvq_launch_amax_heads(static_cast<const uint16_t*>(q), n_tokens, nullptr, 0, num_q_heads, d.head_dim,
+                              scratch, 448.0f, q_scale_out, s);
+  else
+    e = kvq_launch_amax(static_cast<const uint16_t*>(q), n_tokens * num_q_heads * d.head_dim, nullptr, 0, scratch,
+                        448.0f, q_scale_out, s);
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
 int kvq_dequantize_prev_kv(const kvq_cache* c, const int32_t* pages, int32_t n_pages, const float* g_scale,

@@ -124,6 +124,11 @@ struct GqaDecodeArgs {
   // at position seq_lens[b] - 1, quantized and written by the split holding it
   const uint16_t* new_k;
   const uint16_t* new_v;
+  // FP8-domain attention (kvq_decode_fp8q): Q rounded to E4M3 with these
+  // scales (TENSOR mode: [1]; HEAD mode: [hq]; null = 1.0) and QK^T on FP8
+  // matrix cores straight from the cached codes
+  int q8;
+  const float* q_scale;
 };
 
 struct MlaDecodeArgs {

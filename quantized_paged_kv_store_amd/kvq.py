@@ -73,6 +73,16 @@ def _lib():
                                         c_void_p, c_int32, c_float, c_void_p, c_void_p, c_void_p, c_void_p,
                                         c_void_p, c_size_t, c_void_p]
         L.kvq_decode_append.restype = c_int32
+        L.kvq_decode_fp8q.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_int32,
+                                      c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                      c_void_p]
+        L.kvq_decode_fp8q.restype = c_int32
+        L.kvq_decode_append_fp8q.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p,
+                                             c_int32, c_void_p, c_int32, c_float, c_void_p, c_void_p, c_void_p,
+                                             c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+        L.kvq_decode_append_fp8q.restype = c_int32
+        L.kvq_compute_q_scale.argtypes = [c_void_p, c_void_p, c_int64, c_int32, c_void_p, c_void_p]
+        L.kvq_compute_q_scale.restype = c_int32
         L.kvq_dequantize_prev_kv.argtypes = [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                              c_void_p, c_void_p]
         L.kvq_dequantize_prev_kv.restype = c_int32
@@ -265,6 +275,64 @@ def kvq_decode_append(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor | N
                                     0 if workspace is None else workspace.numel(), _stream(dev)),
            "kvq_decode_append")
     return out, lse
+
+
+def _n_q_scales(cache: Cache, num_q_heads: int) -> int:
+    """Floats of a q_scale argument: Hq with per-head scales, else 1."""
+    return num_q_heads if cache.desc.scale_mode == SCALE_MODES["head"] else 1
+
+
+def kvq_compute_q_scale(cache: Cache, q: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """E4M3 query scales (amax / 448, per tensor or per query head as the
+    cache's scale mode) from a calibration batch q [tokens, Hq, D] BF16."""
+    dev = cache.device
+    assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.device == dev and q.dim() == 3
+    if out is None:
+        out = torch.empty(_n_q_scales(cache, q.shape[1]), dtype=torch.float32, device=dev)
+    _check(_lib().kvq_compute_q_scale(cache.handle, _ptr(q), q.shape[0], q.shape[1], _ptr(out), _stream(dev)),
+           "kvq_compute_q_scale")
+    return out
+
+
+def _decode_fp8q(name, cache, k_new, v_new, q, page_table, seq_lens, max_seq_len, sm_scale, q_scale, k_scale,
+                 v_scale, out, lse, workspace):
+    dev = cache.device
+    B, Hq, _ = q.shape
+    for t in (q, k_new, v_new):
+        assert t is None or (t.dtype == torch.bfloat16 and t.is_contiguous() and t.device == dev)
+    assert page_table.dtype == torch.int32 and page_table.is_contiguous() and page_table.dim() == 2
+    assert seq_lens.dtype == torch.int32 and seq_lens.numel() == B
+    if out is None:
+        out = torch.empty((B, Hq, cache.desc.v_dim), dtype=torch.float32, device=dev)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    need = kvq_decode_workspace_bytes(cache, B, Hq, max_seq_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    qs = _dev_f32(q_scale, dev, _n_q_scales(cache, Hq))
+    ks, vs = _dev_f32(k_scale, dev, _n_scales(cache)), _dev_f32(v_scale, dev, _n_scales(cache, "v"))
+    head = (cache.handle,) + ((_ptr(k_new), _ptr(v_new)) if name == "kvq_decode_append_fp8q" else ())
+    _check(getattr(_lib(), name)(*head, _ptr(q), B, Hq, _ptr(page_table), page_table.shape[1], _ptr(seq_lens),
+                                 max_seq_len, float(sm_scale), _ptr(qs), _ptr(ks), _ptr(vs), _ptr(out), _ptr(lse),
+                                 _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(dev)), name)
+    return out, lse
+
+
+def kvq_decode_fp8q(cache: Cache, q: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                    max_seq_len: int, sm_scale: float, q_scale=None, k_scale=None, v_scale=None, out=None, lse=None,
+                    workspace=None):
+    """kvq_decode with Q rounded to E4M3 (q / q_scale) and QK^T on FP8 matrix
+    cores. Returns (out fp32 [B, Hq, D], lse fp32 [B, Hq])."""
+    return _decode_fp8q("kvq_decode_fp8q", cache, None, None, q, page_table, seq_lens, max_seq_len, sm_scale,
+                        q_scale, k_scale, v_scale, out, lse, workspace)
+
+
+def kvq_decode_append_fp8q(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                           page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int, sm_scale: float,
+                           q_scale=None, k_scale=None, v_scale=None, out=None, lse=None, workspace=None):
+    """kvq_decode_append followed by kvq_decode_fp8q, in one launch."""
+    return _decode_fp8q("kvq_decode_append_fp8q", cache, k_new, v_new, q, page_table, seq_lens, max_seq_len,
+                        sm_scale, q_scale, k_scale, v_scale, out, lse, workspace)
 
 
 def kvq_dequantize_prev_kv(cache: Cache, pages: torch.Tensor, k_scale_out=None, v_scale_out=None, g=None,

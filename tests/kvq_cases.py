@@ -93,7 +93,9 @@ class Case:
     def run_gpu(self, decode=True, append=False):
         """append: the last token of every sequence is not stored separately;
         kvq_decode_append stores it and decodes in one call (one new token per
-        sequence required)."""
+        sequence required). append without decode leaves those tokens, as
+        self.append_rows (device BF16 [B, ...] K and V), to the caller's own
+        append call."""
         w = self.w
         assert not append or w.new_tokens == 1
         self.cache = K.kvq_alloc_pages(w.dtype, w.kind, w.kv_heads, w.head_dim, w.v_dim, w.page_size,
@@ -157,9 +159,11 @@ class Case:
                     if vb is not None:
                         vb[b] = vn[i].reshape(row)
                     i += 1
-            self.out, self.lse = K.kvq_decode_append(
-                self.cache, self._bf16(kb), None if vb is None else self._bf16(vb), self.q_dev, self.table_dev,
-                self.lens_dev, self.max_len, I.sm_scale(w), self.k_scale, self.v_scale)
+            self.append_rows = (self._bf16(kb), None if vb is None else self._bf16(vb))
+            if decode:
+                self.out, self.lse = K.kvq_decode_append(
+                    self.cache, *self.append_rows, self.q_dev, self.table_dev, self.lens_dev, self.max_len,
+                    I.sm_scale(w), self.k_scale, self.v_scale)
         elif decode:
             self.out, self.lse = K.kvq_decode(self.cache, self.q_dev, self.table_dev, self.lens_dev, self.max_len,
                                               I.sm_scale(w), self.k_scale, self.v_scale)

@@ -300,3 +300,35 @@ def test_extend_attention_argument_errors():
     assert call(q=c_void_p(FAKE_DEV + 2)) == ARG                 # 16-byte alignment
     assert call(dq=None) == ARG                                  # pages but no workspace
     assert call(batch=-1) == ARG and call(page=0) == ARG and call(max_chunk=-1) == ARG
+
+
+def test_fp8q_decode_and_q_scale_argument_errors(handles):
+    """FP8-domain decode: FP8 GQA caches with tensor or per-head scales only;
+    q_scale 4-byte aligned; kvq_compute_q_scale's argument checks."""
+    lib, h = handles
+    P = c_void_p(FAKE_DEV)
+
+    def dec(cache, qs=None, batch=4, hq=8):
+        return lib.kvq_decode_fp8q(cache, P, batch, hq, P, 4, P, 64, 0.1, qs, None, None, P, None, None, 0, None)
+    assert dec(h["mx"]) == UNSUP and dec(h["mla"], hq=128) == UNSUP             # codes are not FP8
+    assert dec(h["fp8"], qs=c_void_p(FAKE_DEV + 2)) == ARG                       # misaligned q_scale
+    assert dec(h["fp8"], batch=0) == OK                                          # empty batch
+    assert dec(h["fp8"], hq=7) == ARG                                            # as kvq_decode
+    app = lambda cache, k, v: lib.kvq_decode_append_fp8q(cache, k, v, P, 4, 8, P, 4, P, 64, 0.1, None, None, None,
+                                                         P, None, None, 0, None)
+    assert app(h["fp8"], None, P) == ARG and app(h["fp8"], P, None) == ARG and app(h["mx"], P, P) == UNSUP
+    q = lib.kvq_compute_q_scale
+    assert q(h["mx"], P, 4, 8, P, None) == UNSUP
+    assert q(h["fp8"], P, 4, 8, None, None) == ARG                               # no output
+    assert q(h["fp8"], P, -1, 8, P, None) == ARG
+    assert q(h["fp8"], P, 4, 7, P, None) == ARG                                  # Hq % Hkv
+    assert q(h["fp8"], None, 4, 8, P, None) == ARG and q(h["fp8"], c_void_p(FAKE_DEV + 2), 4, 8, P, None) == ARG
+    # KIVI caches fold a channel scale into the query: not an FP8-domain case
+    d = _desc("e4m3", hkv=2)
+    d.scale_mode = 2
+    need = c_size_t()
+    hk = c_void_p()
+    assert lib.kvq_alloc_pages(byref(d), None, 0, byref(need), None) == OK
+    assert lib.kvq_alloc_pages(byref(d), c_void_p(FAKE_DEV), need.value, byref(need), byref(hk)) == OK
+    assert dec(hk) == UNSUP and q(hk, P, 4, 8, P, None) == UNSUP
+    lib.kvq_free_handle(hk)

@@ -1,7 +1,7 @@
 """The entry points captured in a HIP graph (store + decode, the one-launch
 append step with tensor and KIVI-style scales, dequantize_prev_kv + extend
-attention): every replay (with eager
-work and synchronizations in between) must reproduce the eager result."""
+attention): every replay, with eager work and synchronizations in between,
+must reproduce the eager result."""
 import numpy as np
 import pytest
 import torch
