@@ -1,6 +1,6 @@
 """The entry points captured in a HIP graph (store + decode, the one-launch
-append step with tensor and KIVI-style scales, dequantize_prev_kv + extend
-attention): every replay, with eager work and synchronizations in between,
+append step with tensor and KIVI-style scales and in the FP8 domain,
+dequantize_prev_kv + extend attention): every replay, with eager work and synchronizations in between,
 must reproduce the eager result."""
 import numpy as np
 import pytest
@@ -134,3 +134,33 @@ def test_graph_replay_dequant_prev_and_extend_match_eager():
         assert np.array_equal(dk.cpu().numpy(), eager_dk)
         assert np.array_equal(out.cpu().numpy(), eager) and np.array_equal(lse.cpu().numpy(), eager_lse)
         _ = (q.float() * 2).sum().item()
+
+
+def test_graph_replay_fp8q_append_matches_eager():
+    """FP8-domain append step (kvq_decode_append_fp8q) captured in a HIP graph."""
+    w = I.WORKLOADS["llama3_8b"].with_(batch=2, max_len=3000, min_len=3000, scale_mode="amax_head")
+    c = Case(w).run_gpu(decode=False, append=True)
+    qs = K.kvq_compute_q_scale(c.cache, c.q_dev)
+    need = K.kvq_decode_workspace_bytes(c.cache, w.batch, w.q_heads, c.max_len)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=c.dev)
+    out = torch.empty((w.batch, w.q_heads, w.v_dim), dtype=torch.float32, device=c.dev)
+    lse = torch.empty((w.batch, w.q_heads), dtype=torch.float32, device=c.dev)
+
+    def step():
+        K.kvq_decode_append_fp8q(c.cache, *c.append_rows, c.q_dev, c.table_dev, c.lens_dev, c.max_len,
+                                 I.sm_scale(w), qs, c.k_scale, c.v_scale, out=out, lse=lse, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager, eager_lse = out.cpu().numpy().copy(), lse.cpu().numpy().copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for _ in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), eager) and np.array_equal(lse.cpu().numpy(), eager_lse)
+        _ = (c.q_dev.float() * 2).sum().item()
