@@ -280,7 +280,7 @@ def bench_dequant_prev(w, args, dev):
 
     import quantized_paged_kv_store_amd as K
     t0 = time.time()
-    st = setup(w, dev, args.rotate, args.fp8q)
+    st = setup(w, dev, args.rotate)
     log(f"setup {time.time() - t0:.1f} s")
     caches = st["caches"]
     d = caches[0].desc
@@ -521,7 +521,7 @@ def main():
         bench_extend(w, args, dev)
         return
     t0 = time.time()
-    st = setup(w, dev, args.rotate)
+    st = setup(w, dev, args.rotate, args.fp8q)
     log(f"setup {time.time() - t0:.1f} s")
     # a decode step with one new token per sequence appends it and decodes in
     # one launch (kvq_decode_append); a chunked step stores, then decodes

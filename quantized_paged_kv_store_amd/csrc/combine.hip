@@ -7,12 +7,9 @@
 // reported with the natural-log LSE (LSE * ln 2). Splits past the sequence
 // end were never written and are not read.
 //
-// The merge reads ~1 MB and is bound by memory latency, not bandwidth, so a
-// lane owns one output element of one (sequence, query head) and merges
-// without any exchange: it loads up to 8 splits' LSEs (the same addresses
-// in every lane: one broadcast load each) and its 8 output elements at once,
-// folds them into a running (max, sum, weighted sum), and repeats for more
-// splits. One HBM round trip for the usual <= 8 splits; no LDS, no barrier.
+// One workgroup per (sequence, query head): the split weights are computed
+// once into LDS, then every thread streams its output elements over the
+// splits with independent, coalesced loads.
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -20,45 +17,45 @@ namespace {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kMaxSplits = 128;
-constexpr int kBatch = 8;  // splits loaded per round
 
-__global__ void __launch_bounds__(64) combine_kernel(const CombineArgs a) {
-  const int chunks = (a.dv + 63) >> 6;
-  const int h = blockIdx.x / chunks, d = ((blockIdx.x - h * chunks) << 6) + threadIdx.x;
-  const int b = blockIdx.y;
+__global__ void __launch_bounds__(128) combine_kernel(const CombineArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   int L = a.seq_lens[b];
   L = L < 0 ? 0 : (L > a.max_len ? a.max_len : L);
   int n = (L + a.tokens_per_split - 1) / a.tokens_per_split;
   n = n > a.num_splits ? a.num_splits : n;
   const int64_t hq = (int64_t)b * a.hq + h;
+  __shared__ float sw[kMaxSplits];
+  __shared__ float s_lse;
   const float* lse_s = a.ws_lse + hq * a.num_splits;
-  const float* o_s = a.ws_o + hq * a.num_splits * (int64_t)a.dv + (d < a.dv ? d : 0);
-  float M = kNegInf, W = 0.f, acc = 0.f;
-  for (int s0 = 0; s0 < n; s0 += kBatch) {
-    float x[kBatch], o[kBatch];
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const bool ok = s0 + j < n;
-      x[j] = ok ? lse_s[s0 + j] : kNegInf;
-      o[j] = ok ? o_s[(int64_t)(s0 + j) * a.dv] : 0.f;
-    }
-    float Mn = M;
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) Mn = fmaxf(Mn, x[j]);
-    if (Mn == kNegInf) continue;
-    const float r = __builtin_amdgcn_exp2f(M - Mn);  // 0 while M is -inf
-    W *= r;
-    acc *= r;
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      const float e = __builtin_amdgcn_exp2f(x[j] - Mn);
-      W += e;
-      acc = fmaf(e, o[j], acc);
-    }
-    M = Mn;
+  if (tid < 64) {
+    // wave 0: max and sum over at most 128 splits, two per lane
+    const float x0 = tid < n ? lse_s[tid] : kNegInf;
+    const float x1 = tid + 64 < n ? lse_s[tid + 64] : kNegInf;
+    float M = fmaxf(x0, x1);
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    const float e0 = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(x0 - M);
+    const float e1 = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(x1 - M);
+    float W = e0 + e1;
+    for (int off = 32; off > 0; off >>= 1) W += __shfl_xor(W, off, 64);
+    const float inv = W > 0.f ? 1.0f / W : 0.f;
+    sw[tid] = e0 * inv;
+    sw[tid + 64] = e1 * inv;
+    if (tid == 0) s_lse = W > 0.f ? (M + __log2f(W)) * 0.6931471805599453f : kNegInf;
   }
-  if (d < a.dv) a.out[hq * a.dv + d] = W > 0.f ? acc / W : 0.f;
-  if (a.lse && d == 0) a.lse[hq] = W > 0.f ? (M + __log2f(W)) * 0.6931471805599453f : kNegInf;
+  __syncthreads();
+  const float* o_s = a.ws_o + hq * a.num_splits * (int64_t)a.dv;
+  for (int d = tid; d < a.dv; d += blockDim.x) {
+    float acc0 = 0.f, acc1 = 0.f;
+    int s = 0;
+    for (; s + 1 < n; s += 2) {
+      acc0 += sw[s] * o_s[(int64_t)s * a.dv + d];
+      acc1 += sw[s + 1] * o_s[(int64_t)(s + 1) * a.dv + d];
+    }
+    if (s < n) acc0 += sw[s] * o_s[(int64_t)s * a.dv + d];
+    a.out[hq * a.dv + d] = acc0 + acc1;
+  }
+  if (tid == 0 && a.lse) a.lse[hq] = s_lse;
 }
 
 }  // namespace
@@ -66,7 +63,7 @@ __global__ void __launch_bounds__(64) combine_kernel(const CombineArgs a) {
 
 hipError_t kvq_launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.num_splits > kvq::kMaxSplits) return hipErrorInvalidValue;
-  const dim3 grid(a.hq * ((a.dv + 63) / 64), a.batch);
-  kvq::combine_kernel<<<grid, 64, 0, s>>>(a);
+  const dim3 grid(a.hq, a.batch);
+  kvq::combine_kernel<<<grid, 128, 0, s>>>(a);
   return hipGetLastError();
 }
