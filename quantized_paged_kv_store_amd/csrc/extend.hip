@@ -72,6 +72,9 @@ __device__ __forceinline__ u32x2 lds_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+// POW2: the workspace page size is a power of two (page and offset of a key
+// by shift and mask instead of a division)
+template <bool POW2>
 __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a) {
   const int nwg = gridDim.x;  // a multiple of 8
   const int work = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
@@ -119,30 +122,51 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
 
   // global -> registers: a prefix block is 2 + 2 E4M3 chunks of 16 bytes
   // (16 elements) per thread, a chunk block 4 + 4 BF16 chunks (8 elements);
-  // keys past the prefix or the chunk read zeros. Every register is written
-  // on both paths.
+  // keys past the prefix or the chunk read zeros (only blocks that reach
+  // past the end check keys). Every register is written on both paths.
+  // Thread tid loads keys tid/8 + 32 i (prefix) or tid/16 + 16 i (chunk).
+  const int pkey = tid >> 3, pcol = 16 * (tid & 7);
+  const int ckey = tid >> 4, ccol = 8 * (tid & 15);
+  const int pshift = __builtin_ctz(P);  // used when P is a power of two
+  const int64_t crow = (int64_t)a.hkv * XD;  // elements between consecutive chunk tokens
   uint4 rk[4], rvv[4];
   auto load_block = [&](int kb) {
+    if (kb < nb0) {
+      const bool full = (kb + 1) * XKB <= L0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const bool prefix = kb < nb0;
-      const int c = tid + 256 * i;
-      const int key = prefix ? (c >> 3) : (c >> 4);
-      const int t = prefix ? kb * XKB + key : (kb - nb0) * XKB + key;
-      const bool ok = prefix ? (i < 2 && t < L0) : (t < C);
-      const uint8_t* kp;
-      const uint8_t* vp;
-      if (prefix) {
-        const int64_t r = ((int64_t)(po + t / P) * a.hkv + kvh) * P + t % P;
-        kp = a.dq_k + r * XD + 16 * (c & 7);
-        vp = a.dq_v + r * XD + 16 * (c & 7);
-      } else {
-        const int64_t r = ((int64_t)(q0 + t) * a.hkv + kvh) * XD + 8 * (c & 15);
-        kp = reinterpret_cast<const uint8_t*>(a.k_new + r);
-        vp = reinterpret_cast<const uint8_t*>(a.v_new + r);
+      for (int i = 0; i < 2; ++i) {
+        const int t = kb * XKB + pkey + 32 * i;
+        const int pg = POW2 ? (t >> pshift) : t / P;
+        const int off = t - pg * P;
+        const int64_t r = ((int64_t)(po + pg) * a.hkv + kvh) * P + off;
+        const uint4* kp = reinterpret_cast<const uint4*>(a.dq_k + r * XD + pcol);
+        const uint4* vp = reinterpret_cast<const uint4*>(a.dq_v + r * XD + pcol);
+        if (full) {
+          rk[i] = *kp;
+          rvv[i] = *vp;
+        } else {
+          rk[i] = t < L0 ? *kp : make_uint4(0, 0, 0, 0);
+          rvv[i] = t < L0 ? *vp : make_uint4(0, 0, 0, 0);
+        }
       }
-      rk[i] = ok ? *reinterpret_cast<const uint4*>(kp) : make_uint4(0, 0, 0, 0);
-      rvv[i] = ok ? *reinterpret_cast<const uint4*>(vp) : make_uint4(0, 0, 0, 0);
+      rk[2] = rk[3] = rvv[2] = rvv[3] = make_uint4(0, 0, 0, 0);
+    } else {
+      const int tb = (kb - nb0) * XKB;
+      const bool full = tb + XKB <= C;
+      const int64_t e0 = (int64_t)(q0 + tb + ckey) * crow + (int64_t)kvh * XD + ccol;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = tb + ckey + 16 * i;
+        const uint4* kp = reinterpret_cast<const uint4*>(a.k_new + e0 + 16 * i * crow);
+        const uint4* vp = reinterpret_cast<const uint4*>(a.v_new + e0 + 16 * i * crow);
+        if (full) {
+          rk[i] = *kp;
+          rvv[i] = *vp;
+        } else {
+          rk[i] = t < C ? *kp : make_uint4(0, 0, 0, 0);
+          rvv[i] = t < C ? *vp : make_uint4(0, 0, 0, 0);
+        }
+      }
     }
   };
   // registers -> LDS buffer: K rows as bf16; V rows as fp16 codes (prefix) or
@@ -344,6 +368,9 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
 
 hipError_t kvq_launch_extend(const ExtendArgs& a, hipStream_t s) {
   const int64_t nwg = (a.n_work + 7) / 8 * 8;
-  kvq::extend_attn_kernel<<<(unsigned)nwg, 256, 0, s>>>(a);
+  if ((a.page_size & (a.page_size - 1)) == 0)
+    kvq::extend_attn_kernel<true><<<(unsigned)nwg, 256, 0, s>>>(a);
+  else
+    kvq::extend_attn_kernel<false><<<(unsigned)nwg, 256, 0, s>>>(a);
   return hipGetLastError();
 }
