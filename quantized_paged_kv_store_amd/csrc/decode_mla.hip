@@ -140,8 +140,8 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
 
   __shared__ __attribute__((aligned(16))) uint8_t sm_k[kStepTokens * kKRow];
   __shared__ __attribute__((aligned(16))) uint8_t sm_p[4 * 2 * 64 * 16];           // [k step][head block][lane][8 x fp16]
-  __shared__ __attribute__((aligned(16))) float sm_s[kWavesMla * 4 * 64 * 4];     // partial scores [wave][quad][lane][4]
-  __shared__ float sm_mx[2][kHeadsPerWG];
+  __shared__ __attribute__((aligned(16))) float sm_s[kWavesMla * 2 * 64 * 4];     // partial scores [wave][quad][lane][4]
+  __shared__ float sm_mx[2][2][kHeadsPerWG];                                       // [token half][k half][head]
   __shared__ float sm_alpha[kHeadsPerWG];
   __shared__ float sm_l[4][kHeadsPerWG];
   __shared__ float sm_e[4][kHeadsPerWG];
@@ -344,36 +344,50 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
       }
       __builtin_amdgcn_sched_group_barrier(0x008, kDepth - 1, 0);
     }
-    // publish the partial scores for the wave holding the other half of the dot product
+    // Each wave turns values 8kh..8kh+7 of the scores into P (the B operand
+    // of PV k step 2tb + kh), so it needs the other half of the dot product
+    // for those 8 only: it publishes the 8 partials its partner (kh ^ 1)
+    // needs and adds the 8 it gets back. Same sums, in the same order, as
+    // exchanging all 16.
+    float mine[8];
+    {
+      float give[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      *reinterpret_cast<f32x4*>(sm_s + ((wave * 4 + q) * 64 + lane) * 4) =
-          f32x4{sc[4 * q], sc[4 * q + 1], sc[4 * q + 2], sc[4 * q + 3]};
-    __syncthreads();
-    // both waves add the same two partials, so they hold identical scores
+      for (int u = 0; u < 8; ++u) {
+        mine[u] = kh ? sc[8 + u] : sc[u];
+        give[u] = kh ? sc[u] : sc[8 + u];
+      }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x4 o4 = *reinterpret_cast<const f32x4*>(sm_s + (((wave ^ 2) * 4 + q) * 64 + lane) * 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sc[4 * q + i] += o4[i];
+      for (int q2 = 0; q2 < 2; ++q2)
+        *reinterpret_cast<f32x4*>(sm_s + ((wave * 2 + q2) * 64 + lane) * 4) =
+            f32x4{give[4 * q2], give[4 * q2 + 1], give[4 * q2 + 2], give[4 * q2 + 3]};
     }
-    // lane value v holds token 32tb + 8(v/4) + 4hh + v%4 of the step
+    __syncthreads();
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      const f32x4 o4 = *reinterpret_cast<const f32x4*>(sm_s + (((wave ^ 2) * 2 + q2) * 64 + lane) * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mine[4 * q2 + i] += o4[i];
+    }
+    // value u of mine is token 32tb + 16kh + 8(u/4) + 4hh + u%4 of the step
     if (__builtin_expect(tail, 0)) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int tl = 32 * tb + 8 * (v >> 2) + 4 * hh + (v & 3);
-        if (!((ok >> (tl >> 4)) & 1) || tA * kTile + tl >= L) sc[v] = kNegInf;
+      for (int u = 0; u < 8; ++u) {
+        const int tl = 32 * tb + 16 * kh + 8 * (u >> 2) + 4 * hh + (u & 3);
+        if (!((ok >> (tl >> 4)) & 1) || tA * kTile + tl >= L) mine[u] = kNegInf;
       }
     }
-    float mx = sc[0];
+    // maximum over this wave's 16 tokens (8 per lane half), then over the
+    // four (token half, k half) waves of the head block
+    float mx = mine[0];
 #pragma unroll
-    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[v]);
+    for (int u = 1; u < 8; ++u) mx = fmaxf(mx, mine[u]);
     mx = fmaxf(mx, shfl_xor_f32(mx, 32)) * sscale;
     const int hl = 32 * hgp + r32;
-    if (kh == 0 && hh == 0) sm_mx[tb][hl] = mx;
+    if (hh == 0) sm_mx[tb][kh][hl] = mx;
     __syncthreads();
     {
-      mx = fmaxf(mx, sm_mx[tb ^ 1][hl]);
+      mx = fmaxf(fmaxf(sm_mx[0][0][hl], sm_mx[0][1][hl]), fmaxf(sm_mx[1][0][hl], sm_mx[1][1][hl]));
       // the reference maximum only moves when a score exceeds it by more
       // than 2^kSlack, so the rescale of the accumulators below is rare; P
       // then stays <= 2^(kSlack + kPBias) = 2^15 in fp16. The four waves of
@@ -382,10 +396,9 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
       const float m_new = move ? mx : m_run;
       const float mb2 = (m_new == kNegInf) ? 0.f : m_new - kPBias;
       const float alpha = move ? ((m_run == kNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new)) : 1.0f;
-      // this wave turns values 8kh..8kh+7 into P: the B operand of PV k step 2tb + kh
       float p[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(kh ? sc[8 + u] : sc[u], sscale, -mb2));
+      for (int u = 0; u < 8; ++u) p[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(mine[u], sscale, -mb2));
       uint32_t pk[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) pk[i] = pack_f16x2(p[2 * i], p[2 * i + 1]);
