@@ -22,11 +22,11 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 
-# per-source extras: the MLA and extend kernels keep their MFMA accumulators in VGPR form
+# per-source extras: the extend kernel keeps its MFMA accumulators in VGPR form
 # (otherwise the compiler parks them in AGPRs and copies all 128 of them
-# through VGPRs on every step)
-EXTRA = {"decode_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-         "extend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# through VGPRs on every step); the MLA kernel wants the default, with its
+# output accumulators in the AGPRs
+EXTRA = {"extend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _hipcc() -> str:

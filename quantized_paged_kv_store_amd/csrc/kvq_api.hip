@@ -108,28 +108,30 @@ SplitPlan plan_gqa(int batch, int hkv, int max_len) {
   return {(int)tps, (int)ns};
 }
 
-// MLA: one workgroup (4 waves) per (sequence, split, 64-head group) and one
+// MLA: one workgroup (4 waves, all query heads) per (sequence, split) and one
 // per CU, so the default target is one round of 256 workgroups; each split
-// is an even number of 16-token tiles whose pages fit the LDS page-id stage.
+// is an even number of 16-token tiles (whole 32-token steps) whose pages fit
+// the LDS page-id stage.
 SplitPlan plan_mla(int batch, int hq, int max_len, int page_size) {
+  (void)hq;
   const int ntiles = (max_len + kvq::kTile - 1) / kvq::kTile;
   const int tpp = page_size / kvq::kTile;
-  const int64_t units = (int64_t)batch * (hq / 64);
+  const int64_t units = batch;
   int64_t target = 256;
   if (const char* e = getenv("KVQ_DECODE_TARGET_WGS")) {
     const long v = strtol(e, nullptr, 10);
     if (v >= 1 && v <= (1 << 20)) target = v;
   }
-  const int64_t cap = ((int64_t)(kvq::kMlaMaxSplitPages - 1) * tpp) & ~(int64_t)3;
+  const int64_t cap = ((int64_t)(kvq::kMlaMaxSplitPages - 1) * tpp) & ~(int64_t)1;
   int64_t tps = units > 0 ? (ntiles * units + target - 1) / target : ntiles;
-  if (tps < 4) tps = 4;
-  tps = (tps + 3) & ~(int64_t)3;  // whole 64-token steps
+  if (tps < 2) tps = 2;
+  tps = (tps + 1) & ~(int64_t)1;  // whole 32-token steps
   if (tps > cap) tps = cap;
   int64_t ns = ntiles > 0 ? (ntiles + tps - 1) / tps : 1;
   if (ns > 128) {
     ns = 128;
     tps = (ntiles + ns - 1) / ns;
-    tps = (tps + 3) & ~(int64_t)3;
+    tps = (tps + 1) & ~(int64_t)1;
     ns = (ntiles + tps - 1) / tps;
   }
   if (ns < 1) ns = 1;
