@@ -295,26 +295,26 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
     S.ok = ok;
   };
 
-  // dequantize the step held in S into K^ buffer `buf`: elements
-  // [128w, 128w+128) of its 32 tokens and this thread's rope item per tile;
-  // tokens that are not real are written as zeros
-  auto dequant = [&](const Step& S, uint8_t* buf, auto tail_tag) {
+  // dequantize chunk c of the step held in S into K^ buffer `buf`: chunks
+  // 0..3 are elements [64(2w + c%2), +64) of tile c/2's 16 tokens, chunks 4
+  // and 5 this thread's rope item of tile c-4; tokens that are not real are
+  // written as zeros
+  auto dequant_chunk = [&](const Step& S, uint8_t* buf, const int c, auto tail_tag) {
     constexpr bool kTail = decltype(tail_tag)::value;
     const int tA = S.tA;
-#pragma unroll
-    for (int s = 0; s < kStepTiles; ++s) {
+    if (c < 4) {
+      const int s = c >> 1, j = c & 1;
       const int nvalid = kTail ? (((S.ok >> s) & 1) ? max(0, min(4, L - (tA + s) * kTile - 4 * g)) : 0) : 4;
+      uint2 x[4];
+      dequant16(S.v[s][j], S.vs[s][j], x);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        uint2 x[4];
-        dequant16(S.v[s][j], S.vs[s][j], x);
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          if (kTail && tt >= nvalid) x[tt] = make_uint2(0u, 0u);
-          const int row = 16 * s + 4 * g + tt;
-          *reinterpret_cast<uint2*>(buf + row * kKRow + 2 * (64 * (2 * wave + j) + 4 * col)) = x[tt];
-        }
+      for (int tt = 0; tt < 4; ++tt) {
+        if (kTail && tt >= nvalid) x[tt] = make_uint2(0u, 0u);
+        const int row = 16 * s + 4 * g + tt;
+        *reinterpret_cast<uint2*>(buf + row * kKRow + 2 * (64 * (2 * wave + j) + 4 * col)) = x[tt];
       }
+    } else {
+      const int s = c - 4;
       const f16x2 rsc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(S.rs[s], 1.0f, false);
       const f16x2 rs2 = {rsc[0], rsc[0]};
       uint32_t r0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(S.r[s], 1.0f, 0) * rs2);
@@ -354,10 +354,16 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
   Step R;
   issue(R);
   int tA_c = R.tA, ok_c = R.ok;
-  if (is_tail(tA_c, ok_c))
-    dequant(R, sm_k, std::true_type{});
-  else
-    dequant(R, sm_k, std::false_type{});
+  {
+    auto all_chunks = [&](auto tail_tag) {
+#pragma unroll
+      for (int c = 0; c < 6; ++c) dequant_chunk(R, sm_k, c, tail_tag);
+    };
+    if (is_tail(tA_c, ok_c))
+      all_chunks(std::true_type{});
+    else
+      all_chunks(std::false_type{});
+  }
   issue(R);
   __syncthreads();
 
@@ -366,14 +372,14 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
     uint8_t* nb = sm_k + ((st & 1) ^ 1) * kBuf;
     const int tA_n = R.tA, ok_n = R.ok;
 
-    // 1. S^T[token i][head h0 + r32] over all 576 elements, two chains;
-    //    the next step is dequantized into the other buffer meanwhile
+    // 1. S^T[token i][head h0 + r32] over all 576 elements from buffer kb,
+    //    the K^ operand read three products ahead
     f32x16 sc0;
-    auto scores_and_next = [&](auto tail_tag) {
+    {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sc0[i] = 0.f;
       const uint8_t* krow = kb + r32 * kKRow + 16 * hh;
-      constexpr int kDepth = 4;  // K^ fragments read ahead of their products
+      constexpr int kDepth = 4;
       f16x8 ka[kDepth];
 #pragma unroll
       for (int ks = 0; ks < kDepth - 1; ++ks) ka[ks] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4*>(krow + 32 * ks));
@@ -385,18 +391,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
         sc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[ks % kDepth], qf[ks], sc0, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, kDepth - 1, 0);
-#pragma unroll
-      for (int i = 0; i < 36 - (kDepth - 1); ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, kDepth - 1, 0);
-    };
-    if (is_tail(tA_n, ok_n))
-      scores_and_next(std::true_type{});
-    else
-      scores_and_next(std::false_type{});
+    }
 
     // 2. value v of the scores is token 8(v/4) + 4hh + v%4 of the step
     float s[16];
@@ -469,10 +464,17 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    if (is_tail(tA_n, ok_n))
-      dequant(R, nb, std::true_type{});
-    else
-      dequant(R, nb, std::false_type{});
+    // 4. the next step into buffer nb, then the loads of the step after
+    {
+      auto all_chunks = [&](auto tail_tag) {
+#pragma unroll
+        for (int c = 0; c < 6; ++c) dequant_chunk(R, nb, c, tail_tag);
+      };
+      if (is_tail(tA_n, ok_n))
+        all_chunks(std::true_type{});
+      else
+        all_chunks(std::false_type{});
+    }
     issue(R);
     __syncthreads();  // buffer kb is rewritten by the next step's dequantization
     tA_c = tA_n;
