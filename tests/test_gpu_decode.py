@@ -114,6 +114,60 @@ def test_mla_split_count_invariance():
         assert rel_l2(o, outs[0][0]) < 3e-4 and np.allclose(l, outs[0][1], atol=1e-5)
 
 
+class _RampCase(Case):
+    """The 64 rope dims of latent row t scaled by 1 + 0.015 t (input generation
+    only; both sides see the same BF16 rows). They enter the scores but not
+    V, so the largest score of each 32-token step keeps climbing while the
+    outputs stay unit-scale: the MLA kernel's lazy reference maximum moves
+    again and again inside one split and its accumulators are rescaled."""
+
+    def rows(self, b, t0, t1):
+        k, v = super().rows(b, t0, t1)
+        kf = I.bf16_to_f32(k)
+        kf[:, 512:] *= (1.0 + 0.015 * np.arange(t0, t1, dtype=np.float32))[:, None]
+        return I.bf16_bits(kf), v
+
+
+@pytest.mark.parametrize("hq,P,target", [(128, 64, "3"), (64, 16, "3"), (128, 64, None)])
+def test_mla_reference_moves(hq, P, target):
+    lens = [3000, 1500, 33]
+    w = I.Workload(f"mla-ramp-{hq}", "nvfp4", "mla", len(lens), hq, 1, 576, 512, P, max(lens), 0, 1, "mla", seed=19)
+    # the inputs do what the test is for: on sequence 0, head 0, the running
+    # maximum of the (log2-domain) scores rises past the reference + 2^8 many
+    # times after the first 32-token step
+    c = _RampCase(w, lens=lens)
+    k, _ = c.rows(0, 0, lens[0])
+    q = I.bf16_to_f32(I.queries(w))[0, 0]
+    s2 = (I.bf16_to_f32(k) @ q) * I.sm_scale(w) / np.log(2.0)
+    ref, moves = s2[:32].max(), 0
+    for t0 in range(32, lens[0], 32):
+        m = s2[t0:t0 + 32].max()
+        if m > ref + 8.0:
+            ref, moves = m, moves + 1
+    assert moves >= 5, moves
+    if target is not None:
+        os.environ["KVQ_DECODE_TARGET_WGS"] = target   # one split per sequence: direct output path
+    try:
+        c.run_gpu()
+    finally:
+        os.environ.pop("KVQ_DECODE_TARGET_WGS", None)
+    ids = [0, 1, 2]
+    what = f"mla ramp Hq{hq} P{P} target {target}"
+    want, wlse, _, _ = c.oracle_decode(ids)
+    assert_close(c.out.cpu().numpy()[ids], want[ids], what)
+    # LSE: these scores reach ~10^2, so their fp32 accumulation error counts.
+    # An LSE moves by at most the largest error of its scores, and a score's
+    # error is at most sm_scale * gamma_576 * sum_i |q_i k_i| (k^ within 1.5x
+    # of the BF16 row for NVFP4), so that bound (plus 1e-4) is the tolerance.
+    gamma = 576 * 2.0 ** -24 / (1 - 576 * 2.0 ** -24)
+    qa = np.abs(I.bf16_to_f32(I.queries(w)))
+    glse = c.lse.cpu().numpy()
+    for b in ids:
+        ka = np.abs(I.bf16_to_f32(c.rows(b, 0, lens[b])[0]))
+        tol = 1e-4 + I.sm_scale(w) * gamma * 1.5 * float((qa[b] @ ka.T).max())
+        assert np.allclose(glse[b], wlse[b], rtol=0, atol=tol), (what, b, tol, np.abs(glse[b] - wlse[b]).max())
+
+
 @pytest.mark.parametrize("dtype", ["e4m3", "mx16"])
 def test_one_workspace_serves_calls_of_any_shape(dtype):
     """One workspace, sized for the largest call, serves calls of different
