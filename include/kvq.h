@@ -95,7 +95,7 @@ typedef struct kvq_cache_desc {
  *   GQA x FP4_MX16:     head_dim == 128
  *   MLA x NVFP4:        head_dim == 576, v_dim == 512
  *   decode, GQA:        G = Hq / Hkv in [1, 16], max_seq_len <= 2,097,152
- *   decode, MLA:        Hq in {64, 128}                                      */
+ *   decode, MLA:        1 <= Hq <= 128                                       */
 
 /* Byte offsets (from the start of the caller's cache memory) and sizes of the
  * buffers inside one cache. Absent buffers have size 0. Each buffer is

@@ -16,8 +16,9 @@
 //   O^T[d][h] += V^T[d][t] . P^T[t][h]      v_mfma_f32_32x32x16_f16, P * 2^7
 // and g is factored out of both (applied to the scores and to the output).
 //
-// Workgroup = 4 waves, one per SIMD, = all (up to 128) query heads of one
-// (sequence, context split). One wave per SIMD has 256 VGPRs and 256 AGPRs:
+// Workgroup = 4 waves, one per SIMD, = all (1 to 128) query heads of one
+// (sequence, context split); head columns past the head count carry a zero
+// query and are not written. One wave per SIMD has 256 VGPRs and 256 AGPRs:
 // wave w owns heads 32w..32w+31 outright, with their query in VGPRs (144)
 // and their whole O^T (512 x 32 fp32) in the AGPRs, so its scores, softmax
 // and PV need nothing from the other waves. A step covers 32 tokens (two
@@ -150,7 +151,8 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
   const int g = lane >> 4, col = lane & 15;   // dequant role: token group, element quad
   const int r32 = lane & 31, hh = lane >> 5;  // MFMA role: row / column, k half
   const int h0 = kHeadsPerWave * wave;        // this wave's first head
-  const bool active = h0 < a.hq;              // wave-uniform; idle waves only dequantize
+  // this lane's head column exists (waves past the head count only dequantize)
+  const bool head_ok = h0 + r32 < a.hq;
 
   const int L = min(max(a.seq_lens[b], 0), a.max_len);
   const int ntiles = (L + kTile - 1) / kTile;
@@ -193,7 +195,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
   // B operand of k step ks: head h0 + r32, elements 16*ks + 8*hh .. +7
   f16x8 qf[36];
   float sscale = 0.f;
-  if (active) {
+  if (head_ok) {
     const uint16_t* qrow = a.q + ((int64_t)b * a.hq + h0 + r32) * kDk;
     uint32_t mx = 0;
 #pragma unroll
@@ -484,7 +486,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
   // ---- epilogue: normalize and write this split's partial (or the output) ----
   l_run += shfl_xor_f32(l_run, 32);
   e_run += shfl_xor_f32(e_run, 32);
-  if (!active) return;
+  if (!head_ok) return;
   const bool direct = a.num_splits == 1;
   const float inv = l_run > 0.f ? a.g_scale[0] / l_run : 0.f;
   const int64_t hq = (int64_t)b * a.hq + h0 + r32;

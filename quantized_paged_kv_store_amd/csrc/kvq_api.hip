@@ -363,7 +363,7 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* c, int32_t batch, int32_t hq,
   if (!c || batch < 0 || hq < 1 || max_len < 0) return 0;
   if (c->desc.kind == KVQ_GQA)
     return workspace_for(plan_gqa(batch, c->desc.num_kv_heads, max_len), batch, hq, c->desc.v_dim).total;
-  if (hq != 64 && hq != 128) return 0;
+  if (hq < 1 || hq > 128) return 0;
   return workspace_for(plan_mla(batch, hq, max_len, c->desc.page_size), batch, hq, c->desc.v_dim).total;
 }
 
@@ -464,7 +464,7 @@ int decode_impl(const kvq_cache* c, const void* k_new, const void* v_new, const 
     return KVQ_OK;
   }
   // MLA
-  if (hq != 64 && hq != 128) return KVQ_ERR_UNSUPPORTED;
+  if (hq < 1 || hq > 128) return KVQ_ERR_UNSUPPORTED;
   if (!k_scale) return KVQ_ERR_ARG;  // the NVFP4 global scale
   const SplitPlan plan = plan_mla(batch, hq, max_len, c->desc.page_size);
   // pages one split touches, whatever its alignment to page boundaries

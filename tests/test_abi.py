@@ -184,9 +184,11 @@ def test_mla_decode_argument_errors(handles):
     lib, h = handles
     P = c_void_p(FAKE_DEV)
     mla = lambda hq, ks, batch=2: (h["mla"], P, batch, hq, P, 16, P, 1000, 0.04, ks, None, P, None, None, 0, None)
-    assert lib.kvq_decode(*mla(96, P)) == UNSUP          # 64 or 128 heads only
+    assert lib.kvq_decode(*mla(129, P)) == UNSUP         # at most 128 heads (one workgroup per split)
+    assert lib.kvq_decode(*mla(0, P)) == ARG
     assert lib.kvq_decode(*mla(128, None)) == ARG        # the NVFP4 global scale is required
-    assert lib.kvq_decode_workspace_bytes(h["mla"], 2, 96, 1000) == 0
+    assert lib.kvq_decode_workspace_bytes(h["mla"], 2, 129, 1000) == 0
+    assert lib.kvq_decode_workspace_bytes(h["mla"], 2, 16, 1000) > 0
 
 
 def test_decode_append_argument_errors(handles):
@@ -198,7 +200,7 @@ def test_decode_append_argument_errors(handles):
     assert lib.kvq_decode_append(h["fp8"], c_void_p(FAKE_DEV + 2), P, *tail) == ARG  # 16-byte aligned rows
     mla = (P, 2, 128, P, 16, P, 1000, 0.04, P, None, P, None, None, 0, None)
     assert lib.kvq_decode_append(h["mla"], P, P, *mla) == ARG                      # MLA has no V rows
-    assert lib.kvq_decode_append(h["mla"], P, None, P, 2, 96, P, 16, P, 1000, 0.04, P, None, P, None, None, 0,
+    assert lib.kvq_decode_append(h["mla"], P, None, P, 2, 129, P, 16, P, 1000, 0.04, P, None, P, None, None, 0,
                                  None) == UNSUP
     assert lib.kvq_decode_append(h["fp8"], P, P, P, 0, 8, P, 4, P, 64, 0.1, None, None, P, None, None, 0,
                                  None) == OK                                       # empty batch

@@ -44,7 +44,7 @@ def test_append_gqa(dtype, D, G, P):
     _check(a, b, f"append {dtype} D{D} G{G} P{P}", [0, 1, 4, 9])
 
 
-@pytest.mark.parametrize("hq,P", [(128, 64), (64, 16)])
+@pytest.mark.parametrize("hq,P", [(128, 64), (64, 16), (16, 64)])
 def test_append_mla(hq, P):
     w = I.Workload(f"append-mla-{hq}", "nvfp4", "mla", len(LENS), hq, 1, 576, 512, P, max(LENS), 0, 1, "mla",
                    seed=22)
