@@ -375,7 +375,9 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
     const int tA_n = R.tA, ok_n = R.ok;
 
     // 1. S^T[token i][head h0 + r32] over all 576 elements from buffer kb,
-    //    the K^ operand read three products ahead
+    //    the K^ operand read three products ahead. Every product (here and
+    //    in PV) is fenced from the scheduler: left free, it hoists all 36
+    //    operand reads ahead of the chain and the wave runs out of VGPRs.
     f32x16 sc0;
     {
 #pragma unroll
