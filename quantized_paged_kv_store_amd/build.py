@@ -22,11 +22,9 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 
-# per-source extras: the extend kernel keeps its MFMA accumulators in VGPR form
-# (otherwise the compiler parks them in AGPRs and copies all 128 of them
-# through VGPRs on every step); the MLA kernel wants the default, with its
-# output accumulators in the AGPRs
-EXTRA = {"extend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# per-source extras: none; the MLA and extend kernels want the default MFMA
+# form, with their accumulators in the AGPRs
+EXTRA = {}
 
 
 def _hipcc() -> str:

@@ -7,11 +7,15 @@
 // code * s_k or s_v, the workspace's per-tensor scales) and to their own BF16
 // K/V causally; the G query heads of a KV head share its K/V (GQA).
 //
-// Work split: one workgroup (4 waves) per (sequence, KV head, tile of
-// 128 / G chunk tokens): 128 query rows (token, head), 32 per wave. Block ids
-// are remapped so that all tiles of one (sequence, KV head) run on one XCD
-// (the 8 XCDs take block ids round robin): they stream the same prefix, which
-// then stays in that XCD's L2.
+// Work split: one workgroup (4 waves, one per SIMD) per (sequence, KV head,
+// tile of 256 / G chunk tokens): 256 query rows (token, head), 64 per wave in
+// two 32-row blocks. Each K and V^T fragment a wave reads from LDS feeds the
+// products of both row blocks, which halves the LDS operand traffic per flop
+// and spreads the per-block staging over twice the work. The score and output
+// accumulators (64 + 128 registers) live in the AGPRs, the query operands and
+// the staging in VGPRs. Block ids are remapped so that all tiles of one
+// (sequence, KV head) run on one XCD (the 8 XCDs take block ids round robin):
+// they stream the same prefix, which then stays in that XCD's L2.
 //
 // Per 64-key block, staged in LDS (K and V row-major, K as bf16, V as fp16
 // codes for the prefix and bf16 values for the chunk; two buffers, the next
@@ -43,7 +47,7 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int XD = 128;             // head dim
 constexpr int XKB = 64;             // keys per block
-constexpr int XROWS = 128;          // query rows per workgroup
+constexpr int XROWS = kExtendRows;  // query rows per workgroup (64 per wave, two 32-row blocks)
 constexpr int XK_STRIDE = XD + 8;   // 16-bit elements per LDS K row: 272 B, rows 4 banks apart
 constexpr int XV_STRIDE = XD + 32;  // per LDS V row: 320 B, rows 16 banks apart (transposed reads)
 constexpr float kXNegInf = -__builtin_huge_valf();
@@ -63,6 +67,41 @@ __device__ __forceinline__ void split_bf16(const float* p, bf16x8& hi, bf16x8& l
   const u32x4 l = {pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3]), pack_bf16x2(r[4], r[5]), pack_bf16x2(r[6], r[7])};
   hi = __builtin_bit_cast(bf16x8, h);
   lo = __builtin_bit_cast(bf16x8, l);
+}
+
+// acc *= alpha on accumulators that live in AGPRs, one element at a time
+// through a VGPR (VALU cannot read AGPRs), so a rare rescale does not pull
+// the accumulators into VGPRs; the trailing s_nop covers the VALU write ->
+// matrix-core read of the AGPRs by the next product
+__device__ __forceinline__ void scale_acc(f32x16& o, float alpha) {
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = o[i];
+  float t;
+  asm volatile(
+      "v_accvgpr_read_b32 %16, %0\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %0, %16\n\t"
+      "v_accvgpr_read_b32 %16, %1\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %1, %16\n\t"
+      "v_accvgpr_read_b32 %16, %2\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %2, %16\n\t"
+      "v_accvgpr_read_b32 %16, %3\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %3, %16\n\t"
+      "v_accvgpr_read_b32 %16, %4\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %4, %16\n\t"
+      "v_accvgpr_read_b32 %16, %5\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %5, %16\n\t"
+      "v_accvgpr_read_b32 %16, %6\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %6, %16\n\t"
+      "v_accvgpr_read_b32 %16, %7\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %7, %16\n\t"
+      "v_accvgpr_read_b32 %16, %8\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %8, %16\n\t"
+      "v_accvgpr_read_b32 %16, %9\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %9, %16\n\t"
+      "v_accvgpr_read_b32 %16, %10\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %10, %16\n\t"
+      "v_accvgpr_read_b32 %16, %11\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %11, %16\n\t"
+      "v_accvgpr_read_b32 %16, %12\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %12, %16\n\t"
+      "v_accvgpr_read_b32 %16, %13\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %13, %16\n\t"
+      "v_accvgpr_read_b32 %16, %14\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %14, %16\n\t"
+      "v_accvgpr_read_b32 %16, %15\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %15, %16\n\t"
+      "s_nop 4"
+      : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]), "+a"(x[4]), "+a"(x[5]), "+a"(x[6]), "+a"(x[7]),
+        "+a"(x[8]), "+a"(x[9]), "+a"(x[10]), "+a"(x[11]), "+a"(x[12]), "+a"(x[13]), "+a"(x[14]), "+a"(x[15]),
+        "=&v"(t)
+      : "v"(alpha));
+#pragma unroll
+  for (int i = 0; i < 16; ++i) o[i] = x[i];
 }
 
 // transposed 4 x 16-bit LDS read: in each 16-lane group, lane i receives
@@ -96,20 +135,27 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, hh = lane >> 5;
-  const int row = 32 * wave + j;  // this lane's query row
-  const int tok = t0 + row / G;
-  const int head = kvh * G + row % G;
-  const bool rv = tok < C;
+  // this lane's query rows: 64 wave + 32 rb + j for row blocks rb = 0, 1
+  int tok[2], head[2];
+  bool rv[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = 64 * wave + 32 * rb + j;
+    tok[rb] = t0 + row / G;
+    head[rb] = kvh * G + row % G;
+    rv[rb] = tok[rb] < C;
+  }
 
-  // Q^T operand: lane (row, half hh) holds d = 16 ks + 8 hh .. + 7 (zero for
+  // Q^T operands: lane (row, half hh) holds d = 16 ks + 8 hh .. + 7 (zero for
   // rows past the chunk: their scores are 0 and their outputs not written)
-  bf16x8 qf[XD / 16];
-  {
-    const uint16_t* qp = a.q + ((int64_t)(q0 + (rv ? tok : 0)) * a.hq + head) * XD + 8 * hh;
+  bf16x8 qf[2][XD / 16];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const uint16_t* qp = a.q + ((int64_t)(q0 + (rv[rb] ? tok[rb] : 0)) * a.hq + head[rb]) * XD + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < XD / 16; ++ks) {
-      uint4 w = rv ? *reinterpret_cast<const uint4*>(qp + 16 * ks) : make_uint4(0, 0, 0, 0);
-      qf[ks] = __builtin_bit_cast(bf16x8, w);
+      uint4 w = rv[rb] ? *reinterpret_cast<const uint4*>(qp + 16 * ks) : make_uint4(0, 0, 0, 0);
+      qf[rb][ks] = __builtin_bit_cast(bf16x8, w);
     }
   }
 
@@ -203,12 +249,14 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
   const float sm2 = a.sm_scale * kXLog2e;
   const float skv = a.s_k ? a.s_k[0] : 1.0f;
   const float svv = a.s_v ? a.s_v[0] : 1.0f;
-  f32x16 o[XD / 32];
+  f32x16 o[2][XD / 32];  // O^T per row block: elements 32 dt .. +31 x 32 rows
 #pragma unroll
-  for (int dt = 0; dt < XD / 32; ++dt)
+  for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) o[dt][v] = 0.f;
-  float m_ref = kXNegInf, l_run = 0.f;
+    for (int dt = 0; dt < XD / 32; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[rb][dt][v] = 0.f;
+  float m_ref[2] = {kXNegInf, kXNegInf}, l_run[2] = {0.f, 0.f};
   // transposed-read lane address: lane 4e + c of each 16-lane group reads key
   // row 4 hh + e, elements 16 ((lane >> 4) & 1) + 4 c (+ 32 dt)
   const int v_lane = (4 * hh + ((lane & 15) >> 2)) * XV_STRIDE + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -222,97 +270,128 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
     constexpr bool MASK = decltype(mask_tag)::value;
     const uint16_t* kd = sk[kb & 1];
     const uint16_t* vd = sv[kb & 1];
-    // every LDS operand of the block is read up front (K for the scores, V^T
-    // for PV, which does not depend on the scores)
-    bf16x8 ka[2][XD / 16];
+    // scores for the 64 keys, both row blocks: tile kt holds keys
+    // 32 kt + 8 (v/4) + 4 hh + v%4. Each K fragment (read three products
+    // ahead) serves the two row blocks; every product is fenced from the
+    // scheduler, which would otherwise hoist all operand reads and spill.
+    f32x16 acc[2][2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int ks = 0; ks < XD / 16; ++ks)
-        ka[kt][ks] = *reinterpret_cast<const bf16x8*>(kd + (32 * kt + j) * XK_STRIDE + 16 * ks + 8 * hh);
-    u32x4 va[4][XD / 32];
-#pragma unroll
-    for (int stp = 0; stp < 4; ++stp) {
-      const uint16_t* vb = vd + v_lane + (32 * (stp >> 1) + 16 * (stp & 1)) * XV_STRIDE;
-#pragma unroll
-      for (int dt = 0; dt < XD / 32; ++dt) {
-        const u32x2 lo = lds_tr16(vb + 32 * dt), hi = lds_tr16(vb + 32 * dt + 8 * XV_STRIDE);
-        va[stp][dt] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-      }
-    }
-    // scores for the 64 keys: tile kt holds keys 32 kt + 8 (v/4) + 4 hh + v%4
-    f32x16 acc[2];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[kt][v] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < XD / 16; ++ks)
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
-        acc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kt][ks], qf[ks], acc[kt], 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[rb][kt][v] = 0.f;
+    {
+      constexpr int kDepth = 3;
+      auto kread = [&](int i) {  // i = 2 ks + kt
+        return *reinterpret_cast<const bf16x8*>(kd + (32 * (i & 1) + j) * XK_STRIDE + 16 * (i >> 1) + 8 * hh);
+      };
+      bf16x8 ka[kDepth];
+#pragma unroll
+      for (int i = 0; i < kDepth - 1; ++i) ka[i] = kread(i);
+#pragma unroll
+      for (int i = 0; i < 2 * (XD / 16); ++i) {
+        if (i + kDepth - 1 < 2 * (XD / 16)) ka[(i + kDepth - 1) % kDepth] = kread(i + kDepth - 1);
+        const int kt = i & 1, ks = i >> 1;
+        acc[0][kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i % kDepth], qf[0][ks], acc[0][kt], 0, 0, 0);
+        acc[1][kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i % kDepth], qf[1][ks], acc[1][kt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     const float scl = PRE ? sm2 * skv : sm2;  // > 0: the maximum commutes with it
-    float s[2][16];
-    float mx = kXNegInf;
-    if constexpr (MASK) {
-      const int lim = PRE ? L0 - kb * XKB : tok - (kb - nb0) * XKB + 1;  // keys below lim are visible
+    // P of both row blocks in the B-operand layout of the four 16-key PV
+    // steps (fp16 for the prefix, bf16 hi + lo for the chunk)
+    u32x4 ph[2][4], pl[2][4];
+    bool move_any = false;
+    float alpha[2];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+    for (int rb = 0; rb < 2; ++rb) {
+      float s[2][16];
+      float mx = kXNegInf;
+      if constexpr (MASK) {
+        const int lim = PRE ? L0 - kb * XKB : tok[rb] - (kb - nb0) * XKB + 1;  // keys below lim are visible
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = 32 * kt + 8 * (v >> 2) + 4 * hh + (v & 3);
-          s[kt][v] = key < lim ? acc[kt][v] : kXNegInf;
-          mx = fmaxf(mx, s[kt][v]);
-        }
-    } else {
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          s[kt][v] = acc[kt][v];
-          mx = fmaxf(mx, s[kt][v]);
-        }
-    }
-    mx = fmaxf(mx, shfl_xor_f32(mx, 32)) * scl;
-    // lazy reference: move (and rescale) only when a score exceeds it by 2^8
-    if (__builtin_amdgcn_ballot_w64(mx > m_ref + kXLazy) != 0ull) {
-      const float m_new = fmaxf(m_ref, mx);
-      const float alpha = (m_ref == kXNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < XD / 32; ++dt) o[dt] *= alpha;
-      m_ref = m_new;
-    }
-    const float mb = (m_ref == kXNegInf) ? 0.f : m_ref - kXPBias;
-    float psum = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        s[kt][v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][v], scl, -mb));
-        psum += s[kt][v];
-      }
-    l_run += psum;
-    // O^T += V^T P^T, 16 keys per step
-#pragma unroll
-    for (int stp = 0; stp < 4; ++stp) {
-      const float* pv = &s[stp >> 1][8 * (stp & 1)];
-      if constexpr (PRE) {
-        const u32x4 pp = {pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]), pack_f16x2(pv[4], pv[5]),
-                          pack_f16x2(pv[6], pv[7])};
-        const f16x8 pb = __builtin_bit_cast(f16x8, pp);
-#pragma unroll
-        for (int dt = 0; dt < XD / 32; ++dt)
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va[stp][dt]), pb, o[dt], 0, 0, 0);
+          for (int v = 0; v < 16; ++v) {
+            const int key = 32 * kt + 8 * (v >> 2) + 4 * hh + (v & 3);
+            s[kt][v] = key < lim ? acc[rb][kt][v] : kXNegInf;
+            mx = fmaxf(mx, s[kt][v]);
+          }
       } else {
-        bf16x8 ph, pl;
-        split_bf16(pv, ph, pl);
 #pragma unroll
-        for (int dt = 0; dt < XD / 32; ++dt) {
-          const bf16x8 ab = __builtin_bit_cast(bf16x8, va[stp][dt]);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, ph, o[dt], 0, 0, 0);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, pl, o[dt], 0, 0, 0);
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            s[kt][v] = acc[rb][kt][v];
+            mx = fmaxf(mx, s[kt][v]);
+          }
+      }
+      mx = fmaxf(mx, shfl_xor_f32(mx, 32)) * scl;
+      // lazy reference: move (and rescale) only when a score exceeds it by 2^8
+      const bool move = mx > m_ref[rb] + kXLazy;
+      const float m_new = move ? mx : m_ref[rb];
+      alpha[rb] = move ? ((m_ref[rb] == kXNegInf) ? 0.f : __builtin_amdgcn_exp2f(m_ref[rb] - m_new)) : 1.0f;
+      move_any |= move;
+      m_ref[rb] = m_new;
+      const float mb = (m_new == kXNegInf) ? 0.f : m_new - kXPBias;
+      float psum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          s[kt][v] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][v], scl, -mb));
+          psum += s[kt][v];
         }
+      l_run[rb] = l_run[rb] * alpha[rb] + psum;
+#pragma unroll
+      for (int stp = 0; stp < 4; ++stp) {
+        const float* pv = &s[stp >> 1][8 * (stp & 1)];
+        if constexpr (PRE) {
+          ph[rb][stp] = u32x4{pack_f16x2(pv[0], pv[1]), pack_f16x2(pv[2], pv[3]), pack_f16x2(pv[4], pv[5]),
+                              pack_f16x2(pv[6], pv[7])};
+        } else {
+          bf16x8 h, l;
+          split_bf16(pv, h, l);
+          ph[rb][stp] = __builtin_bit_cast(u32x4, h);
+          pl[rb][stp] = __builtin_bit_cast(u32x4, l);
+        }
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(move_any) != 0ull) {  // rare after the first blocks
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int dt = 0; dt < XD / 32; ++dt) scale_acc(o[rb][dt], alpha[rb]);
+    }
+    // O^T += V^T P^T, 16 keys per step; each V^T fragment (read two products
+    // ahead) serves both row blocks
+    {
+      constexpr int kVDepth = 3;
+      auto vread = [&](int i) {  // i = 4 stp + dt
+        const uint16_t* vb = vd + v_lane + (32 * ((i >> 2) >> 1) + 16 * ((i >> 2) & 1)) * XV_STRIDE + 32 * (i & 3);
+        const u32x2 lo = lds_tr16(vb), hi = lds_tr16(vb + 8 * XV_STRIDE);
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+      };
+      u32x4 va[kVDepth];
+#pragma unroll
+      for (int i = 0; i < kVDepth - 1; ++i) va[i] = vread(i);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i + kVDepth - 1 < 16) va[(i + kVDepth - 1) % kVDepth] = vread(i + kVDepth - 1);
+        const int stp = i >> 2, dt = i & 3;
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          if constexpr (PRE) {
+            o[rb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va[i % kVDepth]),
+                                                               __builtin_bit_cast(f16x8, ph[rb][stp]), o[rb][dt], 0, 0, 0);
+          } else {
+            const bf16x8 ab = __builtin_bit_cast(bf16x8, va[i % kVDepth]);
+            o[rb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, __builtin_bit_cast(bf16x8, ph[rb][stp]), o[rb][dt], 0, 0, 0);
+            o[rb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, __builtin_bit_cast(bf16x8, pl[rb][stp]), o[rb][dt], 0, 0, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // the next block into the other buffer (last read by the previous
@@ -336,7 +415,9 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
   if (nb0 > nfull0) block(T{}, T{}, nb0 - 1);
   if (nb0 > 0) {  // the prefix values carry the workspace V scale
 #pragma unroll
-    for (int dt = 0; dt < XD / 32; ++dt) o[dt] *= svv;
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int dt = 0; dt < XD / 32; ++dt) scale_acc(o[rb][dt], svv);
   }
   // chunk: blocks whose keys all precede the tile's first token and lie in
   // the chunk need no mask, the rest (the diagonal) do
@@ -345,21 +426,24 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
   for (int kb = nb0; kb < nb0 + nfree; ++kb) block(F{}, F{}, kb);
   for (int kb = nb0 + nfree; kb < nb; ++kb) block(F{}, T{}, kb);
 
-  l_run += shfl_xor_f32(l_run, 32);
-  if (rv) {
-    const float inv = l_run > 0.f ? 1.0f / l_run : 0.f;
-    float* op = a.out + ((int64_t)(q0 + tok) * a.hq + head) * XD;
 #pragma unroll
-    for (int dt = 0; dt < XD / 32; ++dt)
+  for (int rb = 0; rb < 2; ++rb) {
+    const float lr = l_run[rb] + shfl_xor_f32(l_run[rb], 32);
+    if (rv[rb]) {
+      const float inv = lr > 0.f ? 1.0f / lr : 0.f;
+      float* op = a.out + ((int64_t)(q0 + tok[rb]) * a.hq + head[rb]) * XD;
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const float4 val = make_float4(o[dt][4 * a4] * inv, o[dt][4 * a4 + 1] * inv, o[dt][4 * a4 + 2] * inv,
-                                       o[dt][4 * a4 + 3] * inv);
-        *reinterpret_cast<float4*>(op + 32 * dt + 8 * a4 + 4 * hh) = val;
-      }
-    if (a.lse && hh == 0)
-      a.lse[(int64_t)(q0 + tok) * a.hq + head] =
-          l_run > 0.f ? (m_ref + __log2f(l_run) - kXPBias) * kXLn2 : kXNegInf;
+      for (int dt = 0; dt < XD / 32; ++dt)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          const float4 val = make_float4(o[rb][dt][4 * a4] * inv, o[rb][dt][4 * a4 + 1] * inv,
+                                         o[rb][dt][4 * a4 + 2] * inv, o[rb][dt][4 * a4 + 3] * inv);
+          *reinterpret_cast<float4*>(op + 32 * dt + 8 * a4 + 4 * hh) = val;
+        }
+      if (a.lse && hh == 0)
+        a.lse[(int64_t)(q0 + tok[rb]) * a.hq + head[rb]] =
+            lr > 0.f ? (m_ref[rb] + __log2f(lr) - kXPBias) * kXLn2 : kXNegInf;
+    }
   }
 }
 

@@ -608,12 +608,12 @@ int kvq_extend_attention(const void* q, const void* k_new, const void* v_new, co
   if (num_kv_heads < 1 || num_q_heads < 1 || num_q_heads % num_kv_heads) return KVQ_ERR_ARG;
   if (head_dim != 128) return KVQ_ERR_UNSUPPORTED;
   const int G = num_q_heads / num_kv_heads;
-  if (G > 16 || (G & (G - 1))) return KVQ_ERR_UNSUPPORTED;  // 128 query rows per workgroup = 128/G tokens
+  if (G > 16 || (G & (G - 1))) return KVQ_ERR_UNSUPPORTED;  // 256 query rows per workgroup = 256/G tokens
   if (batch == 0 || total_q == 0 || max_chunk == 0) return KVQ_OK;
   if (!q || !k_new || !v_new || !cu_q || !prefix_len || !page_off || !out) return KVQ_ERR_ARG;
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out)) return KVQ_ERR_ARG;
   if (n_pages > 0 && (!dq_k || !dq_v || !aligned16(dq_k) || !aligned16(dq_v))) return KVQ_ERR_ARG;
-  const int TT = 128 / G;
+  const int TT = kvq::kExtendRows / G;
   const int64_t q_tiles = ((int64_t)max_chunk + TT - 1) / TT;
   const int64_t n_work = (int64_t)batch * num_kv_heads * q_tiles;
   if (n_work > INT32_MAX - 8) return KVQ_ERR_UNSUPPORTED;

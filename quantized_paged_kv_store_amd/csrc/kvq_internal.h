@@ -22,6 +22,7 @@ constexpr int kTile = 16;      // tokens per tile inside a page
 constexpr int kWaves = 4;      // waves per decode workgroup
 constexpr int kAmaxBlocks = 1024;
 constexpr int kMlaMaxSplitPages = 1024;  // page ids one MLA split stages in LDS
+constexpr int kExtendRows = 256;         // (chunk token, query head) rows per extend workgroup
 
 // ------------------------------------------------------- vector typedefs --
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -176,7 +177,7 @@ struct ExtendArgs {
   float* out;              // fp32 [total_q][hq][128]
   float* lse;              // fp32 [total_q][hq] or null (natural log)
   int total_q, n_pages, batch, hq, hkv, group, page_size, max_chunk;
-  int q_tiles, n_work;     // tiles of 128/group chunk tokens per sequence; batch * hkv * q_tiles
+  int q_tiles, n_work;     // tiles of kExtendRows/group chunk tokens per sequence; batch * hkv * q_tiles
   float sm_scale;
 };
 

@@ -296,7 +296,7 @@ def test_extend_attention_argument_errors():
     assert call(batch=0) == OK and call(total_q=0) == OK and call(max_chunk=0) == OK      # no-ops
     assert call(d=64) == UNSUP                                   # head_dim 128 only
     assert call(hq=48, hkv=2) == UNSUP                           # G = 24
-    assert call(hq=6, hkv=2) == UNSUP                            # G = 3: 128 rows / G not whole tokens
+    assert call(hq=6, hkv=2) == UNSUP                            # G = 3: 256 rows / G not whole tokens
     assert call(hq=33, hkv=2) == ARG                             # Hq % Hkv
     assert call(q=None) == ARG and call(out=None) == ARG
     assert call(q=c_void_p(FAKE_DEV + 2)) == ARG                 # 16-byte alignment
