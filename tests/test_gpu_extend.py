@@ -42,6 +42,7 @@ def _oracle(inp, s_k, s_v, sm, rows=None):
     (8, 32, [100, 0, 257], [33, 16, 17]),
     (4, 16, [500, 31], [40, 3]),
     (1, 16, [70, 129], [129, 5]),
+    (1, 32, [40, 0], [300, 513]),      # G = 1: 256 chunk tokens per tile, so these span 2 and 3 tiles
     (2, 64, [64, 640], [200, 1]),
 ])
 def test_extend_matches_oracle(G, P, prefix, chunk):
