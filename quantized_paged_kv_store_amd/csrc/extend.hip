@@ -7,15 +7,15 @@
 // code * s_k or s_v, the workspace's per-tensor scales) and to their own BF16
 // K/V causally; the G query heads of a KV head share its K/V (GQA).
 //
-// Work split: one workgroup (4 waves, one per SIMD) per (sequence, KV head,
-// tile of 256 / G chunk tokens): 256 query rows (token, head), 64 per wave in
-// two 32-row blocks. Each K and V^T fragment a wave reads from LDS feeds the
-// products of both row blocks, which halves the LDS operand traffic per flop
-// and spreads the per-block staging over twice the work. The score and output
-// accumulators (64 + 128 registers) live in the AGPRs, the query operands and
-// the staging in VGPRs. Block ids are remapped so that all tiles of one
-// (sequence, KV head) run on one XCD (the 8 XCDs take block ids round robin):
-// they stream the same prefix, which then stays in that XCD's L2.
+// Work split: one workgroup (8 waves, two per SIMD) per (sequence, KV head,
+// tile of 256 / G chunk tokens): 256 query rows (token, head), 32 per wave.
+// Two waves per SIMD let one wave's softmax run under the other's matrix
+// products; that needs <= 256 registers per wave, which holds because the
+// operands are read from LDS just in time through short rings instead of
+// being hoisted, and the next block's staging is spread over 512 threads.
+// Block ids are remapped so that all tiles of one (sequence, KV head) run on
+// one XCD (the 8 XCDs take block ids round robin): they stream the same
+// prefix, which then stays in that XCD's L2.
 //
 // Per 64-key block, staged in LDS (K and V row-major, K as bf16, V as fp16
 // codes for the prefix and bf16 values for the chunk; two buffers, the next
@@ -47,7 +47,13 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int XD = 128;             // head dim
 constexpr int XKB = 64;             // keys per block
-constexpr int XROWS = kExtendRows;  // query rows per workgroup (64 per wave, two 32-row blocks)
+constexpr int XROWS = kExtendRows;  // query rows per workgroup
+constexpr int XWAVES = 8;           // waves per workgroup (two per SIMD)
+constexpr int XRB = XROWS / (32 * XWAVES);  // 32-row blocks per wave (each K / V^T fragment feeds all of them)
+constexpr int XTHREADS = 64 * XWAVES;
+constexpr int XPI = XKB * 8 / XTHREADS;   // 16-byte prefix chunks (K and V each) per thread and block
+constexpr int XCI = XKB * 16 / XTHREADS;  // 16-byte chunk chunks (K and V each) per thread and block
+static_assert(XRB >= 1 && XPI >= 1 && XCI >= 1, "workgroup shape");
 constexpr int XK_STRIDE = XD + 8;   // 16-bit elements per LDS K row: 272 B, rows 4 banks apart
 constexpr int XV_STRIDE = XD + 32;  // per LDS V row: 320 B, rows 16 banks apart (transposed reads)
 constexpr float kXNegInf = -__builtin_huge_valf();
@@ -69,41 +75,6 @@ __device__ __forceinline__ void split_bf16(const float* p, bf16x8& hi, bf16x8& l
   lo = __builtin_bit_cast(bf16x8, l);
 }
 
-// acc *= alpha on accumulators that live in AGPRs, one element at a time
-// through a VGPR (VALU cannot read AGPRs), so a rare rescale does not pull
-// the accumulators into VGPRs; the trailing s_nop covers the VALU write ->
-// matrix-core read of the AGPRs by the next product
-__device__ __forceinline__ void scale_acc(f32x16& o, float alpha) {
-  float x[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] = o[i];
-  float t;
-  asm volatile(
-      "v_accvgpr_read_b32 %16, %0\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %0, %16\n\t"
-      "v_accvgpr_read_b32 %16, %1\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %1, %16\n\t"
-      "v_accvgpr_read_b32 %16, %2\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %2, %16\n\t"
-      "v_accvgpr_read_b32 %16, %3\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %3, %16\n\t"
-      "v_accvgpr_read_b32 %16, %4\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %4, %16\n\t"
-      "v_accvgpr_read_b32 %16, %5\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %5, %16\n\t"
-      "v_accvgpr_read_b32 %16, %6\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %6, %16\n\t"
-      "v_accvgpr_read_b32 %16, %7\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %7, %16\n\t"
-      "v_accvgpr_read_b32 %16, %8\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %8, %16\n\t"
-      "v_accvgpr_read_b32 %16, %9\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %9, %16\n\t"
-      "v_accvgpr_read_b32 %16, %10\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %10, %16\n\t"
-      "v_accvgpr_read_b32 %16, %11\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %11, %16\n\t"
-      "v_accvgpr_read_b32 %16, %12\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %12, %16\n\t"
-      "v_accvgpr_read_b32 %16, %13\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %13, %16\n\t"
-      "v_accvgpr_read_b32 %16, %14\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %14, %16\n\t"
-      "v_accvgpr_read_b32 %16, %15\n\tv_mul_f32 %16, %16, %17\n\tv_accvgpr_write_b32 %15, %16\n\t"
-      "s_nop 4"
-      : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]), "+a"(x[4]), "+a"(x[5]), "+a"(x[6]), "+a"(x[7]),
-        "+a"(x[8]), "+a"(x[9]), "+a"(x[10]), "+a"(x[11]), "+a"(x[12]), "+a"(x[13]), "+a"(x[14]), "+a"(x[15]),
-        "=&v"(t)
-      : "v"(alpha));
-#pragma unroll
-  for (int i = 0; i < 16; ++i) o[i] = x[i];
-}
-
 // transposed 4 x 16-bit LDS read: in each 16-lane group, lane i receives
 // element i%4 of the 8-byte reads of lanes i/4 + 4e (e = 0..3)
 __device__ __forceinline__ u32x2 lds_tr16(const uint16_t* p) {
@@ -114,7 +85,7 @@ __device__ __forceinline__ u32x2 lds_tr16(const uint16_t* p) {
 // POW2: the workspace page size is a power of two (page and offset of a key
 // by shift and mask instead of a division)
 template <bool POW2>
-__global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a) {
+__global__ void __launch_bounds__(XTHREADS, 1) extend_attn_kernel(const ExtendArgs a) {
   const int nwg = gridDim.x;  // a multiple of 8
   const int work = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
   if (work >= a.n_work) return;
@@ -135,12 +106,12 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = lane & 31, hh = lane >> 5;
-  // this lane's query rows: 64 wave + 32 rb + j for row blocks rb = 0, 1
-  int tok[2], head[2];
-  bool rv[2];
+  // this lane's query rows: 32 XRB wave + 32 rb + j for its XRB row blocks
+  int tok[XRB], head[XRB];
+  bool rv[XRB];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
-    const int row = 64 * wave + 32 * rb + j;
+  for (int rb = 0; rb < XRB; ++rb) {
+    const int row = 32 * XRB * wave + 32 * rb + j;
     tok[rb] = t0 + row / G;
     head[rb] = kvh * G + row % G;
     rv[rb] = tok[rb] < C;
@@ -148,9 +119,9 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
 
   // Q^T operands: lane (row, half hh) holds d = 16 ks + 8 hh .. + 7 (zero for
   // rows past the chunk: their scores are 0 and their outputs not written)
-  bf16x8 qf[2][XD / 16];
+  bf16x8 qf[XRB][XD / 16];
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < XRB; ++rb) {
     const uint16_t* qp = a.q + ((int64_t)(q0 + (rv[rb] ? tok[rb] : 0)) * a.hq + head[rb]) * XD + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < XD / 16; ++ks) {
@@ -175,13 +146,13 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
   const int ckey = tid >> 4, ccol = 8 * (tid & 15);
   const int pshift = __builtin_ctz(P);  // used when P is a power of two
   const int64_t crow = (int64_t)a.hkv * XD;  // elements between consecutive chunk tokens
-  uint4 rk[4], rvv[4];
+  uint4 rk[XCI], rvv[XCI];
   auto load_block = [&](int kb) {
     if (kb < nb0) {
       const bool full = (kb + 1) * XKB <= L0;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int t = kb * XKB + pkey + 32 * i;
+      for (int i = 0; i < XPI; ++i) {
+        const int t = kb * XKB + pkey + (XTHREADS / 8) * i;
         const int pg = POW2 ? (t >> pshift) : t / P;
         const int off = t - pg * P;
         const int64_t r = ((int64_t)(po + pg) * a.hkv + kvh) * P + off;
@@ -195,16 +166,17 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
           rvv[i] = t < L0 ? *vp : make_uint4(0, 0, 0, 0);
         }
       }
-      rk[2] = rk[3] = rvv[2] = rvv[3] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = XPI; i < XCI; ++i) rk[i] = rvv[i] = make_uint4(0, 0, 0, 0);
     } else {
       const int tb = (kb - nb0) * XKB;
       const bool full = tb + XKB <= C;
       const int64_t e0 = (int64_t)(q0 + tb + ckey) * crow + (int64_t)kvh * XD + ccol;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = tb + ckey + 16 * i;
-        const uint4* kp = reinterpret_cast<const uint4*>(a.k_new + e0 + 16 * i * crow);
-        const uint4* vp = reinterpret_cast<const uint4*>(a.v_new + e0 + 16 * i * crow);
+      for (int i = 0; i < XCI; ++i) {
+        const int t = tb + ckey + (XTHREADS / 16) * i;
+        const uint4* kp = reinterpret_cast<const uint4*>(a.k_new + e0 + (XTHREADS / 16) * i * crow);
+        const uint4* vp = reinterpret_cast<const uint4*>(a.v_new + e0 + (XTHREADS / 16) * i * crow);
         if (full) {
           rk[i] = *kp;
           rvv[i] = *vp;
@@ -220,8 +192,8 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
   auto store_block = [&](int kb, uint16_t* kd, uint16_t* vd) {
     if (kb < nb0) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int c = tid + 256 * i, key = c >> 3, dc = c & 7;
+      for (int i = 0; i < XPI; ++i) {
+        const int c = tid + XTHREADS * i, key = c >> 3, dc = c & 7;
         const uint4 k = rk[i], v = rvv[i];
         const uint4 k0 = {fp8x2_to_bf16x2<KVQ_FP8_E4M3, false>(k.x), fp8x2_to_bf16x2<KVQ_FP8_E4M3, true>(k.x),
                           fp8x2_to_bf16x2<KVQ_FP8_E4M3, false>(k.y), fp8x2_to_bf16x2<KVQ_FP8_E4M3, true>(k.y)};
@@ -238,8 +210,8 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = tid + 256 * i, key = c >> 4, dc = c & 15;
+      for (int i = 0; i < XCI; ++i) {
+        const int c = tid + XTHREADS * i, key = c >> 4, dc = c & 15;
         *reinterpret_cast<uint4*>(kd + key * XK_STRIDE + 8 * dc) = rk[i];
         *reinterpret_cast<uint4*>(vd + key * XV_STRIDE + 8 * dc) = rvv[i];
       }
@@ -249,14 +221,19 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
   const float sm2 = a.sm_scale * kXLog2e;
   const float skv = a.s_k ? a.s_k[0] : 1.0f;
   const float svv = a.s_v ? a.s_v[0] : 1.0f;
-  f32x16 o[2][XD / 32];  // O^T per row block: elements 32 dt .. +31 x 32 rows
+  f32x16 o[XRB][XD / 32];  // O^T per row block: elements 32 dt .. +31 x 32 rows
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb)
+  for (int rb = 0; rb < XRB; ++rb)
 #pragma unroll
     for (int dt = 0; dt < XD / 32; ++dt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) o[rb][dt][v] = 0.f;
-  float m_ref[2] = {kXNegInf, kXNegInf}, l_run[2] = {0.f, 0.f};
+  float m_ref[XRB], l_run[XRB];
+#pragma unroll
+  for (int rb = 0; rb < XRB; ++rb) {
+    m_ref[rb] = kXNegInf;
+    l_run[rb] = 0.f;
+  }
   // transposed-read lane address: lane 4e + c of each 16-lane group reads key
   // row 4 hh + e, elements 16 ((lane >> 4) & 1) + 4 c (+ 32 dt)
   const int v_lane = (4 * hh + ((lane & 15) >> 2)) * XV_STRIDE + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
@@ -270,13 +247,13 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
     constexpr bool MASK = decltype(mask_tag)::value;
     const uint16_t* kd = sk[kb & 1];
     const uint16_t* vd = sv[kb & 1];
-    // scores for the 64 keys, both row blocks: tile kt holds keys
+    // scores for the 64 keys, every row block: tile kt holds keys
     // 32 kt + 8 (v/4) + 4 hh + v%4. Each K fragment (read three products
-    // ahead) serves the two row blocks; every product is fenced from the
+    // ahead) serves all row blocks; every product is fenced from the
     // scheduler, which would otherwise hoist all operand reads and spill.
-    f32x16 acc[2][2];
+    f32x16 acc[XRB][2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < XRB; ++rb)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -293,19 +270,20 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
       for (int i = 0; i < 2 * (XD / 16); ++i) {
         if (i + kDepth - 1 < 2 * (XD / 16)) ka[(i + kDepth - 1) % kDepth] = kread(i + kDepth - 1);
         const int kt = i & 1, ks = i >> 1;
-        acc[0][kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i % kDepth], qf[0][ks], acc[0][kt], 0, 0, 0);
-        acc[1][kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i % kDepth], qf[1][ks], acc[1][kt], 0, 0, 0);
+#pragma unroll
+        for (int rb = 0; rb < XRB; ++rb)
+          acc[rb][kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i % kDepth], qf[rb][ks], acc[rb][kt], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     const float scl = PRE ? sm2 * skv : sm2;  // > 0: the maximum commutes with it
-    // P of both row blocks in the B-operand layout of the four 16-key PV
+    // P of every row block in the B-operand layout of the four 16-key PV
     // steps (fp16 for the prefix, bf16 hi + lo for the chunk)
-    u32x4 ph[2][4], pl[2][4];
+    u32x4 ph[XRB][4], pl[XRB][4];
     bool move_any = false;
-    float alpha[2];
+    float alpha[XRB];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
+    for (int rb = 0; rb < XRB; ++rb) {
       float s[2][16];
       float mx = kXNegInf;
       if constexpr (MASK) {
@@ -360,12 +338,12 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
     }
     if (__builtin_amdgcn_ballot_w64(move_any) != 0ull) {  // rare after the first blocks
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < XRB; ++rb)
 #pragma unroll
-        for (int dt = 0; dt < XD / 32; ++dt) scale_acc(o[rb][dt], alpha[rb]);
+        for (int dt = 0; dt < XD / 32; ++dt) o[rb][dt] *= alpha[rb];
     }
     // O^T += V^T P^T, 16 keys per step; each V^T fragment (read two products
-    // ahead) serves both row blocks
+    // ahead) serves all row blocks
     {
       constexpr int kVDepth = 3;
       auto vread = [&](int i) {  // i = 4 stp + dt
@@ -381,7 +359,7 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
         if (i + kVDepth - 1 < 16) va[(i + kVDepth - 1) % kVDepth] = vread(i + kVDepth - 1);
         const int stp = i >> 2, dt = i & 3;
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
+        for (int rb = 0; rb < XRB; ++rb) {
           if constexpr (PRE) {
             o[rb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va[i % kVDepth]),
                                                                __builtin_bit_cast(f16x8, ph[rb][stp]), o[rb][dt], 0, 0, 0);
@@ -415,9 +393,9 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
   if (nb0 > nfull0) block(T{}, T{}, nb0 - 1);
   if (nb0 > 0) {  // the prefix values carry the workspace V scale
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < XRB; ++rb)
 #pragma unroll
-      for (int dt = 0; dt < XD / 32; ++dt) scale_acc(o[rb][dt], svv);
+      for (int dt = 0; dt < XD / 32; ++dt) o[rb][dt] *= svv;
   }
   // chunk: blocks whose keys all precede the tile's first token and lie in
   // the chunk need no mask, the rest (the diagonal) do
@@ -427,7 +405,7 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
   for (int kb = nb0 + nfree; kb < nb; ++kb) block(F{}, T{}, kb);
 
 #pragma unroll
-  for (int rb = 0; rb < 2; ++rb) {
+  for (int rb = 0; rb < XRB; ++rb) {
     const float lr = l_run[rb] + shfl_xor_f32(l_run[rb], 32);
     if (rv[rb]) {
       const float inv = lr > 0.f ? 1.0f / lr : 0.f;
@@ -453,8 +431,8 @@ __global__ void __launch_bounds__(256, 1) extend_attn_kernel(const ExtendArgs a)
 hipError_t kvq_launch_extend(const ExtendArgs& a, hipStream_t s) {
   const int64_t nwg = (a.n_work + 7) / 8 * 8;
   if ((a.page_size & (a.page_size - 1)) == 0)
-    kvq::extend_attn_kernel<true><<<(unsigned)nwg, 256, 0, s>>>(a);
+    kvq::extend_attn_kernel<true><<<(unsigned)nwg, kvq::XTHREADS, 0, s>>>(a);
   else
-    kvq::extend_attn_kernel<false><<<(unsigned)nwg, 256, 0, s>>>(a);
+    kvq::extend_attn_kernel<false><<<(unsigned)nwg, kvq::XTHREADS, 0, s>>>(a);
   return hipGetLastError();
 }
