@@ -33,15 +33,17 @@ PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, vendor figure
 
 
 def measured_traffic(w, op="decode", fp8q=False):
-    """HBM bytes per launch of the decode (op "decode") or dequantize_prev_kv
-    (op "dequant_prev") kernel from the committed rocprofv3 counter runs, or
-    None when no measurement exists for this workload or the kernel's sources
-    changed since it was taken."""
+    """HBM bytes per launch of the decode (op "decode"), dequantize_prev_kv
+    (op "dequant_prev") or extend attention (op "extend") kernel from the
+    committed rocprofv3 counter runs, or None when no measurement exists for
+    this workload or the kernel's sources changed since it was taken."""
     import hashlib
     if op == "decode":
         kind = "gqa" if w.kind == "gqa" else "mla"
         mode = {"amax_head": "_head", "kivi": "_kivi"}.get(w.scale_mode, "") + ("_fp8q" if fp8q else "")
         path = os.path.join(ROOT, "profiles", f"kvq_decode_{kind}_{w.name}_{w.dtype}{mode}_traffic.json")
+    elif op == "extend":
+        path = os.path.join(ROOT, "profiles", f"kvq_extend_attn_{w.name}_traffic.json")
     else:
         path = os.path.join(ROOT, "profiles", f"kvq_dequant_prev_{w.dtype}_{w.name}_traffic.json")
     if not os.path.exists(path):
@@ -440,7 +442,8 @@ def bench_extend(w, args, dev):
                                f"(scales 0.05), chunk K/V BF16, causal within the chunk",
                    "algorithmic_flops_per_step": fl},
         "roofline": {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / PEAK_F16_TFLOPS, 4), "traffic": None,
+                     "frac": round(ach / PEAK_F16_TFLOPS, 4), "traffic": measured_traffic(w, "extend"),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
                      "kernel": "extend_attn_kernel (bf16 / fp16 MFMA)", "kernel_ms": round(ext_ms, 4)},
         "kernel_ms": {"extend": round(ext_ms, 4), "dequant_prev": round(dq_ms, 4), "store": round(sto_ms, 4)},
     }
