@@ -231,6 +231,19 @@ def cpu_baseline(w, seconds_hint=20.0, fp8q=False):
     else:
         decode_attention(oc, q, table, lens, I.sm_scale(w), ks, vs, batch_ids=[b])
     t_dec = time.perf_counter() - t0
+    # the same decode with one host thread (BLAS limited to 1), reported beside
+    t1 = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            if fp8q:
+                decode_attention_fp8q(oc, q, table, lens, I.sm_scale(w), qs, ks, vs, batch_ids=[b])
+            else:
+                decode_attention(oc, q, table, lens, I.sm_scale(w), ks, vs, batch_ids=[b])
+            t1 = time.perf_counter() - t0
+    except ImportError:
+        pass
     rows = 2 * w.kv_heads if w.kind == "gqa" else 1
     bits = 8.0 if w.dtype in ("e4m3", "e5m2") else 4.5
     nbytes = L * rows * w.head_dim * bits / 8
@@ -244,7 +257,9 @@ def cpu_baseline(w, seconds_hint=20.0, fp8q=False):
             "sample": f"sequence {b} of {w.batch} ({L} tokens, all {w.kv_heads} KV heads): float64 oracle "
                       f"dequant + attention {t_dec:.2f} s; its quantize-and-store of the same tokens "
                       f"{t_codec:.2f} s (not in value)",
-            "decode_s": round(t_dec, 3), "codec_s": round(t_codec, 3)}
+            "decode_s": round(t_dec, 3), "codec_s": round(t_codec, 3),
+            "value_1_thread": None if t1 is None else round(nbytes / t1 / 1e9, 4),
+            "decode_s_1_thread": None if t1 is None else round(t1, 3)}
 
 
 def dequant_prev_cpu_baseline(w, n_pages=None):
