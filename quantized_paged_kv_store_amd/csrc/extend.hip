@@ -242,9 +242,23 @@ __global__ void __launch_bounds__(XTHREADS, 1) extend_attn_kernel(const ExtendAr
   // lo PV); MASK: the block reaches past the prefix end, the chunk end or the
   // tile's diagonal. The four variants are separate code, so the accumulators
   // never cross a branch.
+  // the next block into the other buffer (last read by the previous block's
+  // math, which every wave finished before the last barrier), then the loads
+  // of the block after. Within one barrier interval a wave must do this and
+  // block kb's math in either order; the second half of the waves stages
+  // first, so the two waves sharing a SIMD run their matrix and vector
+  // phases against each other instead of in step.
+  const bool stage_first = __builtin_amdgcn_readfirstlane(wave) >= XWAVES / 2;
+  auto stage_next = [&](int kb) {
+    if (kb + 1 < nb) {
+      store_block(kb + 1, sk[(kb + 1) & 1], sv[(kb + 1) & 1]);
+      if (kb + 2 < nb) load_block(kb + 2);
+    }
+  };
   auto block = [&](auto pre_tag, auto mask_tag, int kb) {
     constexpr bool PRE = decltype(pre_tag)::value;
     constexpr bool MASK = decltype(mask_tag)::value;
+    if (stage_first) stage_next(kb);
     const uint16_t* kd = sk[kb & 1];
     const uint16_t* vd = sv[kb & 1];
     // scores for the 64 keys, every row block: tile kt holds keys
@@ -372,12 +386,7 @@ __global__ void __launch_bounds__(XTHREADS, 1) extend_attn_kernel(const ExtendAr
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // the next block into the other buffer (last read by the previous
-    // block's math, which every wave finished before the last barrier)
-    if (kb + 1 < nb) {
-      store_block(kb + 1, sk[(kb + 1) & 1], sv[(kb + 1) & 1]);
-      if (kb + 2 < nb) load_block(kb + 2);
-    }
+    if (!stage_first) stage_next(kb);
     __syncthreads();
   };
 
