@@ -134,8 +134,10 @@ __global__ void __launch_bounds__(XTHREADS, 1) extend_attn_kernel(const ExtendAr
   const int tl = min(t0 + TT, C) - 1;  // last chunk token of this tile
   const int nb = nb0 + tl / XKB + 1;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sk[2][XKB * XK_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t sv[2][XKB * XV_STRIDE];
+  // four block buffers: block kb lives in buffer kb % 4, staged two blocks
+  // ahead, and the workgroup meets at a barrier after every odd block
+  __shared__ __attribute__((aligned(16))) uint16_t sk[4][XKB * XK_STRIDE];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[4][XKB * XV_STRIDE];
 
   // global -> registers: a prefix block is 2 + 2 E4M3 chunks of 16 bytes
   // (16 elements) per thread, a chunk block 4 + 4 BF16 chunks (8 elements);
@@ -242,25 +244,25 @@ __global__ void __launch_bounds__(XTHREADS, 1) extend_attn_kernel(const ExtendAr
   // lo PV); MASK: the block reaches past the prefix end, the chunk end or the
   // tile's diagonal. The four variants are separate code, so the accumulators
   // never cross a branch.
-  // the next block into the other buffer (last read by the previous block's
-  // math, which every wave finished before the last barrier), then the loads
-  // of the block after. Within one barrier interval a wave must do this and
-  // block kb's math in either order; the second half of the waves stages
-  // first, so the two waves sharing a SIMD run their matrix and vector
-  // phases against each other instead of in step.
+  // block kb + 2 into its buffer (last read by block kb - 2, which every
+  // wave finished before the last barrier; read again after the next
+  // barrier), then the loads of block kb + 3. A wave may do this before or
+  // after block kb's math; the second half of the waves stages first, so the
+  // two waves sharing a SIMD run their matrix and vector phases against each
+  // other instead of in step.
   const bool stage_first = __builtin_amdgcn_readfirstlane(wave) >= XWAVES / 2;
   auto stage_next = [&](int kb) {
-    if (kb + 1 < nb) {
-      store_block(kb + 1, sk[(kb + 1) & 1], sv[(kb + 1) & 1]);
-      if (kb + 2 < nb) load_block(kb + 2);
+    if (kb + 2 < nb) {
+      store_block(kb + 2, sk[(kb + 2) & 3], sv[(kb + 2) & 3]);
+      if (kb + 3 < nb) load_block(kb + 3);
     }
   };
   auto block = [&](auto pre_tag, auto mask_tag, int kb) {
     constexpr bool PRE = decltype(pre_tag)::value;
     constexpr bool MASK = decltype(mask_tag)::value;
     if (stage_first) stage_next(kb);
-    const uint16_t* kd = sk[kb & 1];
-    const uint16_t* vd = sv[kb & 1];
+    const uint16_t* kd = sk[kb & 3];
+    const uint16_t* vd = sv[kb & 3];
     // scores for the 64 keys, every row block: tile kt holds keys
     // 32 kt + 8 (v/4) + 4 hh + v%4. Each K fragment (read three products
     // ahead) serves all row blocks; every product is fenced from the
@@ -387,12 +389,16 @@ __global__ void __launch_bounds__(XTHREADS, 1) extend_attn_kernel(const ExtendAr
       }
     }
     if (!stage_first) stage_next(kb);
-    __syncthreads();
+    if (kb & 1) __syncthreads();  // uniform: every wave runs the same blocks
   };
 
   load_block(0);
   store_block(0, sk[0], sv[0]);
-  if (nb > 1) load_block(1);
+  if (nb > 1) {
+    load_block(1);
+    store_block(1, sk[1], sv[1]);
+    if (nb > 2) load_block(2);
+  }
   __syncthreads();
   using T = std::true_type;
   using F = std::false_type;
