@@ -18,8 +18,9 @@
 // prefix, which then stays in that XCD's L2.
 //
 // Per 64-key block, staged in LDS (K and V row-major, K as bf16, V as fp16
-// codes for the prefix and bf16 values for the chunk; two buffers, the next
-// block converted and stored while the current one is used):
+// codes for the prefix and bf16 values for the chunk; four buffers, a block
+// converted and stored two blocks before it is used, one workgroup barrier
+// per two blocks):
 //   S^T[key][row]  = K[key][:] . Q^T[:][row]   v_mfma_f32_32x32x16_bf16
 //                    (E4M3 codes and BF16 values are exact in bf16; s_k and
 //                    sm_scale multiply the scores)
