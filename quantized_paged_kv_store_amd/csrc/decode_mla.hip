@@ -22,7 +22,8 @@
 // wave w owns heads 32w..32w+31 outright, with their query in VGPRs (144)
 // and their whole O^T (512 x 32 fp32) in the AGPRs, so its scores, softmax
 // and PV need nothing from the other waves. A step covers 32 tokens (two
-// 16-token tiles) and the K^ tile is double-buffered in LDS; per step, wave w
+// 16-token tiles); the K^ tile has four LDS buffers, a step dequantized two
+// steps before it is used; per step, wave w
 //   1. scores its 32 heads against the 32 tokens over the full dot product
 //      (36 MFMAs, the K^ operand read from the current buffer three
 //      products ahead);
@@ -31,10 +32,10 @@
 //      (V^T: one element, 8 tokens per lane) read straight from the
 //      token-major K^ tile with ds_read_b64_tr_b16, gfx950's transposing LDS
 //      read, so the latent is dequantized once per workgroup;
-//   4. dequantizes its share of the next step (elements [128w, 128w+128) and
-//      a quarter of the rope group) into the other buffer and issues the
-//      loads of the step after;
-// and the workgroup meets at one barrier.
+//   4. dequantizes its share of step st + 2 (elements [128w, 128w+128) and
+//      a quarter of the rope group) into its buffer and issues the loads of
+//      step st + 3;
+// and the workgroup meets at a barrier after every second step.
 #include <type_traits>
 
 #include "store_row.h"
@@ -169,7 +170,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
     return;
   }
 
-  __shared__ __attribute__((aligned(16))) uint8_t sm_k[2 * kBuf];
+  __shared__ __attribute__((aligned(16))) uint8_t sm_k[4 * kBuf];
   __shared__ int sm_pg[kMlaMaxSplitPages];
 
   const int tpp = a.page_size / kTile;
@@ -354,25 +355,32 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
   // static.
   const int nsteps = (t_end - t_begin + kStepTiles - 1) / kStepTiles;
   Step R;
-  issue(R);
-  int tA_c = R.tA, ok_c = R.ok;
-  {
+  auto dequant_all = [&](uint8_t* buf) {
     auto all_chunks = [&](auto tail_tag) {
 #pragma unroll
-      for (int c = 0; c < 6; ++c) dequant_chunk(R, sm_k, c, tail_tag);
+      for (int c = 0; c < 6; ++c) dequant_chunk(R, buf, c, tail_tag);
     };
-    if (is_tail(tA_c, ok_c))
+    if (is_tail(R.tA, R.ok))
       all_chunks(std::true_type{});
     else
       all_chunks(std::false_type{});
-  }
+  };
+  // steps 0 and 1 into buffers 0 and 1; step 2's loads in flight
+  issue(R);
+  int tA_c = R.tA, ok_c = R.ok;
+  dequant_all(sm_k);
+  issue(R);
+  int tA_1 = R.tA, ok_1 = R.ok;
+  dequant_all(sm_k + kBuf);
   issue(R);
   __syncthreads();
 
+  // Step st is read from buffer st % 4 while step st + 2 is dequantized into
+  // buffer (st + 2) % 4 (last read by step st - 2, which every wave finished
+  // before the last barrier); the workgroup meets after every odd step.
   for (int st = 0; st < nsteps; ++st) {
-    const uint8_t* kb = sm_k + (st & 1) * kBuf;
-    uint8_t* nb = sm_k + ((st & 1) ^ 1) * kBuf;
-    const int tA_n = R.tA, ok_n = R.ok;
+    const uint8_t* kb = sm_k + (st & 3) * kBuf;
+    uint8_t* nb = sm_k + ((st + 2) & 3) * kBuf;
 
     // 1. S^T[token i][head h0 + r32] over all 576 elements from buffer kb,
     //    the K^ operand read three products ahead. Every product (here and
@@ -468,21 +476,15 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // 4. the next step into buffer nb, then the loads of the step after
-    {
-      auto all_chunks = [&](auto tail_tag) {
-#pragma unroll
-        for (int c = 0; c < 6; ++c) dequant_chunk(R, nb, c, tail_tag);
-      };
-      if (is_tail(tA_n, ok_n))
-        all_chunks(std::true_type{});
-      else
-        all_chunks(std::false_type{});
-    }
+    // 4. step st + 2 into buffer nb, then the loads of step st + 3
+    const int tA_2 = R.tA, ok_2 = R.ok;
+    dequant_all(nb);
     issue(R);
-    __syncthreads();  // buffer kb is rewritten by the next step's dequantization
-    tA_c = tA_n;
-    ok_c = ok_n;
+    if (st & 1) __syncthreads();  // uniform: every wave runs the same steps
+    tA_c = tA_1;
+    ok_c = ok_1;
+    tA_1 = tA_2;
+    ok_1 = ok_2;
   }
 
   // ---- epilogue: normalize and write this split's partial (or the output) ----
