@@ -191,6 +191,24 @@ def test_mla_decode_argument_errors(handles):
     assert lib.kvq_decode_workspace_bytes(h["mla"], 2, 16, 1000) > 0
 
 
+def test_split_plan_cap(handles, monkeypatch):
+    """Aimed at far more workgroups than one sequence has tiles, the planners
+    stop at 128 splits: GQA 40,000 tokens = 2,500 tiles -> 157 splits of 16
+    tiles, capped to 128, re-tiled at 20 tiles = 125 splits; MLA 8,192 tokens
+    = 512 tiles -> 256 two-tile splits, capped to 128 of 4 tiles. The
+    workspace is splits x (Dv + 1) floats per (sequence, head), each part
+    rounded up to 256 bytes."""
+    lib, h = handles
+    monkeypatch.setenv("KVQ_DECODE_TARGET_WGS", "100000")
+    up = lambda x: (x + 255) // 256 * 256
+    assert lib.kvq_decode_workspace_bytes(h["fp8"], 1, 8, 40000) == up(8 * 125 * 128 * 4) + up(8 * 125 * 4)
+    assert lib.kvq_decode_workspace_bytes(h["mla"], 1, 16, 8192) == up(16 * 128 * 512 * 4) + up(16 * 128 * 4)
+    monkeypatch.setenv("KVQ_DECODE_TARGET_WGS", "1")
+    # one split per sequence when it fits (no workspace); 1,024 tiles per GQA split at most
+    assert lib.kvq_decode_workspace_bytes(h["fp8"], 1, 8, 16384) == 0
+    assert lib.kvq_decode_workspace_bytes(h["fp8"], 1, 8, 40000) == up(8 * 3 * 128 * 4) + up(8 * 3 * 4)
+
+
 def test_decode_append_argument_errors(handles):
     lib, h = handles
     P = c_void_p(FAKE_DEV)

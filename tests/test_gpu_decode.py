@@ -80,6 +80,46 @@ def test_split_count_invariance():
         assert rel_l2(o, outs[0][0]) < 3e-4 and np.allclose(l, outs[0][1], atol=1e-5)
 
 
+def _decode_at_target(c, w, target):
+    """kvq_decode with the split planner aimed at `target` workgroups; also
+    returns the workspace size that plan needs."""
+    os.environ["KVQ_DECODE_TARGET_WGS"] = target
+    try:
+        ws = K.kvq_decode_workspace_bytes(c.cache, len(c.lens), w.q_heads, c.max_len)
+        o, l = K.kvq_decode(c.cache, c.q_dev, c.table_dev, c.lens_dev, c.max_len, I.sm_scale(w),
+                            c.k_scale, c.v_scale)
+        torch.cuda.synchronize()
+        return o, l, ws
+    finally:
+        del os.environ["KVQ_DECODE_TARGET_WGS"]
+
+
+@pytest.mark.parametrize("kind", ["gqa", "mla"])
+def test_many_splits_merge(kind):
+    """More than 64 splits of one sequence (the merge then holds two split
+    LSEs per lane) up to the planners' cap of 128: GQA, 40,000 tokens at
+    16-token tiles (125 splits); MLA, 8,192 tokens at 32-token steps (128
+    splits). Checked against the oracle and against a launch with a few long
+    splits, which differs only by each split's own fp16 rounding of p."""
+    if kind == "gqa":
+        w = I.WORKLOADS["llama3_8b"].with_(batch=1, max_len=40000, min_len=40000)
+        c = Case(w).run_gpu(decode=False)
+    else:
+        w = I.Workload("mla-splits", "nvfp4", "mla", 1, 16, 1, 576, 512, 64, 8192, 0, 1, "mla", seed=11)
+        c = Case(w, lens=[8192]).run_gpu(decode=False)
+    dv = c.cache.desc.v_dim
+    o_many, l_many, ws_many = _decode_at_target(c, w, "100000")
+    o_few, l_few, _ = _decode_at_target(c, w, "1")
+    # workspace = splits x (dv + 1) floats per (sequence, head), two 256-byte alignments
+    assert ws_many > 64 * w.q_heads * (dv + 1) * 4 + 512, ws_many
+    assert ws_many <= 128 * w.q_heads * (dv + 1) * 4 + 512, ws_many
+    c.out, c.lse = o_many, l_many
+    _check(c, [0], f"{kind} many splits")
+    assert rel_l2(o_many.cpu().numpy(), o_few.cpu().numpy()) < 3e-4
+    # fp32 sums of unrounded weights over differently placed splits: the oracle's LSE bound
+    assert np.allclose(l_many.cpu().numpy(), l_few.cpu().numpy(), rtol=0, atol=1e-4)
+
+
 def test_llama3_8b_decode_sampled():
     """The benchmark workload at full size (batch 8, 20,480 tokens, FP8 E4M3,
     launch configuration as timed); oracle on sequences 0 and 5."""
