@@ -120,6 +120,38 @@ def test_many_splits_merge(kind):
     assert np.allclose(l_many.cpu().numpy(), l_few.cpu().numpy(), rtol=0, atol=1e-4)
 
 
+def test_max_length_property():
+    """The longest context decode accepts: 2,097,152 tokens = 128 splits of
+    1,024 tiles. Every K row is the same, so the softmax weights are uniform;
+    V cycles through 7 rows. Then out = the count-weighted mean of the 7
+    dequantized V rows and LSE = sm_scale q.k^ + ln L, both from the oracle's
+    quantizer on those rows only; a lost or repeated tile moves the LSE."""
+    from oracle import quantize as Q
+    from oracle.formats import E4M3
+    L, P = 128 * 1024 * 16, 16
+    w = I.Workload("maxlen", "e4m3", "gqa", 1, 4, 1, 128, 128, P, L, L, 0, "llama", seed=12)
+    rng = np.random.default_rng(12)
+    k0 = I.bf16_bits(rng.standard_normal(128).astype(np.float32))
+    v7 = I.bf16_bits(rng.standard_normal((7, 128)).astype(np.float32))
+    c = Case(w, lens=[L])
+    t = np.arange(L)
+    kp = np.broadcast_to(k0, (L, 1, 128)).copy()   # rows [n, Hkv, D]
+    vp = v7[t % 7][:, None, :]
+    c.data = {"pre": (kp, vp, I.slots_for(c.table[0], t, P)), "new": (None, None, np.zeros(0, np.int64))}
+    c.run_gpu()
+    assert K.kvq_decode_workspace_bytes(c.cache, 1, 4, L) == 4 * 128 * (128 + 1) * 4  # 128 splits
+    ks, vs = c.oracle_scales()
+    khat = Q.dequantize_fp8(Q.quantize_fp8(I.bf16_to_f32(k0).astype(np.float64), ks, E4M3), ks, E4M3)
+    vhat = Q.dequantize_fp8(Q.quantize_fp8(I.bf16_to_f32(v7).astype(np.float64), vs, E4M3), vs, E4M3)
+    counts = np.bincount(t % 7, minlength=7).astype(np.float64)
+    want = counts @ vhat / L
+    q = I.bf16_to_f32(c.q[0]).astype(np.float64)
+    want_lse = I.sm_scale(w) * (q @ khat) + np.log(L)
+    got, glse = c.out.cpu().numpy()[0], c.lse.cpu().numpy()[0]
+    assert np.allclose(got, want[None, :], rtol=1e-5, atol=1e-6), np.abs(got - want).max()
+    assert np.allclose(glse, want_lse, rtol=0, atol=1e-4), (glse, want_lse)
+
+
 def test_llama3_8b_decode_sampled():
     """The benchmark workload at full size (batch 8, 20,480 tokens, FP8 E4M3,
     launch configuration as timed); oracle on sequences 0 and 5."""
