@@ -152,6 +152,38 @@ def test_max_length_property():
     assert np.allclose(glse, want_lse, rtol=0, atol=1e-4), (glse, want_lse)
 
 
+def test_mla_max_length_property():
+    """MLA at the longest accepted context (2,097,152 tokens, 128 splits of
+    256 pages of 64). The query's first 512 dims are zero and every latent row
+    has the same rope dims, so the weights are uniform while the value part
+    (dims 0..511) cycles through 7 rows: out = their count-weighted mean after
+    NVFP4 rounding, LSE = sm_scale q_rope.k^_rope + ln L (the oracle's
+    quantizer on the 7 rows; the rope dims are whole 16-element blocks)."""
+    from oracle import quantize as Q
+    L, P = 128 * 1024 * 16, 64
+    w = I.Workload("mla-maxlen", "nvfp4", "mla", 1, 16, 1, 576, 512, P, L, L, 0, "mla", seed=13)
+    rng = np.random.default_rng(13)
+    rows = I.bf16_bits(np.concatenate([rng.standard_normal((7, 512)), np.tile(rng.standard_normal(64), (7, 1))],
+                                      axis=1).astype(np.float32))
+    c = Case(w, lens=[L])
+    t = np.arange(L)
+    c.data = {"pre": (rows[t % 7], None, I.slots_for(c.table[0], t, P)), "new": (None, None, np.zeros(0, np.int64))}
+    c.run_gpu(decode=False)
+    qz = c.q.copy()
+    qz[..., :512] = 0
+    o, l = K.kvq_decode(c.cache, c._bf16(qz), c.table_dev, c.lens_dev, L, I.sm_scale(w), c.k_scale, None)
+    torch.cuda.synchronize()
+    g, _ = c.oracle_scales()
+    lat = Q.dequantize_nvfp4(*Q.quantize_nvfp4(I.bf16_to_f32(rows).astype(np.float64), g), g)
+    counts = np.bincount(t % 7, minlength=7).astype(np.float64)
+    want = counts @ lat[:, :512] / L
+    q = I.bf16_to_f32(qz[0]).astype(np.float64)
+    want_lse = I.sm_scale(w) * (q[:, 512:] @ lat[0, 512:]) + np.log(L)
+    got, glse = o.cpu().numpy()[0], l.cpu().numpy()[0]
+    assert np.allclose(got, want[None, :], rtol=1e-5, atol=1e-6), np.abs(got - want).max()
+    assert np.allclose(glse, want_lse, rtol=0, atol=1e-4), (glse, want_lse)
+
+
 def test_llama3_8b_decode_sampled():
     """The benchmark workload at full size (batch 8, 20,480 tokens, FP8 E4M3,
     launch configuration as timed); oracle on sequences 0 and 5."""
