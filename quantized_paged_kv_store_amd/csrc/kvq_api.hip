@@ -1,6 +1,5 @@
 // C ABI of libkvq: argument validation, cache layout, split planning and
 // kernel launches. Every check happens before anything is enqueued.
-#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -10,12 +9,19 @@
 #include <vector>
 
 #include "kvq_internal.h"
+#include "kvq_testing.h"
 
 namespace {
 
 constexpr size_t kAlign = 256;
 constexpr size_t kScratchBytes = kvq::kAmaxBlocks * sizeof(unsigned);
 constexpr int kMaxDecodeLen = 128 * 1024 * kvq::kTile;  // 128 splits x 1024 tiles
+// Default split-planner targets (workgroups per decode launch), from same-box
+// sweeps on the 8B-shape FP8 and Qwen3-shape FP4 steps (GQA) and the
+// DeepSeek-R1-shape step (MLA: one workgroup per CU).
+constexpr int kGqaTargetWgs = 512;
+constexpr int kMlaTargetWgs = 256;
+constexpr int kMaxTargetWgs = 1 << 20;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -85,14 +91,11 @@ struct SplitPlan {
 // Context split: enough workgroups to fill 256 CUs several times over, each
 // split an even number of 16-token tiles (waves consume tile pairs), at most
 // 1024 tiles per split and 128 splits per sequence (so max_len <= 2M tokens).
-SplitPlan plan_gqa(int batch, int hkv, int max_len) {
+// `target` = workgroups to aim at, 0 = the default.
+SplitPlan plan_gqa(int batch, int hkv, int max_len, int target_wgs) {
   const int ntiles = (max_len + kvq::kTile - 1) / kvq::kTile;
   const int64_t units = (int64_t)batch * hkv;
-  int64_t target = 512;
-  if (const char* e = getenv("KVQ_DECODE_TARGET_WGS")) {
-    const long v = strtol(e, nullptr, 10);
-    if (v >= 1 && v <= (1 << 20)) target = v;
-  }
+  const int64_t target = target_wgs > 0 ? target_wgs : kGqaTargetWgs;
   int64_t tps = units > 0 ? (ntiles * units + target - 1) / target : ntiles;
   if (tps < 16) tps = 16;  // 2 tile pairs per wave at least
   tps = (tps + 1) & ~(int64_t)1;
@@ -112,16 +115,11 @@ SplitPlan plan_gqa(int batch, int hkv, int max_len) {
 // per CU, so the default target is one round of 256 workgroups; each split
 // is an even number of 16-token tiles (whole 32-token steps) whose pages fit
 // the LDS page-id stage.
-SplitPlan plan_mla(int batch, int hq, int max_len, int page_size) {
-  (void)hq;
+SplitPlan plan_mla(int batch, int max_len, int page_size, int target_wgs) {
   const int ntiles = (max_len + kvq::kTile - 1) / kvq::kTile;
   const int tpp = page_size / kvq::kTile;
   const int64_t units = batch;
-  int64_t target = 256;
-  if (const char* e = getenv("KVQ_DECODE_TARGET_WGS")) {
-    const long v = strtol(e, nullptr, 10);
-    if (v >= 1 && v <= (1 << 20)) target = v;
-  }
+  const int64_t target = target_wgs > 0 ? target_wgs : kMlaTargetWgs;
   const int64_t cap = ((int64_t)(kvq::kMlaMaxSplitPages - 1) * tpp) & ~(int64_t)1;
   int64_t tps = units > 0 ? (ntiles * units + target - 1) / target : ntiles;
   if (tps < 2) tps = 2;
@@ -294,6 +292,7 @@ int kvq_alloc_pages(const kvq_cache_desc* d, void* dev_mem, size_t dev_bytes, si
   c->base = static_cast<uint8_t*>(dev_mem);
   c->code_block_bytes = cb;
   c->scale_block_bytes = sb;
+  c->split_target = 0;
   *out = c;
   return KVQ_OK;
 }
@@ -305,6 +304,12 @@ int kvq_cache_layout(const kvq_cache* c, kvq_layout* out) {
 }
 
 void kvq_free_handle(kvq_cache* c) { delete c; }
+
+int kvq_testing_set_split_target(kvq_cache* c, int32_t target_wgs) {
+  if (!c || target_wgs < 0 || target_wgs > kMaxTargetWgs) return KVQ_ERR_ARG;
+  c->split_target = target_wgs;
+  return KVQ_OK;
+}
 
 int kvq_compute_scale(const kvq_cache* c, const void* x0, int64_t n0, const void* x1, int64_t n1, float* scale_out,
                       void* stream) {
@@ -362,9 +367,10 @@ int kvq_store(const kvq_cache* c, const void* k, const void* v, const int64_t* s
 size_t kvq_decode_workspace_bytes(const kvq_cache* c, int32_t batch, int32_t hq, int32_t max_len) {
   if (!c || batch < 0 || hq < 1 || max_len < 0) return 0;
   if (c->desc.kind == KVQ_GQA)
-    return workspace_for(plan_gqa(batch, c->desc.num_kv_heads, max_len), batch, hq, c->desc.v_dim).total;
-  if (hq < 1 || hq > 128) return 0;
-  return workspace_for(plan_mla(batch, hq, max_len, c->desc.page_size), batch, hq, c->desc.v_dim).total;
+    return workspace_for(plan_gqa(batch, c->desc.num_kv_heads, max_len, c->split_target), batch, hq,
+                         c->desc.v_dim).total;
+  if (hq > 128) return 0;
+  return workspace_for(plan_mla(batch, max_len, c->desc.page_size, c->split_target), batch, hq, c->desc.v_dim).total;
 }
 
 namespace {
@@ -389,16 +395,17 @@ int decode_impl(const kvq_cache* c, const void* k_new, const void* v_new, const 
     if (!aligned16(k_new)) return KVQ_ERR_ARG;
     if (d.kind == KVQ_GQA ? (!v_new || !aligned16(v_new)) : v_new != nullptr) return KVQ_ERR_ARG;
   }
+  // the length cap first: it keeps the page count below in range
+  if (max_len > kMaxDecodeLen) return KVQ_ERR_UNSUPPORTED;
   const int P = d.page_size;
   if (page_table_stride < (max_len + P - 1) / P || page_table_stride < 1) return KVQ_ERR_ARG;
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (max_len > kMaxDecodeLen) return KVQ_ERR_UNSUPPORTED;
   if (d.kind == KVQ_GQA) {
     if (hq % d.num_kv_heads) return KVQ_ERR_ARG;
     const int G = hq / d.num_kv_heads;
     if (G > 16) return KVQ_ERR_UNSUPPORTED;
     if (d.scale_mode == KVQ_SCALE_KIVI && (!k_scale || !aligned16(k_scale))) return KVQ_ERR_ARG;
-    const SplitPlan plan = plan_gqa(batch, d.num_kv_heads, max_len);
+    const SplitPlan plan = plan_gqa(batch, d.num_kv_heads, max_len, c->split_target);
     const WsLayout wl = workspace_for(plan, batch, hq, d.v_dim);
     const size_t need = wl.total;
     if (need && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % kAlign)) return KVQ_ERR_SIZE;
@@ -466,7 +473,7 @@ int decode_impl(const kvq_cache* c, const void* k_new, const void* v_new, const 
   // MLA
   if (hq < 1 || hq > 128) return KVQ_ERR_UNSUPPORTED;
   if (!k_scale) return KVQ_ERR_ARG;  // the NVFP4 global scale
-  const SplitPlan plan = plan_mla(batch, hq, max_len, c->desc.page_size);
+  const SplitPlan plan = plan_mla(batch, max_len, c->desc.page_size, c->split_target);
   // pages one split touches, whatever its alignment to page boundaries
   if (mla_split_pages(plan, P) > kvq::kMlaMaxSplitPages) return KVQ_ERR_UNSUPPORTED;
   const WsLayout wl = workspace_for(plan, batch, hq, d.v_dim);

@@ -14,6 +14,7 @@ struct kvq_cache {
   uint8_t* base;             // caller's device memory
   int64_t code_block_bytes;  // bytes of codes per (page, kv head)
   int64_t scale_block_bytes; // bytes of block scales per (page, kv head)
+  int32_t split_target;      // decode workgroups the split planners aim at; 0 = default
 };
 
 namespace kvq {

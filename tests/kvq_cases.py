@@ -90,17 +90,19 @@ class Case:
         return self._to_dev(a).view(torch.bfloat16)
 
     # ------------------------------------------------------------ HIP path --
-    def run_gpu(self, decode=True, append=False):
+    def run_gpu(self, decode=True, append=False, split_target=0):
         """append: the last token of every sequence is not stored separately;
         kvq_decode_append stores it and decodes in one call (one new token per
         sequence required). append without decode leaves those tokens, as
         self.append_rows (device BF16 [B, ...] K and V), to the caller's own
-        append call."""
+        append call. split_target: decode workgroups the split planner aims
+        at (0 = the library default)."""
         w = self.w
         assert not append or w.new_tokens == 1
         self.cache = K.kvq_alloc_pages(w.dtype, w.kind, w.kv_heads, w.head_dim, w.v_dim, w.page_size,
                                        self.npages, device=self.dev, fill=self.fill,
                                        scale_mode=cache_scale_mode(w))
+        K.set_split_target(self.cache, split_target)
         pre = [(b, 0, int(self.prefill[b])) for b in range(w.batch) if self.prefill[b] > 0]
         new = [(b, int(self.prefill[b]), int(self.lens[b])) for b in range(w.batch) if self.lens[b] > self.prefill[b]]
         if self.data is None:

@@ -23,8 +23,8 @@ def _lib():
     return K.library()
 
 
-def _declared():
-    src = open(os.path.join(ROOT, "include", "kvq.h")).read()
+def _declared(header="kvq.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(kvq_\w+)\s*\(", src, flags=re.M)))
 
@@ -38,6 +38,9 @@ def test_exports_every_declared_function():
                           "kvq_profile_read", "kvq_decode_append"}
     for n in names:
         assert hasattr(lib, n), n
+    for header in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        for n in _declared(header):
+            assert hasattr(lib, n), (header, n)
 
 
 def test_status_strings():
@@ -168,6 +171,11 @@ def test_decode_argument_errors(handles):
     bad = list(args(8, 4, 64, None, 0))
     bad[1] = None
     assert lib.kvq_decode(*bad) == ARG
+    # lengths past the 2,097,152-token cap are refused before the page count
+    # ceil(max_len / P) is formed (near INT32_MAX that sum would overflow)
+    assert lib.kvq_decode(*args(8, 1, 2**31 - 1, None, 0)) == UNSUP
+    assert lib.kvq_decode(*args(8, 1, 2**21 + 1, None, 0)) == UNSUP
+    assert lib.kvq_decode(*args(8, 2**17, 2**21, None, 0)) != UNSUP
 
 
 def test_profile_entry_points_without_gpu():
@@ -191,7 +199,7 @@ def test_mla_decode_argument_errors(handles):
     assert lib.kvq_decode_workspace_bytes(h["mla"], 2, 16, 1000) > 0
 
 
-def test_split_plan_cap(handles, monkeypatch):
+def test_split_plan_cap(handles):
     """Aimed at far more workgroups than one sequence has tiles, the planners
     stop at 128 splits: GQA 40,000 tokens = 2,500 tiles -> 157 splits of 16
     tiles, capped to 128, re-tiled at 20 tiles = 125 splits; MLA 8,192 tokens
@@ -199,11 +207,13 @@ def test_split_plan_cap(handles, monkeypatch):
     workspace is splits x (Dv + 1) floats per (sequence, head), each part
     rounded up to 256 bytes."""
     lib, h = handles
-    monkeypatch.setenv("KVQ_DECODE_TARGET_WGS", "100000")
+    for name in ("fp8", "mla"):
+        assert lib.kvq_testing_set_split_target(h[name], 100000) == OK
     up = lambda x: (x + 255) // 256 * 256
     assert lib.kvq_decode_workspace_bytes(h["fp8"], 1, 8, 40000) == up(8 * 125 * 128 * 4) + up(8 * 125 * 4)
     assert lib.kvq_decode_workspace_bytes(h["mla"], 1, 16, 8192) == up(16 * 128 * 512 * 4) + up(16 * 128 * 4)
-    monkeypatch.setenv("KVQ_DECODE_TARGET_WGS", "1")
+    for name in ("fp8", "mla"):
+        assert lib.kvq_testing_set_split_target(h[name], 1) == OK
     # one split per sequence when it fits (no workspace); 1,024 tiles per GQA split at most
     assert lib.kvq_decode_workspace_bytes(h["fp8"], 1, 8, 16384) == 0
     assert lib.kvq_decode_workspace_bytes(h["fp8"], 1, 8, 40000) == up(8 * 3 * 128 * 4) + up(8 * 3 * 4)

@@ -1,7 +1,6 @@
 """GPU parity of kvq_decode against the oracle (same seeded inputs, oracle
 computed in float64 from its own quantization of them): max-abs <= 4e-3 and
 rel-L2 <= 1e-3 on every checked output, LSE within 1e-4."""
-import os
 
 import numpy as np
 import pytest
@@ -68,14 +67,11 @@ def test_split_count_invariance():
     w = I.WORKLOADS["llama3_8b"].with_(batch=2, max_len=6000, min_len=6000)
     c = Case(w).run_gpu(decode=False)
     outs = []
-    for target in ("1", "64", "100000"):
-        os.environ["KVQ_DECODE_TARGET_WGS"] = target
-        try:
+    for target in (1, 64, 100000):
+        with K.split_target(c.cache, target):
             o, l = K.kvq_decode(c.cache, c.q_dev, c.table_dev, c.lens_dev, c.max_len, I.sm_scale(w),
                                 c.k_scale, c.v_scale)
             outs.append((o.cpu().numpy(), l.cpu().numpy()))
-        finally:
-            del os.environ["KVQ_DECODE_TARGET_WGS"]
     for o, l in outs[1:]:
         assert rel_l2(o, outs[0][0]) < 3e-4 and np.allclose(l, outs[0][1], atol=1e-5)
 
@@ -83,15 +79,12 @@ def test_split_count_invariance():
 def _decode_at_target(c, w, target):
     """kvq_decode with the split planner aimed at `target` workgroups; also
     returns the workspace size that plan needs."""
-    os.environ["KVQ_DECODE_TARGET_WGS"] = target
-    try:
+    with K.split_target(c.cache, int(target)):
         ws = K.kvq_decode_workspace_bytes(c.cache, len(c.lens), w.q_heads, c.max_len)
         o, l = K.kvq_decode(c.cache, c.q_dev, c.table_dev, c.lens_dev, c.max_len, I.sm_scale(w),
                             c.k_scale, c.v_scale)
         torch.cuda.synchronize()
         return o, l, ws
-    finally:
-        del os.environ["KVQ_DECODE_TARGET_WGS"]
 
 
 @pytest.mark.parametrize("kind", ["gqa", "mla"])
@@ -207,13 +200,10 @@ def test_mla_split_count_invariance():
     w = I.WORKLOADS["dsr1_mla"].with_(batch=2, max_len=9000, min_len=9000)
     c = Case(w).run_gpu(decode=False)
     outs = []
-    for target in ("1", "32", "100000"):
-        os.environ["KVQ_DECODE_TARGET_WGS"] = target
-        try:
+    for target in (1, 32, 100000):
+        with K.split_target(c.cache, target):
             o, l = K.kvq_decode(c.cache, c.q_dev, c.table_dev, c.lens_dev, c.max_len, I.sm_scale(w), c.k_scale, None)
             outs.append((o.cpu().numpy(), l.cpu().numpy()))
-        finally:
-            del os.environ["KVQ_DECODE_TARGET_WGS"]
     for o, l in outs[1:]:
         assert rel_l2(o, outs[0][0]) < 3e-4 and np.allclose(l, outs[0][1], atol=1e-5)
 
@@ -249,12 +239,8 @@ def test_mla_reference_moves(hq, P, target):
         if m > ref + 8.0:
             ref, moves = m, moves + 1
     assert moves >= 5, moves
-    if target is not None:
-        os.environ["KVQ_DECODE_TARGET_WGS"] = target   # one split per sequence: direct output path
-    try:
-        c.run_gpu()
-    finally:
-        os.environ.pop("KVQ_DECODE_TARGET_WGS", None)
+    # target 3: one split per sequence, the direct output path
+    c.run_gpu(split_target=0 if target is None else int(target))
     ids = [0, 1, 2]
     what = f"mla ramp Hq{hq} P{P} target {target}"
     want, wlse, _, _ = c.oracle_decode(ids)
