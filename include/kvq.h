@@ -3,7 +3,9 @@
  *
  * C ABI of libkvq.so. Every argument is a plain pointer or integer: host
  * pointers are marked [host], device (HBM) pointers [dev]. The library never
- * allocates device memory; every device buffer belongs to the caller and
+ * allocates device memory (its one device-resident buffer, the static
+ * workspace of kvq_decode_noalloc, is part of its loaded code); every
+ * device buffer an argument names belongs to the caller and
  * must stay alive until the work queued on `stream` has finished. `stream`
  * is a hipStream_t passed as void* (NULL = the default stream). All device
  * work is enqueued asynchronously on that stream; no entry point synchronizes
@@ -70,7 +72,9 @@ typedef enum kvq_status {
   KVQ_ERR_ARG = -1,         /* null pointer, negative size, inconsistent shape */
   KVQ_ERR_UNSUPPORTED = -2, /* valid but not implemented (dtype x kind x dims) */
   KVQ_ERR_SIZE = -3,        /* caller buffer (cache memory, workspace) too small */
-  KVQ_ERR_HIP = -4          /* a HIP launch reported an error */
+  KVQ_ERR_HIP = -4,         /* a HIP launch reported an error */
+  KVQ_ERR_WORKSPACE = -5    /* kvq_decode_noalloc: the call needs more than the
+                               library's static workspace (80 MiB) */
 } kvq_status;
 
 /* Shape of one layer's cache. */
@@ -232,6 +236,26 @@ int kvq_decode(const kvq_cache* cache, const void* q, int32_t batch, int32_t num
                const int32_t* page_table, int32_t page_table_stride, const int32_t* seq_lens,
                int32_t max_seq_len, float sm_scale, const float* k_scale, const float* v_scale,
                float* out, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/* kvq_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, kernels and split plan, with the split partials kept in
+ * a workspace the library holds in device memory (a static array of 80 MiB
+ * on every GPU the library runs on, kept until the process ends) instead of
+ * a caller buffer. The caller still owns every input and output.
+ * The first call on a device looks up that device's workspace address (the
+ * device of `stream`; the current device for the null stream); no call
+ * allocates or frees memory. Calls on one GPU share its workspace: calls that
+ * overlap on that GPU (other streams, other threads, concurrent graph
+ * replays) race, and must be serialized by the caller. Each call writes every
+ * partial it reads, so nothing has to be cleared between calls.
+ * Arguments and errors are kvq_decode's without the workspace, plus
+ * KVQ_ERR_WORKSPACE when kvq_decode_workspace_bytes for this shape exceeds
+ * 80 MiB (83,886,080 bytes), returned before anything is enqueued. */
+int kvq_decode_noalloc(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,
+                       const int32_t* page_table, int32_t page_table_stride, const int32_t* seq_lens,
+                       int32_t max_seq_len, float sm_scale, const float* k_scale, const float* v_scale,
+                       float* out, float* lse, void* stream);
 
 /* One decode step in one launch: appends the token at position seq_lens[b] - 1
  * of every sequence b, then decodes. Equivalent to kvq_store of those tokens

@@ -258,6 +258,7 @@ const char* kvq_status_string(int status) {
     case KVQ_ERR_UNSUPPORTED: return "unsupported format or shape";
     case KVQ_ERR_SIZE: return "buffer too small";
     case KVQ_ERR_HIP: return "HIP launch error";
+    case KVQ_ERR_WORKSPACE: return "decode needs more workspace than the library's static workspace holds";
     default: return "unknown status";
   }
 }
@@ -375,13 +376,27 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* c, int32_t batch, int32_t hq,
 
 namespace {
 
+// kvq_decode_noalloc: the library's static workspace in place of a caller
+// buffer, once every argument has been checked (the size limit first, then
+// the device address of this stream's device).
+int bind_static_workspace(size_t need, hipStream_t s, void** ws, size_t* ws_bytes) {
+  if (need > kvq::kStaticWorkspaceBytes) return KVQ_ERR_WORKSPACE;
+  *ws = nullptr;
+  *ws_bytes = 0;
+  if (need == 0) return KVQ_OK;
+  if (kvq_static_workspace(s, ws) != hipSuccess) return KVQ_ERR_HIP;
+  *ws_bytes = kvq::kStaticWorkspaceBytes;
+  return KVQ_OK;
+}
+
 // kvq_decode, optionally appending the token at position seq_lens[b] - 1 of
 // every sequence first (k_new / v_new non-null: kvq_decode_append)
 // (q8: FP8-domain attention, kvq_decode_fp8q / kvq_decode_append_fp8q)
 int decode_impl(const kvq_cache* c, const void* k_new, const void* v_new, const void* q, int32_t batch, int32_t hq,
                 const int32_t* page_table, int32_t page_table_stride, const int32_t* seq_lens, int32_t max_len,
                 float sm_scale, const float* k_scale, const float* v_scale, float* out, float* lse, void* ws,
-                size_t ws_bytes, void* stream, bool q8 = false, const float* q_scale = nullptr) {
+                size_t ws_bytes, void* stream, bool q8 = false, const float* q_scale = nullptr,
+                bool static_ws = false) {
   if (!c || batch < 0 || hq < 1 || max_len < 0) return KVQ_ERR_ARG;
   if (q8) {
     const kvq_cache_desc& d = c->desc;
@@ -408,6 +423,10 @@ int decode_impl(const kvq_cache* c, const void* k_new, const void* v_new, const 
     const SplitPlan plan = plan_gqa(batch, d.num_kv_heads, max_len, c->split_target);
     const WsLayout wl = workspace_for(plan, batch, hq, d.v_dim);
     const size_t need = wl.total;
+    if (static_ws) {
+      const int st = bind_static_workspace(need, s, &ws, &ws_bytes);
+      if (st != KVQ_OK) return st;
+    }
     if (need && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % kAlign)) return KVQ_ERR_SIZE;
     GqaDecodeArgs a;
     memset(&a, 0, sizeof(a));
@@ -478,6 +497,10 @@ int decode_impl(const kvq_cache* c, const void* k_new, const void* v_new, const 
   if (mla_split_pages(plan, P) > kvq::kMlaMaxSplitPages) return KVQ_ERR_UNSUPPORTED;
   const WsLayout wl = workspace_for(plan, batch, hq, d.v_dim);
   const size_t need = wl.total;
+  if (static_ws) {
+    const int st = bind_static_workspace(need, s, &ws, &ws_bytes);
+    if (st != KVQ_OK) return st;
+  }
   if (need && (!ws || ws_bytes < need || reinterpret_cast<uintptr_t>(ws) % kAlign)) return KVQ_ERR_SIZE;
   MlaDecodeArgs a;
   memset(&a, 0, sizeof(a));
@@ -536,6 +559,13 @@ int kvq_decode(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, con
                void* stream) {
   return decode_impl(c, nullptr, nullptr, q, batch, hq, page_table, page_table_stride, seq_lens, max_len, sm_scale,
                      k_scale, v_scale, out, lse, ws, ws_bytes, stream);
+}
+
+int kvq_decode_noalloc(const kvq_cache* c, const void* q, int32_t batch, int32_t hq, const int32_t* page_table,
+                       int32_t page_table_stride, const int32_t* seq_lens, int32_t max_len, float sm_scale,
+                       const float* k_scale, const float* v_scale, float* out, float* lse, void* stream) {
+  return decode_impl(c, nullptr, nullptr, q, batch, hq, page_table, page_table_stride, seq_lens, max_len, sm_scale,
+                     k_scale, v_scale, out, lse, nullptr, 0, stream, false, nullptr, true);
 }
 
 int kvq_decode_append(const kvq_cache* c, const void* k_new, const void* v_new, const void* q, int32_t batch,

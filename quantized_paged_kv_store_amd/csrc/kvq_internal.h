@@ -24,6 +24,9 @@ constexpr int kWaves = 4;      // waves per decode workgroup
 constexpr int kAmaxBlocks = 1024;
 constexpr int kMlaMaxSplitPages = 1024;  // page ids one MLA split stages in LDS
 constexpr int kExtendRows = 256;         // (chunk token, query head) rows per extend workgroup
+// device-resident workspace of kvq_decode_noalloc: 80 MiB per GPU (the
+// DeepSeek-R1-shape MLA step, batch 64 x 128 heads x 4 splits, needs 64 MiB)
+constexpr size_t kStaticWorkspaceBytes = (size_t)80 << 20;
 
 // ------------------------------------------------------- vector typedefs --
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -182,6 +185,10 @@ struct ExtendArgs {
   float sm_scale;
 };
 
+// Device address, on the device `stream` belongs to (the current device for
+// the null stream), of the library's static decode workspace of
+// kStaticWorkspaceBytes; looked up once per device.
+hipError_t kvq_static_workspace(hipStream_t stream, void** addr);
 hipError_t kvq_launch_extend(const ExtendArgs& a, hipStream_t s);
 hipError_t kvq_launch_amax(const uint16_t* x0, int64_t n0, const uint16_t* x1, int64_t n1,
                            unsigned* scratch, float fmt_div, float* scale_out, hipStream_t s);

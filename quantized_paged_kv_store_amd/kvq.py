@@ -22,7 +22,8 @@ LIB_PATH = os.environ.get("KVQ_LIB_PATH") or os.path.join(os.path.dirname(os.pat
 DTYPES = {"e4m3": 1, "e5m2": 2, "mx16": 3, "nvfp4": 4}
 SCALE_MODES = {"tensor": 0, "head": 1, "kivi": 2}
 KINDS = {"gqa": 0, "mla": 1}
-STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_ARG", -2: "KVQ_ERR_UNSUPPORTED", -3: "KVQ_ERR_SIZE", -4: "KVQ_ERR_HIP"}
+STATUS = {0: "KVQ_OK", -1: "KVQ_ERR_ARG", -2: "KVQ_ERR_UNSUPPORTED", -3: "KVQ_ERR_SIZE", -4: "KVQ_ERR_HIP",
+          -5: "KVQ_ERR_WORKSPACE"}
 
 
 class KVQError(RuntimeError):
@@ -71,6 +72,9 @@ def _lib():
         L.kvq_decode.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_void_p, c_int32,
                                  c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
         L.kvq_decode.restype = c_int32
+        L.kvq_decode_noalloc.argtypes = [c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_int32, c_void_p,
+                                         c_int32, c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+        L.kvq_decode_noalloc.restype = c_int32
         L.kvq_decode_append.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p, c_int32,
                                         c_void_p, c_int32, c_float, c_void_p, c_void_p, c_void_p, c_void_p,
                                         c_void_p, c_size_t, c_void_p]
@@ -297,10 +301,13 @@ def _decode_call(name: str, cache: Cache, k_new, v_new, q, page_table, seq_lens,
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     _tensor(out, "out", torch.float32, dev, shape=(B, Hq, d.v_dim))
     _tensor(lse, "lse", torch.float32, dev, shape=(B, Hq))
-    need = kvq_decode_workspace_bytes(cache, B, Hq, max_seq_len)
+    noalloc = name == "kvq_decode_noalloc"
+    need = 0 if noalloc else kvq_decode_workspace_bytes(cache, B, Hq, max_seq_len)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     if workspace is not None:
+        if noalloc:
+            raise ValueError("workspace: kvq_decode_noalloc uses the library's own")
         _tensor(workspace, "workspace", torch.uint8, dev, min_numel=need)
     ks, vs = _dev_f32(k_scale, dev, _n_scales(cache)), _dev_f32(v_scale, dev, _n_scales(cache, "v"))
     fp8q = name.endswith("_fp8q")
@@ -309,7 +316,8 @@ def _decode_call(name: str, cache: Cache, k_new, v_new, q, page_table, seq_lens,
     head = (cache.handle,) + ((_ptr(k_new), _ptr(v_new)) if append else ())
     mid = (_ptr(q), B, Hq, _ptr(page_table), page_table.shape[1], _ptr(seq_lens), int(max_seq_len), float(sm_scale))
     scales = ((_ptr(qs),) if fp8q else ()) + (_ptr(ks), _ptr(vs))
-    tail = (_ptr(out), _ptr(lse), _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(dev))
+    tail = (_ptr(out), _ptr(lse)) + (() if noalloc else (_ptr(workspace), 0 if workspace is None else
+                                                           workspace.numel())) + (_stream(dev),)
     _check(getattr(_lib(), name)(*head, *mid, *scales, *tail), name)
     return out, lse
 
@@ -319,6 +327,16 @@ def kvq_decode(cache: Cache, q: torch.Tensor, page_table: torch.Tensor, seq_lens
     """Returns (out fp32 [B, Hq, Dv], lse fp32 [B, Hq])."""
     return _decode_call("kvq_decode", cache, None, None, q, page_table, seq_lens, max_seq_len, sm_scale, None,
                         k_scale, v_scale, out, lse, workspace)
+
+
+def kvq_decode_noalloc(cache: Cache, q: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
+                       max_seq_len: int, sm_scale: float, k_scale=None, v_scale=None, out=None, lse=None):
+    """kvq_decode with the split partials in the library's static device
+    workspace (no device allocation by the library; pass out and lse to keep
+    this binding from allocating them). Calls that overlap on one GPU race.
+    Returns (out fp32 [B, Hq, Dv], lse fp32 [B, Hq])."""
+    return _decode_call("kvq_decode_noalloc", cache, None, None, q, page_table, seq_lens, max_seq_len, sm_scale,
+                        None, k_scale, v_scale, out, lse, None)
 
 
 def kvq_decode_append(cache: Cache, k_new: torch.Tensor, v_new: torch.Tensor | None, q: torch.Tensor,

@@ -5,6 +5,7 @@
 // kernel.
 #include "kvq_internal.h"
 
+hipError_t kvq_static_workspace(hipStream_t, void**) { return hipErrorNoDevice; }
 hipError_t kvq_launch_extend(const ExtendArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t kvq_launch_amax(const uint16_t*, int64_t, const uint16_t*, int64_t, unsigned*, float, float*, hipStream_t) {
   return hipErrorNoDevice;

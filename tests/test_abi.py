@@ -219,6 +219,25 @@ def test_split_plan_cap(handles):
     assert lib.kvq_decode_workspace_bytes(h["fp8"], 1, 8, 40000) == up(8 * 3 * 128 * 4) + up(8 * 3 * 4)
 
 
+def test_noalloc_decode_limit_and_errors(handles):
+    """kvq_decode_noalloc refuses, before any device call, a shape whose split
+    partials exceed its 80 MiB static workspace (KVQ_ERR_WORKSPACE), and
+    otherwise validates like kvq_decode."""
+    lib, h = handles
+    P = c_void_p(FAKE_DEV)
+    f = lib.kvq_decode_noalloc
+    # MLA, 2,048 sequences x 128 heads x 2 splits x 512 floats = 1 GiB
+    assert lib.kvq_decode_workspace_bytes(h["mla"], 2048, 128, 65536) > 80 << 20
+    assert f(h["mla"], P, 2048, 128, P, 1024, P, 65536, 0.04, P, None, P, None, None) == -5
+    # the DeepSeek-R1 shape (64 x 128 heads x 4 splits) fits: 64 MiB + 128 KiB
+    assert lib.kvq_decode_workspace_bytes(h["mla"], 64, 128, 65536) <= 80 << 20
+    assert f(h["fp8"], P, 0, 8, P, 4, P, 64, 0.1, None, None, P, None, None) == OK     # empty batch
+    assert f(h["fp8"], P, 4, 7, P, 4, P, 64, 0.1, None, None, P, None, None) == ARG    # Hq % Hkv
+    assert f(h["mla"], P, 2, 128, P, 16, P, 1000, 0.04, None, None, P, None, None) == ARG  # g required
+    assert f(None, P, 4, 8, P, 4, P, 64, 0.1, None, None, P, None, None) == ARG
+    assert b"static workspace" in lib.kvq_status_string(-5)
+
+
 def test_decode_append_argument_errors(handles):
     lib, h = handles
     P = c_void_p(FAKE_DEV)
