@@ -7,6 +7,7 @@ import pytest
 import torch
 
 import quantized_paged_kv_store_amd as K
+from oracle import quantize as Q
 from quantized_paged_kv_store_amd import inputs as I
 from tests.kvq_cases import Case, assert_close, rel_l2
 
@@ -47,6 +48,41 @@ def test_ragged_lengths(dtype, D, G, P):
     _check(c, ids, f"{dtype} D{D} G{G} P{P}")
     got = c.out.cpu().numpy()
     assert np.all(got[0] == 0) and np.all(np.isneginf(c.lse.cpu().numpy()[0]))
+
+
+class _TinyBlocksCase(Case):
+    """K and V rows of every fifth token scaled by 2^-130 (input generation
+    only; both sides see the same BF16 rows, many of them BF16 subnormals):
+    every 16-element block of those rows has amax below 2^-124, so the store
+    gives it E8M0 scale code 0, i.e. 2^-127."""
+
+    def rows(self, b, t0, t1):
+        k, v = super().rows(b, t0, t1)
+        sel = (np.arange(t0, t1) % 5) == 2
+        kf, vf = I.bf16_to_f32(k).copy(), I.bf16_to_f32(v).copy()
+        kf[sel] *= np.float32(2.0 ** -130)
+        vf[sel] *= np.float32(2.0 ** -130)
+        return I.bf16_bits(kf), I.bf16_bits(vf)
+
+
+def test_mx16_code0_blocks():
+    """MX16 decode over blocks with E8M0 code 0 next to ordinary ones. The
+    decode kernels take code 0 as 2^-126 (the scaled converts refuse the
+    subnormal 2^-127); those blocks are below 1e-36, so the outputs still meet
+    the parity bound against the oracle's exact 2^-127. Codes and scale bytes
+    are compared byte for byte (the store quantizes subnormal BF16 inputs)."""
+    lens = [17, 200, 1000]
+    w = I.Workload("mx16-code0", "mx16", "gqa", len(lens), 8, 2, 128, 128, 16, max(lens), 0, 1, "llama", seed=23)
+    c = _TinyBlocksCase(w, lens=lens).run_gpu()
+    k, v = c.rows(2, 0, 10)
+    _, sk = Q.quantize_mx16(I.bf16_to_f32(k[2]).astype(np.float64))
+    _, sv = Q.quantize_mx16(I.bf16_to_f32(v[2]).astype(np.float64))
+    assert np.all(sk == 0) and np.all(sv == 0)          # the scaled rows are all code-0 blocks
+    ids = [0, 1, 2]
+    want, wlse, oc, pages = c.oracle_decode(ids)
+    for name in ("k_codes", "v_codes", "k_scales", "v_scales"):
+        assert np.array_equal(c.gpu_pages(name, pages), getattr(oc, name)), name
+    _check(c, ids, "mx16 code-0 blocks")
 
 
 def test_single_token_equals_value_row():
