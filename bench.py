@@ -504,6 +504,10 @@ def main():
                     help="FP8 workloads: K scales per channel, V scales per token (KIVI-style)")
     ap.add_argument("--per-head-scales", action="store_true",
                     help="FP8 workloads: one calibrated k/v scale per KV head instead of per tensor")
+    ap.add_argument("--kv-dtype", choices=("e4m3", "e5m2"), default=None,
+                    help="FP8 GQA workloads: the cache's FP8 format (workload variant; default the workload's)")
+    ap.add_argument("--scale", choices=("amax", "one"), default=None,
+                    help="FP8 workloads: per-tensor scales calibrated from the prefill's amax, or 1.0")
     ap.add_argument("--fp8q", action="store_true",
                     help="FP8 GQA workloads: FP8-domain attention (query rounded to E4M3, QK on FP8 MFMA)")
     args = ap.parse_args()
@@ -520,6 +524,12 @@ def main():
     from quantized_paged_kv_store_amd import inputs as I
 
     w = I.WORKLOADS[args.workload]
+    if args.kv_dtype:
+        assert w.dtype in ("e4m3", "e5m2") and w.kind == "gqa", "--kv-dtype applies to FP8 GQA workloads"
+        w = w.with_(dtype=args.kv_dtype)
+    if args.scale:
+        assert w.dtype in ("e4m3", "e5m2"), "--scale applies to FP8 workloads"
+        w = w.with_(scale_mode=args.scale)
     if args.per_head_scales:
         assert w.dtype in ("e4m3", "e5m2"), "per-head scales apply to FP8 caches"
         w = w.with_(scale_mode="amax_head")
@@ -569,8 +579,15 @@ def main():
     run_loop(st, args.steps, True, False)
     torch.cuda.synchronize()
     sto_tot, sto_n = K.kvq_profile_read("store")
+    # the decode kernel alone, back to back with no store between launches
+    run_loop(st, args.steps, False, True)
+    torch.cuda.synchronize()
+    dec_only_tot, dec_only_n = K.kvq_profile_read("decode")
+    K.kvq_profile_read("merge")
     K.kvq_profile_enable(False)
+    # the roofline uses the decode kernel as it runs inside the step
     kern_ms = dec_tot / max(dec_n, 1)
+    kern_only_ms = dec_only_tot / max(dec_only_n, 1)
     merge_ms = mer_tot / max(mer_n, 1) if mer_n else 0.0
     store_kern_ms = sto_tot / max(sto_n, 1)
     kv_bytes = float(st["lens_h"].astype(np.int64).sum()) * st["bpt"]
@@ -583,6 +600,7 @@ def main():
     # other workloads and modes name themselves
     variant = [m for m, on in (("KIVI-style scales", w.scale_mode == "kivi"),
                                ("per-KV-head scales", w.scale_mode == "amax_head"),
+                               ("scale 1.0", w.scale_mode == "one"),
                                ("FP8-domain attention", args.fp8q)) if on]
     metric = METRIC if (w.name == "llama3_8b" and not variant) else (
         f"decode-attn effective KV GB/s (% HBM peak), {w.name} {w.dtype} bs{w.batch} ctx{w.max_len}"
@@ -631,7 +649,10 @@ def main():
                                      + (", FP8-domain QK)" if args.fp8q else ")"),
                            "kernel_ms": round(kern_ms, 5), "algorithmic_bytes_per_launch": kv_bytes}
     res["roofline"]["traffic_unit"] = "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)"
-    res["kernel_ms"] = {"decode": round(kern_ms, 5), "merge": round(merge_ms, 5), "store": round(store_kern_ms, 5)}
+    res["kernel_ms"] = {"decode": round(kern_ms, 5), "merge": round(merge_ms, 5), "store": round(store_kern_ms, 5),
+                        "decode_without_store": round(kern_only_ms, 5)}
+    res["decode_kernel_GBps"] = {"in_step": round(kv_bytes / (kern_ms * 1e-3) / 1e9, 2),
+                                 "without_store": round(kv_bytes / (kern_only_ms * 1e-3) / 1e9, 2)}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, fp8q=args.fp8q)
     print(json.dumps(res), flush=True)
