@@ -111,6 +111,53 @@ def decode_attention_fp8q(cache: OracleCache, q, page_table, seq_lens, sm_scale,
     return decode_attention(cache, q_hat, page_table, seq_lens, sm_scale, k_scale, v_scale, batch_ids)
 
 # --------------------------------------------------------------------------
+# FP8-domain MLA decode (vLLM "Quantized KV Cache" page, overview: attention
+# computed in FP8, the query quantized to FP8 like the keys; "Supported
+# schemes": q_scale per tensor). The MLA latent is NVFP4, whose values no FP8
+# format holds exactly, so the keys take the NVFP4 -> E4M3 step that
+# dequantize_prev_kv defines (PR #21954 analysis page, "code analysis"), with
+# the output scale 8g. Reading adopted: that scale is fixed by g, not
+# calibrated: an NVFP4 value is e2m1 * e4m3 * g, at most 6 * 448 * g, so
+# after the division by 8g every value lies within +-336 and no code
+# saturates, and the division is exact (e2m1 * e4m3 / 8 has at most six
+# significant bits), so each key element is the E4M3 rounding (to nearest,
+# ties to even) of e2m1 * e4m3 / 8. Scores are
+#   sm_scale * sum_d q^_d * (decode(K8 code) * 8g)_d
+# with q^ = decode(quantize_query_fp8(q, q_scale)); the weights then multiply
+# the exact NVFP4 values V^ = latent[:Dv] (the value side stays exact, as in
+# the FP8-domain GQA path).
+# --------------------------------------------------------------------------
+def decode_attention_mla_fp8q(cache: OracleCache, q, page_table, seq_lens, sm_scale, q_scale=None, g=None,
+                              batch_ids=None):
+    """q [B, Hq, Dk] float -> (out [B, Hq, Dv], lse [B, Hq]) float64; an MLA
+    NVFP4 cache, g its global scale (binary32, required)."""
+    from .formats import E4M3, decode
+    from .paged import dequantize_prev_kv
+    from .quantize import fl32
+    spec = cache.spec
+    assert spec.kind == "mla" and spec.dtype == "nvfp4" and g is not None
+    codes, s = quantize_query_fp8(q, q_scale)
+    q_hat = decode(codes.astype(np.int64), E4M3) * s[None, :, None].astype(np.float64)
+    s8 = np.float32(fl32(8.0 * np.float64(np.float32(g))))
+    B, Hq, _ = q_hat.shape
+    out = np.zeros((B, Hq, spec.v_dim))
+    lse = np.full((B, Hq), np.nan)
+    for b in (range(B) if batch_ids is None else batch_ids):
+        L = int(seq_lens[b])
+        if L == 0:
+            out[b], lse[b] = 0.0, -np.inf
+            continue
+        npg = (L + spec.page_size - 1) // spec.page_size
+        pages = np.asarray(page_table[b][:npg], np.int64)
+        k8, _ = dequantize_prev_kv(cache, pages, s8, None, g=g)            # [npg, P, Dk] E4M3 codes
+        k8_hat = decode(k8.reshape(-1, spec.head_dim)[:L].astype(np.int64), E4M3) * np.float64(s8)
+        page, t = _pages_of(page_table[b], L, spec.page_size)
+        v_hat = cache.dequant(page, t, 0, "v", g)
+        out[b], lse[b] = softmax_attention(q_hat[b], k8_hat, v_hat, sm_scale)
+    return out, lse
+
+
+# --------------------------------------------------------------------------
 # Extend (chunked prefill) attention over a quantized prefix. The PR #21954
 # analysis page ("code analysis") has dequantize_prev_kv turn the FP4 prefix
 # into FP8 E4M3 workspaces (dq_k_buffer / dq_v_buffer) because only FP8

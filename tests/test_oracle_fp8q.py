@@ -126,3 +126,101 @@ def test_query_scale_calibration_closed_forms():
     assert s[3] == np.float32(np.float32(1.0) / np.float32(448.0))
     assert list(Q.fp8_query_scales(q, per_head=False)) == [3.0]
     assert list(Q.fp8_query_scales(np.zeros((0, 4, 8)), per_head=False)) == [1.0]
+
+
+# ---------------------------------------------------------------------------
+# FP8-domain MLA (oracle.attention.decode_attention_mla_fp8q): keys are the
+# E4M3 rounding of e2m1 * e4m3 / 8 (the NVFP4 -> E4M3 step of
+# dequantize_prev_kv with the output scale 8g), values stay exact.
+# ---------------------------------------------------------------------------
+from oracle.attention import decode_attention_mla_fp8q  # noqa: E402
+from oracle.paged import dequantize_prev_kv  # noqa: E402
+
+
+def _mla_cache(rows, g, P=16):
+    L = rows.shape[0]
+    npg = (L + P - 1) // P
+    oc = OracleCache(CacheSpec("nvfp4", "mla", 1, 576, 512, P, npg))
+    oc.store(rows, None, np.arange(L), k_scale=np.float32(g))
+    table = np.arange(npg, dtype=np.int32)[None, :]
+    return oc, table
+
+
+def test_mla_fp8_keys_are_torch_e4m3_of_nvfp4_over_8():
+    """Every key code equals torch's float8_e4m3fn rounding of the exact NVFP4
+    value divided by 8g (an independent encoder); blocks scaled far down reach
+    E4M3 subnormals; nothing saturates: |value| <= 336 < 448."""
+    rng = np.random.default_rng(21)
+    L = 70
+    x = rng.standard_normal((L, 576)).astype(np.float32)
+    x[:, :16] *= 8.0
+    x[5:9, 32:64] *= 2.0 ** -9                                   # blocks whose E4M3 scales are tiny
+    x = I.bf16_to_f32(I.bf16_bits(x))
+    g = Q.nvfp4_global_scale(np.abs(x).max())
+    oc, table = _mla_cache(x, g)
+    npg = table.shape[1]
+    s8 = np.float32(8.0 * np.float64(g))
+    k8, _ = dequantize_prev_kv(oc, np.arange(npg), s8, None, g=g)
+    k8 = k8.reshape(-1, 576)[:L]
+    exact = oc.dequant(np.arange(L) // 16, np.arange(L) % 16, 0, "k", g) / (8.0 * np.float64(g))
+    assert np.array_equal(exact, exact.astype(np.float32).astype(np.float64))   # e2m1 * e4m3 / 8: exact in fp32
+    want = torch.from_numpy(exact.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(k8, want)
+    mag = k8 & 0x7F
+    assert mag.max() <= 0x7A and not np.any(mag == 0x7E)                         # 0x7A = 320, <= 336
+    assert np.any((mag > 0) & (mag < 8))                                         # E4M3 subnormals occur
+    assert np.mean(F.decode(k8.astype(np.int64), F.E4M3) != exact) > 0.2         # most keys are rounded
+
+
+def test_mla_fp8_on_grid_equals_plain_decode():
+    """Latent rows of the form e2m1 * 2^k * g with block maxima 6 * 2^k * g:
+    the NVFP4 scales are powers of two, every key e2m1 * 2^k / 8 is an E4M3
+    value, and a query on the E4M3 grid (q_scale 1) is kept as it is, so the
+    FP8-domain result equals the plain MLA decode."""
+    rng = np.random.default_rng(22)
+    L, g = 45, np.float32(2.0 ** -6)
+    e2m1 = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    blocks = rng.choice(e2m1, size=(L, 36, 16)) * rng.choice([-1.0, 1.0], size=(L, 36, 16))
+    blocks[:, :, 0] = 6.0                                                        # block max 6 * 2^k
+    k = rng.integers(-2, 6, size=(L, 36, 1))
+    x = (blocks * 2.0 ** k * np.float64(g)).reshape(L, 576)
+    oc, table = _mla_cache(x, g)
+    q = F.decode(rng.integers(0, 0x7E, size=(2, 8, 576)) | (rng.integers(0, 2, size=(2, 8, 576)) << 7), F.E4M3)
+    q = np.where(np.abs(q) > 240, 0.0, q) * 2.0 ** -6
+    lens = np.array([L, 30])
+    tab = np.repeat(table, 2, axis=0)
+    a, la = decode_attention_mla_fp8q(oc, q, tab, lens, 0.041, 2.0 ** -6, g)
+    b, lb = decode_attention(oc, q, tab, lens, 0.041, g)
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-14) and np.allclose(la, lb, rtol=1e-12, atol=1e-12)
+
+
+def test_mla_fp8_zero_query_is_mean_of_exact_values():
+    """q = 0: every score is 0, so the output is the mean of the exact NVFP4
+    value rows (not of their E4M3 roundings) and the LSE is log L."""
+    rng = np.random.default_rng(23)
+    L = 37
+    x = I.bf16_to_f32(I.bf16_bits(rng.standard_normal((L, 576)).astype(np.float32)))
+    g = Q.nvfp4_global_scale(np.abs(x).max())
+    oc, table = _mla_cache(x, g)
+    out, lse = decode_attention_mla_fp8q(oc, np.zeros((1, 4, 576)), table, [L], 0.04, None, g)
+    v = oc.dequant(np.arange(L) // 16, np.arange(L) % 16, 0, "v", g)
+    assert np.allclose(out[0], v.mean(axis=0)[None, :], rtol=1e-12, atol=1e-15)
+    assert np.allclose(lse, np.log(L), rtol=0, atol=1e-12)
+
+
+def test_mla_fp8_differs_from_plain_beyond_tolerance():
+    """On the DeepSeek-R1-shaped data the FP8-domain result moves far more than
+    the GPU parity tolerance away from the plain MLA decode (so the parity
+    tests tell the paths apart), and stays a few percent from it."""
+    w = I.WORKLOADS["dsr1_mla"].with_(batch=1, max_len=300, min_len=300)
+    k, _ = I.kv_rows(w, 0, 0, 300)
+    x = I.bf16_to_f32(k)
+    g = Q.nvfp4_global_scale(np.abs(x).max())
+    oc, table = _mla_cache(x, g, P=64)
+    q = I.bf16_to_f32(I.queries(w))[:, :16]
+    qs = Q.fp8_query_scales(q, per_head=False)
+    a, _ = decode_attention_mla_fp8q(oc, q, table, [300], I.sm_scale(w), qs, g)
+    b, _ = decode_attention(oc, q, table, [300], I.sm_scale(w), g)
+    d = np.linalg.norm(a - b) / np.linalg.norm(b)
+    assert np.abs(a - b).max() > 4e-3 or d > 1e-3, d
+    assert d < 0.2, d
