@@ -127,18 +127,29 @@ def decode_attention_fp8q(cache: OracleCache, q, page_table, seq_lens, sm_scale,
 # the exact NVFP4 values V^ = latent[:Dv] (the value side stays exact, as in
 # the FP8-domain GQA path).
 # --------------------------------------------------------------------------
+def mla_fp8_keys(cache: OracleCache, page_table_row, length, g):
+    """E4M3 key rows of the first `length` tokens of one MLA sequence: the
+    dequantize_prev_kv rule (exact NVFP4 value, rounded once to binary32,
+    then code = encode_E4M3(fl32(x^ / s))) with s = fl32(8g), applied to the
+    sequence's own rows only (slots past its length hold arbitrary bytes).
+    Returns (codes uint8 [length, Dk], s)."""
+    from .formats import E4M3
+    from .quantize import fl32, quantize_fp8
+    s8 = np.float32(fl32(8.0 * np.float64(np.float32(g))))
+    page, t = _pages_of(page_table_row, length, cache.spec.page_size)
+    x_hat = fl32(cache.dequant(page, t, 0, "k", g))
+    return quantize_fp8(x_hat, s8, E4M3), s8
+
+
 def decode_attention_mla_fp8q(cache: OracleCache, q, page_table, seq_lens, sm_scale, q_scale=None, g=None,
                               batch_ids=None):
     """q [B, Hq, Dk] float -> (out [B, Hq, Dv], lse [B, Hq]) float64; an MLA
     NVFP4 cache, g its global scale (binary32, required)."""
     from .formats import E4M3, decode
-    from .paged import dequantize_prev_kv
-    from .quantize import fl32
     spec = cache.spec
     assert spec.kind == "mla" and spec.dtype == "nvfp4" and g is not None
     codes, s = quantize_query_fp8(q, q_scale)
     q_hat = decode(codes.astype(np.int64), E4M3) * s[None, :, None].astype(np.float64)
-    s8 = np.float32(fl32(8.0 * np.float64(np.float32(g))))
     B, Hq, _ = q_hat.shape
     out = np.zeros((B, Hq, spec.v_dim))
     lse = np.full((B, Hq), np.nan)
@@ -147,10 +158,8 @@ def decode_attention_mla_fp8q(cache: OracleCache, q, page_table, seq_lens, sm_sc
         if L == 0:
             out[b], lse[b] = 0.0, -np.inf
             continue
-        npg = (L + spec.page_size - 1) // spec.page_size
-        pages = np.asarray(page_table[b][:npg], np.int64)
-        k8, _ = dequantize_prev_kv(cache, pages, s8, None, g=g)            # [npg, P, Dk] E4M3 codes
-        k8_hat = decode(k8.reshape(-1, spec.head_dim)[:L].astype(np.int64), E4M3) * np.float64(s8)
+        k8, s8 = mla_fp8_keys(cache, page_table[b], L, g)                   # [L, Dk] E4M3 codes
+        k8_hat = decode(k8.astype(np.int64), E4M3) * np.float64(s8)
         page, t = _pages_of(page_table[b], L, spec.page_size)
         v_hat = cache.dequant(page, t, 0, "v", g)
         out[b], lse[b] = softmax_attention(q_hat[b], k8_hat, v_hat, sm_scale)

@@ -133,7 +133,7 @@ def test_query_scale_calibration_closed_forms():
 # E4M3 rounding of e2m1 * e4m3 / 8 (the NVFP4 -> E4M3 step of
 # dequantize_prev_kv with the output scale 8g), values stay exact.
 # ---------------------------------------------------------------------------
-from oracle.attention import decode_attention_mla_fp8q  # noqa: E402
+from oracle.attention import decode_attention_mla_fp8q, mla_fp8_keys  # noqa: E402
 from oracle.paged import dequantize_prev_kv  # noqa: E402
 
 
@@ -162,6 +162,8 @@ def test_mla_fp8_keys_are_torch_e4m3_of_nvfp4_over_8():
     s8 = np.float32(8.0 * np.float64(g))
     k8, _ = dequantize_prev_kv(oc, np.arange(npg), s8, None, g=g)
     k8 = k8.reshape(-1, 576)[:L]
+    rows, s8r = mla_fp8_keys(oc, table[0], L, g)                  # the rows the decode uses
+    assert s8r == s8 and np.array_equal(rows, k8)
     exact = oc.dequant(np.arange(L) // 16, np.arange(L) % 16, 0, "k", g) / (8.0 * np.float64(g))
     assert np.array_equal(exact, exact.astype(np.float32).astype(np.float64))   # e2m1 * e4m3 / 8: exact in fp32
     want = torch.from_numpy(exact.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
@@ -224,3 +226,21 @@ def test_mla_fp8_differs_from_plain_beyond_tolerance():
     d = np.linalg.norm(a - b) / np.linalg.norm(b)
     assert np.abs(a - b).max() > 4e-3 or d > 1e-3, d
     assert d < 0.2, d
+
+
+def test_mla_fp8_keys_ignore_slots_past_the_length():
+    """Never-written slots of a sequence's last page (here NaN scale bytes)
+    are not read: the key rows and the decode depend on the first L rows only."""
+    rng = np.random.default_rng(24)
+    L, P = 21, 16
+    x = I.bf16_to_f32(I.bf16_bits(rng.standard_normal((L, 576)).astype(np.float32)))
+    g = Q.nvfp4_global_scale(np.abs(x).max())
+    oc = OracleCache(CacheSpec("nvfp4", "mla", 1, 576, 512, P, 2), fill=0xFF)
+    oc.store(x, None, np.arange(L), k_scale=np.float32(g))
+    clean, table = _mla_cache(x, g, P)
+    rows, _ = mla_fp8_keys(oc, table[0], L, g)
+    assert np.array_equal(rows, mla_fp8_keys(clean, table[0], L, g)[0])
+    q = rng.standard_normal((1, 3, 576))
+    a = decode_attention_mla_fp8q(oc, q, table, [L], 0.05, None, g)
+    b = decode_attention_mla_fp8q(clean, q, table, [L], 0.05, None, g)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
