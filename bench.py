@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 METRIC = "decode-attn effective KV GB/s (% HBM peak), 8B-shape FP8 bs8 ctx20K"
 PEAK_HBM_GBPS = 8000.0   # MI355X HBM3E, vendor figure
 PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, vendor figure
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 matrix peak, vendor figure
 
 
 def measured_traffic(w, op="decode", fp8q=False):
@@ -40,7 +41,7 @@ def measured_traffic(w, op="decode", fp8q=False):
     import hashlib
     if op == "decode":
         kind = "gqa" if w.kind == "gqa" else "mla"
-        mode = {"amax_head": "_head", "kivi": "_kivi"}.get(w.scale_mode, "") + ("_fp8q" if fp8q else "")
+        mode = {"amax_head": "_head", "kivi": "_kivi", "one": "_one"}.get(w.scale_mode, "") + ("_fp8q" if fp8q else "")
         path = os.path.join(ROOT, "profiles", f"kvq_decode_{kind}_{w.name}_{w.dtype}{mode}_traffic.json")
     elif op == "extend":
         path = os.path.join(ROOT, "profiles", f"kvq_extend_attn_{w.name}_traffic.json")
@@ -192,7 +193,7 @@ def timed(st, steps, do_store, do_decode, graphs=None, fused=False):
 def cpu_baseline(w, seconds_hint=20.0, fp8q=False):
     """The float64 oracle, untuned, on a bounded sample of the same workload
     (fp8q: the FP8-domain oracle, query scales calibrated on the step's queries)."""
-    from oracle.attention import decode_attention, decode_attention_fp8q
+    from oracle.attention import decode_attention, decode_attention_fp8q, decode_attention_mla_fp8q
     from oracle.formats import E4M3, E5M2
     from oracle import quantize as Q
     from oracle.paged import CacheSpec, OracleCache
@@ -224,12 +225,18 @@ def cpu_baseline(w, seconds_hint=20.0, fp8q=False):
     oc.store(kf, vf, I.slots_for(table[b], np.arange(L), P), k_scale=ks, v_scale=vs)
     t_codec = time.perf_counter() - t0
     q = I.bf16_to_f32(I.queries(w)).astype(np.float64)
-    t0 = time.perf_counter()
     if fp8q:
         qs = Q.fp8_query_scales(q, per_head=w.scale_mode == "amax_head")
-        decode_attention_fp8q(oc, q, table, lens, I.sm_scale(w), qs, ks, vs, batch_ids=[b])
-    else:
-        decode_attention(oc, q, table, lens, I.sm_scale(w), ks, vs, batch_ids=[b])
+
+    def decode_once():
+        if fp8q and w.kind == "mla":
+            decode_attention_mla_fp8q(oc, q, table, lens, I.sm_scale(w), qs, g=ks, batch_ids=[b])
+        elif fp8q:
+            decode_attention_fp8q(oc, q, table, lens, I.sm_scale(w), qs, ks, vs, batch_ids=[b])
+        else:
+            decode_attention(oc, q, table, lens, I.sm_scale(w), ks, vs, batch_ids=[b])
+    t0 = time.perf_counter()
+    decode_once()
     t_dec = time.perf_counter() - t0
     # the same decode with one host thread (BLAS limited to 1), reported beside
     t1 = None
@@ -237,10 +244,7 @@ def cpu_baseline(w, seconds_hint=20.0, fp8q=False):
         from threadpoolctl import threadpool_limits
         with threadpool_limits(limits=1):
             t0 = time.perf_counter()
-            if fp8q:
-                decode_attention_fp8q(oc, q, table, lens, I.sm_scale(w), qs, ks, vs, batch_ids=[b])
-            else:
-                decode_attention(oc, q, table, lens, I.sm_scale(w), ks, vs, batch_ids=[b])
+            decode_once()
             t1 = time.perf_counter() - t0
     except ImportError:
         pass
@@ -509,7 +513,8 @@ def main():
     ap.add_argument("--scale", choices=("amax", "one"), default=None,
                     help="FP8 workloads: per-tensor scales calibrated from the prefill's amax, or 1.0")
     ap.add_argument("--fp8q", action="store_true",
-                    help="FP8 GQA workloads: FP8-domain attention (query rounded to E4M3, QK on FP8 MFMA)")
+                    help="FP8 GQA and NVFP4 MLA workloads: FP8-domain attention (query rounded to E4M3, QK on "
+                         "FP8 MFMA; MLA keys as E4M3 codes of the latent / 8g)")
     args = ap.parse_args()
     if args.copy_ref:
         copy_reference()
@@ -537,8 +542,8 @@ def main():
         assert w.dtype in ("e4m3", "e5m2") and w.kind == "gqa", "KIVI-style scales apply to FP8 GQA caches"
         w = w.with_(scale_mode="kivi")
     if args.fp8q:
-        assert w.dtype in ("e4m3", "e5m2") and w.kind == "gqa" and w.scale_mode != "kivi", \
-            "FP8-domain attention applies to FP8 GQA caches with tensor or per-head scales"
+        assert (w.dtype in ("e4m3", "e5m2") and w.kind == "gqa" and w.scale_mode != "kivi") or w.kind == "mla", \
+            "FP8-domain attention applies to FP8 GQA caches with tensor or per-head scales and to the MLA latent"
     dev = torch.device("cuda:0")
     if args.dequant_prev:
         assert w.dtype in ("mx16", "nvfp4"), "dequantize_prev_kv reads FP4 caches"
@@ -618,7 +623,9 @@ def main():
                         + ("; FP8-domain attention: query rounded to E4M3 with calibrated q_scale, QK^T on "
                            "fp8 MFMA from the cached codes (kvq_decode_append_fp8q)" if args.fp8q else ""),
             "global_batch": w.batch, "seq_len": w.max_len, "kv_dtype": w.dtype,
-            "compute": ("latent codes dequantized to fp16 (E2M1 x E4M3 exact) for QK and PV MFMAs, f32 accumulate"
+            "compute": (("E4M3 query x E4M3 codes of the latent / 8g on fp8 MFMA (QK); latent dequantized to "
+                         "fp16 (E2M1 x E4M3 exact) for the PV MFMAs; f32 accumulate" if args.fp8q else
+                         "latent codes dequantized to fp16 (E2M1 x E4M3 exact) for QK and PV MFMAs, f32 accumulate")
                         if w.kind == "mla" else
                         "E4M3 query x cached FP8 codes on fp8 MFMA (QK); V codes to f16 MFMA operands (PV); f32 "
                         "accumulate" if args.fp8q else
@@ -634,11 +641,18 @@ def main():
     }
     traffic = measured_traffic(w, fp8q=args.fp8q)
     if w.kind == "mla":
-        flops = float(st["lens_h"].astype(np.int64).sum()) * w.q_heads * (w.head_dim + w.v_dim) * 2
+        ntok = float(st["lens_h"].astype(np.int64).sum())
+        qk_flops, pv_flops = ntok * w.q_heads * w.head_dim * 2, ntok * w.q_heads * w.v_dim * 2
+        flops = qk_flops + pv_flops
+        # FP8-domain: QK at the fp8 peak, PV at the fp16 peak; the peak quoted
+        # is the rate that would finish both at their own peaks in one time
+        peak = (flops / (qk_flops / PEAK_FP8_TFLOPS + pv_flops / PEAK_F16_TFLOPS) if args.fp8q
+                else PEAK_F16_TFLOPS)
         ach = flops / (kern_ms * 1e-3) / 1e12
-        res["roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                           "frac": round(ach / PEAK_F16_TFLOPS, 4), "traffic": traffic,
-                           "kernel": "decode_mla_kernel (fp16 MFMA)", "kernel_ms": round(kern_ms, 5),
+        res["roofline"] = {"bound": "mfma", "achieved": round(ach, 2), "peak": round(peak, 1), "unit": "TFLOP/s",
+                           "frac": round(ach / peak, 4), "traffic": traffic,
+                           "kernel": ("decode_mla_kernel (QK fp8 MFMA, PV fp16 MFMA)" if args.fp8q
+                                      else "decode_mla_kernel (fp16 MFMA)"), "kernel_ms": round(kern_ms, 5),
                            "algorithmic_flops_per_launch": flops,
                            "hbm_GBps": round(kv_bytes / (kern_ms * 1e-3) / 1e9, 2)}
     else:

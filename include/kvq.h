@@ -285,12 +285,20 @@ int kvq_decode_append(const kvq_cache* cache, const void* k_new, const void* v_n
  *   sm_scale * q_scale * k_scale * (E4M3(code) . K codes)
  * taken on FP8 matrix cores from the cached codes as they are; the softmax,
  * the value side and every other argument are kvq_decode's.
- *   q_scale: [dev] fp32, one value (cache scale_mode TENSOR) or
- *            [num_q_heads] (scale_mode HEAD), 4-byte aligned; NULL = 1.0.
- *            Queries beyond 448 * q_scale saturate.
- * Caches: GQA, E4M3 or E5M2, scale_mode TENSOR or HEAD (KVQ_ERR_UNSUPPORTED
- * otherwise: MX16 / NVFP4 codes are not FP8, KIVI folds a channel scale into
- * the query). Errors as kvq_decode. */
+ * MLA (NVFP4 latent): NVFP4 values are not FP8 values, so the keys are the
+ * E4M3 rows of the dequantize_prev_kv step ([P4] "code analysis") with the
+ * output scale 8g: K8 = RNE_E4M3(K^ / 8g), exact division, no saturation
+ * (|K^| <= 6 * 448 * g); the scores are
+ *   sm_scale * q_scale * 8g * (E4M3(code) . K8)
+ * on FP8 matrix cores, and the values stay the exact NVFP4 latent (V^ =
+ * K^[:v_dim], fp16 matrix cores), as in kvq_decode.
+ *   q_scale: [dev] fp32, one value (GQA scale_mode TENSOR, and MLA) or
+ *            [num_q_heads] (GQA scale_mode HEAD), 4-byte aligned; NULL =
+ *            1.0. Queries beyond 448 * q_scale saturate.
+ *   k_scale: GQA as kvq_decode; MLA the global scale g (required).
+ * Caches: GQA E4M3 or E5M2 with scale_mode TENSOR or HEAD, and MLA NVFP4
+ * (KVQ_ERR_UNSUPPORTED otherwise: MX16 codes are not FP8, KIVI folds a
+ * channel scale into the query). Errors as kvq_decode. */
 int kvq_decode_fp8q(const kvq_cache* cache, const void* q, int32_t batch, int32_t num_q_heads,
                     const int32_t* page_table, int32_t page_table_stride, const int32_t* seq_lens,
                     int32_t max_seq_len, float sm_scale, const float* q_scale, const float* k_scale,
@@ -315,6 +323,7 @@ int kvq_decode_append_fp8q(const kvq_cache* cache, const void* k_new, const void
  * (binary32 division; an all-zero tensor or head gives 1.0).
  *   q: [dev] BF16 [n_tokens][num_q_heads][head_dim], 16-byte aligned.
  * Uses the cache's scratch buffer: concurrent calls on one cache race.
+ * MLA caches (scale_mode TENSOR): one value over [n_tokens][num_q_heads][576].
  * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED (caches kvq_decode_fp8q rejects),
  * KVQ_ERR_HIP. n_tokens = 0 gives 1.0. */
 int kvq_compute_q_scale(const kvq_cache* cache, const void* q, int64_t n_tokens,

@@ -36,6 +36,23 @@
 //      a quarter of the rope group) into its buffer and issues the loads of
 //      step st + 3;
 // and the workgroup meets at a barrier after every second step.
+//
+// FP8-domain variant (kQ8: kvq_decode_fp8q and kvq_decode_append_fp8q on an
+// MLA cache; vLLM "Quantized KV Cache" page, overview: with an FP8 cache the
+// attention runs in FP8 and the query is quantized too). The query becomes
+// E4M3 codes of Q / q_scale (one scale per tensor), rounded like the FP8
+// store. NVFP4 values are not FP8 values, so the keys take the step the
+// PR #21954 analysis page gives dequantize_prev_kv: E4M3 codes of K^ / (8g),
+// i.e. each e2m1 * e4m3 product divided by 8 and rounded to nearest even
+// (every such value lies within +-336, so none saturates):
+//   S^T[t][h]  = K8[t][:] . Q8^T[:][h]     v_mfma_scale_f32_32x32x64_f8f6f4, unit scales
+// with the score scale sm_scale * q_scale * 8g. The value side stays exact:
+// V^ in fp16 and PV as above. The dequantization writes two token-major
+// tiles per step, E4M3 keys (576 elements, 592-byte rows) and fp16 values
+// (512 elements, 1,024-byte rows whose 16-byte chunks are XOR-swizzled by
+// row, so the four rows a transposed read covers fall in different banks).
+// Three such buffers fit the LDS: step st + 2 goes into the buffer step
+// st - 1 read, and the workgroup meets at a barrier after every step.
 #include <type_traits>
 
 #include "store_row.h"
@@ -56,10 +73,17 @@ constexpr int kStepTokens = kStepTiles * kTile;
 constexpr int kKRow = kDk * 2 + 16;           // bytes per token row of the LDS K^ tile (padded)
 constexpr int kBuf = kStepTokens * kKRow;     // one K^ buffer
 constexpr int kTileCodes = 4608, kTileScales = 576;
+// FP8-domain buffers: an E4M3 key tile and an fp16 value tile per step
+constexpr int kK8Row = kDk + 16;                      // bytes per token row of the E4M3 key tile (padded)
+constexpr int kVRow8 = kDv * 2;                       // bytes per token row of the fp16 value tile
+constexpr int kBufK8 = kStepTokens * kK8Row;          // the key tile, first in the buffer
+constexpr int kBuf8 = kBufK8 + kStepTokens * kVRow8;  // one FP8-domain buffer
 
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(2))) short s16x2;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
 
 __device__ __forceinline__ float f16_lo(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)); }
 __device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)); }
@@ -103,6 +127,18 @@ __device__ __forceinline__ void dequant16(const uint2 v, const uint32_t vs, uint
     x[tt] = make_uint2(__builtin_bit_cast(uint32_t, c[2 * tt] * sc[tt]), __builtin_bit_cast(uint32_t, c[2 * tt + 1] * sc[tt]));
 }
 
+// E4M3 codes of (4 fp16 values) / 8, rounded to nearest even (the scaled
+// convert divides by the power of two it is given)
+__device__ __forceinline__ uint32_t e4m3_over8(const uint2 x) {
+  s16x2 o = {0, 0};
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(o, __builtin_bit_cast(f16x2, x.x), 8.0f, false);
+  o = __builtin_amdgcn_cvt_scalef32_pk_fp8_f16(o, __builtin_bit_cast(f16x2, x.y), 8.0f, true);
+  return __builtin_bit_cast(uint32_t, o);
+}
+
+// 16-byte chunk swizzle of row r of the fp16 value tile (FP8-domain variant):
+// chunk c of the row is stored at chunk c ^ vswz(r)
+__device__ __forceinline__ int vswz(int r) { return 4 * ((r & 3) ^ ((r >> 1) & 2)); }
 
 // O *= alpha on accumulators that live in AGPRs, one element at a time
 // through a VGPR (VALU cannot read AGPRs), so the rare rescale does not pull
@@ -142,7 +178,8 @@ __device__ __forceinline__ void scale_acc(f32x16& o, float alpha) {
 // kWholeSteps: every 32-token step lies inside one page (pages of a multiple
 // of 32 tokens; splits are a whole number of steps), so a step needs one page
 // lookup and one buffer descriptor; otherwise every tile is looked up.
-template <bool kWholeSteps>
+// kQ8: the FP8-domain variant (E4M3 query and keys in the score products).
+template <bool kWholeSteps, bool kQ8>
 __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecodeArgs a) {
   const int unit = blockIdx.x;
   if (unit >= a.batch * a.num_splits) return;
@@ -170,7 +207,9 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
     return;
   }
 
-  __shared__ __attribute__((aligned(16))) uint8_t sm_k[4 * kBuf];
+  constexpr int kNBuf = kQ8 ? 3 : 4;                 // step buffers
+  constexpr int kBufBytes = kQ8 ? kBuf8 : kBuf;
+  __shared__ __attribute__((aligned(16))) uint8_t sm_k[kNBuf * kBufBytes];
   __shared__ int sm_pg[kMlaMaxSplitPages];
 
   const int tpp = a.page_size / kTile;
@@ -194,9 +233,34 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
 
   // ---- Q of this wave's 32 heads, per-head power-of-two scaled ----
   // B operand of k step ks: head h0 + r32, elements 16*ks + 8*hh .. +7
-  f16x8 qf[36];
+  // (kQ8: E4M3 codes of Q / q_scale, elements 64*ks + 32*hh .. +31)
+  f16x8 qf[kQ8 ? 1 : 36];
+  i32x8 q8[kQ8 ? 9 : 1];
   float sscale = 0.f;
-  if (head_ok) {
+  if constexpr (kQ8) {
+    const float qs = a.q_scale ? a.q_scale[0] : 1.0f;
+    sscale = a.sm_scale_log2 * (qs * (8.0f * a.g_scale[0]));
+    if (head_ok) {
+      const uint16_t* qrow = a.q + ((int64_t)b * a.hq + h0 + r32) * kDk;
+#pragma unroll
+      for (int ks = 0; ks < 9; ++ks) {
+        uint32_t w[8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint4 raw = *reinterpret_cast<const uint4*>(qrow + 64 * ks + 32 * hh + 8 * u);
+          // the same binary32 division and saturating RNE as the FP8 store
+          w[2 * u] = encode_fp8x4<KVQ_FP8_E4M3>(bf16_bits_to_f32(raw.x & 0xffffu) / qs, bf16_bits_to_f32(raw.x >> 16) / qs,
+                                                bf16_bits_to_f32(raw.y & 0xffffu) / qs, bf16_bits_to_f32(raw.y >> 16) / qs);
+          w[2 * u + 1] = encode_fp8x4<KVQ_FP8_E4M3>(bf16_bits_to_f32(raw.z & 0xffffu) / qs, bf16_bits_to_f32(raw.z >> 16) / qs,
+                                                    bf16_bits_to_f32(raw.w & 0xffffu) / qs, bf16_bits_to_f32(raw.w >> 16) / qs);
+        }
+        q8[ks] = __builtin_bit_cast(i32x8, w);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 9; ++ks) q8[ks] = i32x8{};
+    }
+  } else if (head_ok) {
     const uint16_t* qrow = a.q + ((int64_t)b * a.hq + h0 + r32) * kDk;
     uint32_t mx = 0;
 #pragma unroll
@@ -314,7 +378,13 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
       for (int tt = 0; tt < 4; ++tt) {
         if (kTail && tt >= nvalid) x[tt] = make_uint2(0u, 0u);
         const int row = 16 * s + 4 * g + tt;
-        *reinterpret_cast<uint2*>(buf + row * kKRow + 2 * (64 * (2 * wave + j) + 4 * col)) = x[tt];
+        if constexpr (kQ8) {
+          const int ch = (8 * (2 * wave + j) + (col >> 1)) ^ vswz(row);
+          *reinterpret_cast<uint2*>(buf + kBufK8 + row * kVRow8 + 16 * ch + 8 * (col & 1)) = x[tt];
+          *reinterpret_cast<uint32_t*>(buf + row * kK8Row + 64 * (2 * wave + j) + 4 * col) = e4m3_over8(x[tt]);
+        } else {
+          *reinterpret_cast<uint2*>(buf + row * kKRow + 2 * (64 * (2 * wave + j) + 4 * col)) = x[tt];
+        }
       }
     } else {
       const int s = c - 4;
@@ -327,7 +397,10 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
         if (!((S.ok >> s) & 1) || tok >= L) r0 = r1 = 0u;
       }
       const int row = 16 * s + 4 * r_g + r_tt;
-      *reinterpret_cast<uint2*>(buf + row * kKRow + 2 * (512 + 4 * r_i)) = make_uint2(r0, r1);
+      if constexpr (kQ8)  // the rope elements are keys only
+        *reinterpret_cast<uint32_t*>(buf + row * kK8Row + kDv + 4 * r_i) = e4m3_over8(make_uint2(r0, r1));
+      else
+        *reinterpret_cast<uint2*>(buf + row * kKRow + 2 * (512 + 4 * r_i)) = make_uint2(r0, r1);
     }
   };
   auto is_tail = [&](int tA, int ok) { return (tA + kStepTiles) * kTile > L || ok != (1 << kStepTiles) - 1; };
@@ -347,6 +420,16 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
   // gets element D + i of rows 0..3.
   const int tr_e = col >> 2, tr_c = col & 3;
   const int v_off = (4 * hh + tr_e) * kKRow + 2 * (16 * ((lane >> 4) & 1) + 4 * tr_c);
+  // kQ8: the same reads from the swizzled value tile. This lane's rows
+  // 16m + 4hh + tr_e (+8) all have swizzle 4 * e8, so the chunk 4db + x it
+  // reads sits at 4(db ^ e8) + x; v_off8[r] serves the blocks db with db % 4 = r.
+  const int e8 = tr_e ^ (2 * hh);
+  int v_off8[kQ8 ? 4 : 1] = {};
+  if constexpr (kQ8)
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    v_off8[r] = kBufK8 + (4 * hh + tr_e) * kVRow8 + 64 * (r ^ e8) + 16 * (2 * ((lane >> 4) & 1) + (tr_c >> 1)) +
+                8 * (tr_c & 1);
 
   // One step of loads is in flight while the previous step is scored and
   // accumulated: the raw registers are refilled right after they have been
@@ -371,23 +454,48 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
   dequant_all(sm_k);
   issue(R);
   int tA_1 = R.tA, ok_1 = R.ok;
-  dequant_all(sm_k + kBuf);
+  dequant_all(sm_k + kBufBytes);
   issue(R);
   __syncthreads();
+  int bc = 0;  // kQ8: buffer of the current step (st % 3)
 
   // Step st is read from buffer st % 4 while step st + 2 is dequantized into
   // buffer (st + 2) % 4 (last read by step st - 2, which every wave finished
   // before the last barrier); the workgroup meets after every odd step.
+  // kQ8: buffers st % 3 and (st + 2) % 3 (last read by step st - 1), and a
+  // barrier after every step.
   for (int st = 0; st < nsteps; ++st) {
-    const uint8_t* kb = sm_k + (st & 3) * kBuf;
-    uint8_t* nb = sm_k + ((st + 2) & 3) * kBuf;
+    const int bn = kQ8 ? (bc == 0 ? 2 : bc - 1) : ((st + 2) & 3);
+    const uint8_t* kb = sm_k + (kQ8 ? bc : (st & 3)) * kBufBytes;
+    uint8_t* nb = sm_k + bn * kBufBytes;
 
     // 1. S^T[token i][head h0 + r32] over all 576 elements from buffer kb,
     //    the K^ operand read three products ahead. Every product (here and
     //    in PV) is fenced from the scheduler: left free, it hoists all 36
     //    operand reads ahead of the chain and the wave runs out of VGPRs.
     f32x16 sc0;
-    {
+    if constexpr (kQ8) {
+      // 9 products of 64 elements: lane (r32, hh) supplies token r32's codes
+      // 64*ks + 32*hh .. +31, the same elements as its query operand
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sc0[i] = 0.f;
+      const uint8_t* krow = kb + r32 * kK8Row + 32 * hh;
+      auto kread = [&](int ks) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(krow + 64 * ks);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(krow + 64 * ks + 16);
+        return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      };
+      constexpr int kDepth = 3;
+      i32x8 ka[kDepth];
+#pragma unroll
+      for (int ks = 0; ks < kDepth - 1; ++ks) ka[ks] = kread(ks);
+#pragma unroll
+      for (int ks = 0; ks < 9; ++ks) {
+        if (ks + kDepth - 1 < 9) ka[(ks + kDepth - 1) % kDepth] = kread(ks + kDepth - 1);
+        sc0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[ks % kDepth], q8[ks], sc0, 0, 0, 0, 127, 0, 127);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
 #pragma unroll
       for (int i = 0; i < 16; ++i) sc0[i] = 0.f;
       const uint8_t* krow = kb + r32 * kKRow + 16 * hh;
@@ -461,9 +569,11 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
       constexpr int kVDepth = 3;  // V^T fragments read ahead of their products
       auto vread = [&](int j) {
         const int m = j >> 4, db = j & 15;
-        const uint8_t* vp = kb + v_off + (16 * m) * kKRow + 64 * db;
-        const u32x2 lo = lds_read_tr16(vp);               // tokens +0..3
-        const u32x2 hi = lds_read_tr16(vp + 8 * kKRow);   // tokens +8..11
+        constexpr int kRow = kQ8 ? kVRow8 : kKRow;
+        const uint8_t* vp = kQ8 ? kb + v_off8[db & 3] + (16 * m) * kRow + 256 * (db >> 2)
+                                : kb + v_off + (16 * m) * kRow + 64 * db;
+        const u32x2 lo = lds_read_tr16(vp);              // tokens +0..3
+        const u32x2 hi = lds_read_tr16(vp + 8 * kRow);   // tokens +8..11
         return __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
       };
       f16x8 va[kVDepth];
@@ -480,7 +590,8 @@ __global__ void __launch_bounds__(kThreads, 1) decode_mla_kernel(const MlaDecode
     const int tA_2 = R.tA, ok_2 = R.ok;
     dequant_all(nb);
     issue(R);
-    if (st & 1) __syncthreads();  // uniform: every wave runs the same steps
+    if (kQ8 || (st & 1)) __syncthreads();  // uniform: every wave runs the same steps
+    bc = kQ8 ? (bc == 2 ? 0 : bc + 1) : 0;
     tA_c = tA_1;
     ok_c = ok_1;
     tA_1 = tA_2;
@@ -521,9 +632,16 @@ hipError_t kvq_launch_decode_mla(const kvq_cache* c, const MlaDecodeArgs& a, hip
   (void)c;
   const int blocks = a.batch * a.num_splits;
   const int tpp = a.page_size / kvq::kTile;
-  if (tpp % kvq::kStepTiles == 0 && a.tiles_per_split % kvq::kStepTiles == 0)
-    kvq::decode_mla_kernel<true><<<blocks, kvq::kThreads, 0, s>>>(a);
-  else
-    kvq::decode_mla_kernel<false><<<blocks, kvq::kThreads, 0, s>>>(a);
+  const bool whole = tpp % kvq::kStepTiles == 0 && a.tiles_per_split % kvq::kStepTiles == 0;
+  if (a.q8) {
+    if (whole)
+      kvq::decode_mla_kernel<true, true><<<blocks, kvq::kThreads, 0, s>>>(a);
+    else
+      kvq::decode_mla_kernel<false, true><<<blocks, kvq::kThreads, 0, s>>>(a);
+  } else if (whole) {
+    kvq::decode_mla_kernel<true, false><<<blocks, kvq::kThreads, 0, s>>>(a);
+  } else {
+    kvq::decode_mla_kernel<false, false><<<blocks, kvq::kThreads, 0, s>>>(a);
+  }
   return hipGetLastError();
 }

@@ -399,8 +399,10 @@ int decode_impl(const kvq_cache* c, const void* k_new, const void* v_new, const 
                 bool static_ws = false) {
   if (!c || batch < 0 || hq < 1 || max_len < 0) return KVQ_ERR_ARG;
   if (q8) {
+    // FP8 GQA caches with tensor or head scales, and the NVFP4 MLA latent
     const kvq_cache_desc& d = c->desc;
-    if (d.kind != KVQ_GQA || !is_fp8(d.dtype) || d.scale_mode == KVQ_SCALE_KIVI) return KVQ_ERR_UNSUPPORTED;
+    const bool gqa = d.kind == KVQ_GQA && is_fp8(d.dtype) && d.scale_mode != KVQ_SCALE_KIVI;
+    if (!gqa && !(d.kind == KVQ_MLA && d.dtype == KVQ_NVFP4)) return KVQ_ERR_UNSUPPORTED;
     if (q_scale && reinterpret_cast<uintptr_t>(q_scale) % 4) return KVQ_ERR_ARG;
   }
   if (batch == 0) return KVQ_OK;
@@ -525,6 +527,8 @@ int decode_impl(const kvq_cache* c, const void* k_new, const void* v_new, const 
   a.out = out;
   a.lse = lse;
   a.new_k = static_cast<const uint16_t*>(k_new);
+  a.q8 = q8 ? 1 : 0;
+  a.q_scale = q_scale;
   hipError_t e;
   {
     Timed timer(1, s);
@@ -598,7 +602,8 @@ int kvq_compute_q_scale(const kvq_cache* c, const void* q, int64_t n_tokens, int
                         void* stream) {
   if (!c || !q_scale_out || n_tokens < 0 || num_q_heads < 1) return KVQ_ERR_ARG;
   const kvq_cache_desc& d = c->desc;
-  if (d.kind != KVQ_GQA || !is_fp8(d.dtype) || d.scale_mode == KVQ_SCALE_KIVI) return KVQ_ERR_UNSUPPORTED;
+  const bool gqa = d.kind == KVQ_GQA && is_fp8(d.dtype) && d.scale_mode != KVQ_SCALE_KIVI;
+  if (!gqa && !(d.kind == KVQ_MLA && d.dtype == KVQ_NVFP4)) return KVQ_ERR_UNSUPPORTED;
   if (num_q_heads % d.num_kv_heads) return KVQ_ERR_ARG;
   if (n_tokens > 0 && (!q || !aligned16(q))) return KVQ_ERR_ARG;
   if (d.scale_mode == KVQ_SCALE_HEAD && num_q_heads > kvq::kAmaxBlocks) return KVQ_ERR_UNSUPPORTED;

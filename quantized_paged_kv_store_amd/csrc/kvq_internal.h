@@ -155,6 +155,10 @@ struct MlaDecodeArgs {
   // optional append (kvq_decode_append): BF16 latent rows [B][576] of the token
   // at position seq_lens[b] - 1, quantized and written before it is read
   const uint16_t* new_k;
+  // FP8-domain attention (kvq_decode_fp8q): Q rounded to E4M3 with q_scale
+  // ([1]; null = 1.0), keys as E4M3 codes of K^ / (8g), values exact
+  int q8;
+  const float* q_scale;
 };
 
 struct CombineArgs {

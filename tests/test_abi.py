@@ -352,14 +352,17 @@ def test_extend_attention_argument_errors():
 
 
 def test_fp8q_decode_and_q_scale_argument_errors(handles):
-    """FP8-domain decode: FP8 GQA caches with tensor or per-head scales only;
-    q_scale 4-byte aligned; kvq_compute_q_scale's argument checks."""
+    """FP8-domain decode: FP8 GQA caches with tensor or per-head scales and the
+    NVFP4 MLA latent only; q_scale 4-byte aligned; kvq_compute_q_scale's
+    argument checks."""
     lib, h = handles
     P = c_void_p(FAKE_DEV)
 
     def dec(cache, qs=None, batch=4, hq=8):
         return lib.kvq_decode_fp8q(cache, P, batch, hq, P, 4, P, 64, 0.1, qs, None, None, P, None, None, 0, None)
-    assert dec(h["mx"]) == UNSUP and dec(h["mla"], hq=128) == UNSUP             # codes are not FP8
+    assert dec(h["mx"]) == UNSUP                                                 # codes are not FP8
+    assert dec(h["mla"], hq=128) == ARG                                          # MLA: g required
+    assert dec(h["mla"], hq=129) == UNSUP
     assert dec(h["fp8"], qs=c_void_p(FAKE_DEV + 2)) == ARG                       # misaligned q_scale
     assert dec(h["fp8"], batch=0) == OK                                          # empty batch
     assert dec(h["fp8"], hq=7) == ARG                                            # as kvq_decode
@@ -368,6 +371,7 @@ def test_fp8q_decode_and_q_scale_argument_errors(handles):
     assert app(h["fp8"], None, P) == ARG and app(h["fp8"], P, None) == ARG and app(h["mx"], P, P) == UNSUP
     q = lib.kvq_compute_q_scale
     assert q(h["mx"], P, 4, 8, P, None) == UNSUP
+    assert q(h["mla"], c_void_p(FAKE_DEV + 2), 4, 8, P, None) == ARG             # MLA served: past UNSUP
     assert q(h["fp8"], P, 4, 8, None, None) == ARG                               # no output
     assert q(h["fp8"], P, -1, 8, P, None) == ARG
     assert q(h["fp8"], P, 4, 7, P, None) == ARG                                  # Hq % Hkv

@@ -3,7 +3,9 @@ with an FP8 cache the attention runs in FP8, the query quantized like K and V,
 q_scale per tensor or per query head): query scales calibrated on the GPU
 bit-exact with the oracle's, and kvq_decode_fp8q / kvq_decode_append_fp8q
 within the parity tolerance of oracle.attention.decode_attention_fp8q fed the
-same stored codes and the same scales."""
+same stored codes and the same scales. On the NVFP4 MLA latent the keys are
+the E4M3 rows of the dequantize_prev_kv step (output scale 8g), checked
+against oracle.attention.decode_attention_mla_fp8q."""
 import numpy as np
 import pytest
 import torch
@@ -11,9 +13,9 @@ import torch
 import quantized_paged_kv_store_amd as K
 from oracle import formats as F
 from oracle import quantize as Q
-from oracle.attention import decode_attention_fp8q, quantize_query_fp8
+from oracle.attention import decode_attention_fp8q, decode_attention_mla_fp8q, mla_fp8_keys, quantize_query_fp8
 from quantized_paged_kv_store_amd import inputs as I
-from tests.kvq_cases import Case, assert_close
+from tests.kvq_cases import Case, assert_close, rel_l2
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -142,3 +144,111 @@ def test_fp8q_llama3_8b_shape_sampled():
                                         I.sm_scale(w), qs, c.k_scale, c.v_scale)
     torch.cuda.synchronize()
     _check(c, out, lse, qs_host, [0, 6], "fp8q llama3_8b")
+
+
+# ------------------------------------------------------------------ MLA --
+def _mla_workload(lens, hq=128, P=64, seed=23):
+    return I.Workload(f"fp8q-mla-{hq}", "nvfp4", "mla", len(lens), hq, 1, 576, 512, P, max(lens), 0, 1, "mla",
+                      seed=seed)
+
+
+def _mla_q_scale(c, how):
+    """Per-tensor query scale calibrated on the decode queries ("cal"), 1.0
+    (None), or 1/8 of the calibrated one so that queries saturate."""
+    if how == "none":
+        return None, None
+    s = K.kvq_compute_q_scale(c.cache, c.q_dev.view(c.w.batch, c.w.q_heads, c.w.head_dim))
+    host = s.cpu().numpy()
+    assert host.shape == (1,) and np.array_equal(host, Q.fp8_query_scales(I.bf16_to_f32(c.q), False))
+    if how == "stale":
+        s = s * 0.125
+        host = (host * np.float32(0.125)).astype(np.float32)
+    return s, host
+
+
+def _mla_lse_bound(oc, otable, qh, lens, g, sm, ids):
+    """1e-4 plus the FP8 matrix cores' accumulation error, taken (as for the
+    GQA caches above) as 2^-10 of sm * sum_d |q^_d k8^_d| for the worst token
+    of each (sequence, head), with k8^ the E4M3 key rows times 8g."""
+    bound = np.full(qh.shape[:2], 1e-4)
+    for b in ids:
+        L = int(lens[b])
+        if L == 0:
+            continue
+        k8, s8 = mla_fp8_keys(oc, otable[b], L, g)
+        kh = np.abs(F.decode(k8.astype(np.int64), F.E4M3)) * np.float64(s8)
+        bound[b] += 2.0 ** -10 * sm * (np.abs(qh[b]) @ kh.T).max(axis=1)
+    return bound
+
+
+def _mla_check(c, out, lse, qs_host, ids, what):
+    oc, otable, _, (g, _) = c.oracle(ids)
+    qf = I.bf16_to_f32(c.q).astype(np.float64)
+    sm = I.sm_scale(c.w)
+    want, wlse = decode_attention_mla_fp8q(oc, qf, otable, c.lens, sm, qs_host, g=g, batch_ids=ids)
+    o, l = out.cpu().numpy(), lse.cpu().numpy()
+    mab, r = assert_close(o[ids], want[ids], what)
+    codes, s = quantize_query_fp8(qf, qs_host)
+    qh = F.decode(codes.astype(np.int64), F.E4M3) * s[None, :, None].astype(np.float64)
+    bound = _mla_lse_bound(oc, otable, qh, c.lens, g, sm, ids)
+    fin = np.isfinite(wlse[ids])
+    assert np.array_equal(fin, np.isfinite(l[ids])), what
+    err = np.abs(l[ids][fin] - wlse[ids][fin])
+    assert np.all(err <= bound[ids][fin]), (what, float(err.max()))
+    for b in ids:
+        if c.lens[b] == 0:
+            assert np.all(o[b] == 0) and np.isneginf(l[b]).all()
+    return mab, r
+
+
+@pytest.mark.parametrize("hq,P,how", [(128, 64, "cal"), (128, 16, "none"), (64, 32, "cal"), (40, 64, "stale"),
+                                      (16, 16, "cal"), (1, 64, "cal")])
+def test_mla_fp8q_matches_oracle(hq, P, how):
+    lens = [0, 1, 17, 64, 100, 1000, 2500]
+    c = Case(_mla_workload(lens, hq, P), lens=lens).run_gpu(decode=False)
+    qs, qs_host = _mla_q_scale(c, how)
+    out, lse = K.kvq_decode_fp8q(c.cache, c.q_dev, c.table_dev, c.lens_dev, c.max_len, I.sm_scale(c.w), qs,
+                                 c.k_scale, None)
+    torch.cuda.synchronize()
+    _mla_check(c, out, lse, qs_host, list(range(len(lens))), f"mla fp8q Hq{hq} P{P} {how}")
+
+
+def test_mla_fp8q_splits_and_append():
+    """Several splits per sequence (the merge path), and the one-launch
+    append bit-identical to store + decode."""
+    lens = [9000, 4097, 33, 2]
+    w = _mla_workload(lens, seed=29)
+    a = Case(w, lens=lens).run_gpu(decode=False)
+    b = Case(w, lens=lens, data=a.data).run_gpu(decode=False, append=True)
+    qs, qs_host = _mla_q_scale(a, "cal")
+    outs = []
+    for target in (1, 0, 4096):
+        with K.split_target(a.cache, target):
+            outs.append(K.kvq_decode_fp8q(a.cache, a.q_dev, a.table_dev, a.lens_dev, a.max_len, I.sm_scale(w), qs,
+                                          a.k_scale, None))
+    ob, lb = K.kvq_decode_append_fp8q(b.cache, b.append_rows[0], None, b.q_dev, b.table_dev, b.lens_dev, b.max_len,
+                                      I.sm_scale(w), qs, b.k_scale, None)
+    torch.cuda.synchronize()
+    for name in ("k_codes", "k_scales"):
+        assert torch.equal(a.cache.view(name), b.cache.view(name)), name
+    assert torch.equal(outs[1][0], ob) and torch.equal(outs[1][1], lb)
+    for o, l in outs:
+        _mla_check(a, o, l, qs_host, [0, 1, 2, 3], "mla fp8q splits")
+
+
+def test_mla_fp8q_dsr1_shape_sampled():
+    """The DeepSeek-R1 MLA decode shape (batch 64, 128 heads, context 65,536,
+    page 64) in the benchmark's launch configuration (one-launch append
+    step); oracle on sequences 0 and 63. Prints the quantization error of
+    both MLA paths against BF16 attention on the unquantized latent."""
+    w = I.WORKLOADS["dsr1_mla"]
+    c = Case(w).run_gpu(decode=False, append=True)
+    qs, qs_host = _mla_q_scale(c, "cal")
+    out, lse = K.kvq_decode_append_fp8q(c.cache, c.append_rows[0], None, c.q_dev, c.table_dev, c.lens_dev,
+                                        c.max_len, I.sm_scale(w), qs, c.k_scale, None)
+    o16, _ = K.kvq_decode(c.cache, c.q_dev, c.table_dev, c.lens_dev, c.max_len, I.sm_scale(w), c.k_scale, None)
+    torch.cuda.synchronize()
+    mab, r = _mla_check(c, out, lse, qs_host, [0, 63], "mla fp8q dsr1")
+    ref = c.unquantized(0)
+    print(f"dsr1_mla FP8-domain: max-abs {mab:.2e} rel-L2 {r:.2e} against the oracle; against BF16 attention "
+          f"rel-L2 {rel_l2(out.cpu().numpy()[0], ref):.3e} (fp16 path {rel_l2(o16.cpu().numpy()[0], ref):.3e})")
