@@ -149,12 +149,22 @@ def test_many_splits_merge(kind):
     assert np.allclose(l_many.cpu().numpy(), l_few.cpu().numpy(), rtol=0, atol=1e-4)
 
 
+def _tile_signs(t):
+    """BF16 bits of +1 for tokens in 16-token tiles 0, 1, 4, 5, ... and -1 in
+    tiles 2, 3, 6, 7, ...: every 4 tiles sum to 0."""
+    return np.where((t >> 5) & 1, np.uint16(0xBF80), np.uint16(0x3F80))
+
+
 def test_max_length_property():
     """The longest context decode accepts: 2,097,152 tokens = 128 splits of
     1,024 tiles. Every K row is the same, so the softmax weights are uniform;
     V cycles through 7 rows. Then out = the count-weighted mean of the 7
     dequantized V rows and LSE = sm_scale q.k^ + ln L, both from the oracle's
-    quantizer on those rows only; a lost or repeated tile moves the LSE."""
+    quantizer on those rows only. V's first 16 elements are +-1 instead, by
+    16-token tile in the pattern + + - - (see _tile_signs): their mean is
+    exactly 0, and a lost, repeated or misplaced tile or 32-token step moves
+    them by at least 16 / L = 7.6e-6, above the 1e-6 tolerance (the LSE
+    alone would move by only ln(L / (L - 16)) = 7.6e-6, below its 1e-4)."""
     from oracle import quantize as Q
     from oracle.formats import E4M3
     L, P = 128 * 1024 * 16, 16
@@ -165,7 +175,8 @@ def test_max_length_property():
     c = Case(w, lens=[L])
     t = np.arange(L)
     kp = np.broadcast_to(k0, (L, 1, 128)).copy()   # rows [n, Hkv, D]
-    vp = v7[t % 7][:, None, :]
+    vp = v7[t % 7][:, None, :].copy()
+    vp[:, 0, :16] = _tile_signs(t)[:, None]
     c.data = {"pre": (kp, vp, I.slots_for(c.table[0], t, P)), "new": (None, None, np.zeros(0, np.int64))}
     c.run_gpu()
     assert K.kvq_decode_workspace_bytes(c.cache, 1, 4, L) == 4 * 128 * (128 + 1) * 4  # 128 splits
@@ -174,6 +185,7 @@ def test_max_length_property():
     vhat = Q.dequantize_fp8(Q.quantize_fp8(I.bf16_to_f32(v7).astype(np.float64), vs, E4M3), vs, E4M3)
     counts = np.bincount(t % 7, minlength=7).astype(np.float64)
     want = counts @ vhat / L
+    want[:16] = 0.0      # +-1 (symmetric codes) in equal numbers
     q = I.bf16_to_f32(c.q[0]).astype(np.float64)
     want_lse = I.sm_scale(w) * (q @ khat) + np.log(L)
     got, glse = c.out.cpu().numpy()[0], c.lse.cpu().numpy()[0]
@@ -187,7 +199,10 @@ def test_mla_max_length_property():
     has the same rope dims, so the weights are uniform while the value part
     (dims 0..511) cycles through 7 rows: out = their count-weighted mean after
     NVFP4 rounding, LSE = sm_scale q_rope.k^_rope + ln L (the oracle's
-    quantizer on the 7 rows; the rope dims are whole 16-element blocks)."""
+    quantizer on the 7 rows; the rope dims are whole 16-element blocks). The
+    first 16-element block is +-1 by 16-token tile (+ + - -): its mean is 0,
+    and a lost, repeated or misplaced tile or 32-token step moves it by at
+    least 16 / L, above the 1e-6 tolerance."""
     from oracle import quantize as Q
     L, P = 128 * 1024 * 16, 64
     w = I.Workload("mla-maxlen", "nvfp4", "mla", 1, 16, 1, 576, 512, P, L, L, 0, "mla", seed=13)
@@ -196,7 +211,9 @@ def test_mla_max_length_property():
                                       axis=1).astype(np.float32))
     c = Case(w, lens=[L])
     t = np.arange(L)
-    c.data = {"pre": (rows[t % 7], None, I.slots_for(c.table[0], t, P)), "new": (None, None, np.zeros(0, np.int64))}
+    lat_rows = rows[t % 7]
+    lat_rows[:, :16] = _tile_signs(t)[:, None]
+    c.data = {"pre": (lat_rows, None, I.slots_for(c.table[0], t, P)), "new": (None, None, np.zeros(0, np.int64))}
     c.run_gpu(decode=False)
     qz = c.q.copy()
     qz[..., :512] = 0
@@ -206,6 +223,7 @@ def test_mla_max_length_property():
     lat = Q.dequantize_nvfp4(*Q.quantize_nvfp4(I.bf16_to_f32(rows).astype(np.float64), g), g)
     counts = np.bincount(t % 7, minlength=7).astype(np.float64)
     want = counts @ lat[:, :512] / L
+    want[:16] = 0.0      # a block of equal magnitudes: +-(the same value) in equal numbers
     q = I.bf16_to_f32(qz[0]).astype(np.float64)
     want_lse = I.sm_scale(w) * (q[:, 512:] @ lat[0, 512:]) + np.log(L)
     got, glse = o.cpu().numpy()[0], l.cpu().numpy()[0]
