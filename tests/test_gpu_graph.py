@@ -136,9 +136,13 @@ def test_graph_replay_dequant_prev_and_extend_match_eager():
         _ = (q.float() * 2).sum().item()
 
 
-def test_graph_replay_fp8q_append_matches_eager():
-    """FP8-domain append step (kvq_decode_append_fp8q) captured in a HIP graph."""
-    w = I.WORKLOADS["llama3_8b"].with_(batch=2, max_len=3000, min_len=3000, scale_mode="amax_head")
+@pytest.mark.parametrize("name", ["llama3_8b", "dsr1_mla"])
+def test_graph_replay_fp8q_append_matches_eager(name):
+    """FP8-domain append step (kvq_decode_append_fp8q) captured in a HIP graph
+    (GQA with per-head query scales; the MLA latent with one)."""
+    w = I.WORKLOADS[name].with_(batch=2, max_len=3000, min_len=3000)
+    if name == "llama3_8b":
+        w = w.with_(scale_mode="amax_head")
     c = Case(w).run_gpu(decode=False, append=True)
     qs = K.kvq_compute_q_scale(c.cache, c.q_dev)
     need = K.kvq_decode_workspace_bytes(c.cache, w.batch, w.q_heads, c.max_len)
