@@ -88,10 +88,14 @@ def quantize_fp8_per_token(x, fmt: Format) -> tuple[np.ndarray, np.ndarray]:
 
 def quantize_fp8(x, scale, fmt: Format) -> np.ndarray:
     """codes = encode(fl32(x / scale)); x holds BF16 values (exact in fp32);
-    scale is a binary32 scalar or an array broadcast against x."""
+    scale is a binary32 scalar or an array broadcast against x. A finite x
+    whose binary32 quotient overflows lies past every format maximum and
+    saturates like any other such value (the overflow reading: saturate)."""
     x32 = fl32(x)
-    q = x32 / np.asarray(scale, dtype=np.float32)
-    return encode(q.astype(np.float64), fmt)
+    with np.errstate(over="ignore"):
+        q = (x32 / np.asarray(scale, dtype=np.float32)).astype(np.float64)
+    q = np.where(np.isinf(q) & np.isfinite(x32), np.copysign(fmt.max_value, q), q)
+    return encode(q, fmt)
 
 
 def dequantize_fp8(codes, scale, fmt: Format) -> np.ndarray:

@@ -48,6 +48,19 @@ def test_fp8_roundtrip_error_bound(fmt, rel):
     assert np.all(np.abs(x - xh) <= bound)
 
 
+@pytest.mark.parametrize("fmt", [F.E4M3, F.E5M2])
+def test_fp8_quotient_overflow_saturates(fmt):
+    """x / s past binary32's range is a value past the format maximum: it
+    takes the saturated code with x's sign, the same code as a quotient just
+    past the maximum, while a quotient just inside it still rounds."""
+    s = np.float32(2.0 ** -70)
+    x = np.array([3.0e38, -3.0e38, 2.0 ** 60, -(2.0 ** 60), 2.0 ** -70, fmt.max_value * 2.0 ** -70])
+    codes = Q.quantize_fp8(x, s, fmt)
+    top = fmt.max_code
+    assert list(codes) == [top, top | fmt.sign_bit, top, top | fmt.sign_bit, int(Q.quantize_fp8(1.0, 1.0, fmt)), top]
+    assert list(Q.quantize_fp8(np.array([3.0e38, -3.0e38]), np.float32(1.0), fmt)) == [top, top | fmt.sign_bit]
+
+
 def test_fp8_scale_default_and_zero_tensor():
     assert Q.fp8_scale(0.0, F.E4M3) == 1.0
     codes = Q.quantize_fp8(np.array([0.0, -0.0, 1.0]), 1.0, F.E4M3)
