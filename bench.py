@@ -104,6 +104,16 @@ def setup(w, dev, rotate, fp8q=False):
         ks = K.kvq_compute_scale(cache, kd)
     K.kvq_store(cache, kd, vd, sd, ks, vs)
     torch.cuda.synchronize(dev)
+    # the bulk store once more, timed: it writes the same bytes again
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    K.kvq_store(cache, kd, vd, sd, ks, vs)
+    e1.record()
+    torch.cuda.synchronize(dev)
+    bulk_ms = e0.elapsed_time(e1)
+    bulk_bytes = kd.numel() * 2 * (2 if vd is not None else 1) + n_pre * K.kvq_bytes_per_token(cache.desc)
+    bulk = {"tokens": n_pre, "ms": round(bulk_ms, 4), "GBps": round(bulk_bytes / (bulk_ms * 1e-3) / 1e9, 1),
+            "bytes": "BF16 rows read + codes and scales written"}
     del kd, vd, sd
     caches = [cache] + [K.Cache(cache.desc, cache.memory.clone()) for _ in range(rotate - 1)]
     # the new tokens stored by every step
@@ -132,7 +142,7 @@ def setup(w, dev, rotate, fp8q=False):
     qs = K.kvq_compute_q_scale(cache, q) if fp8q else None
     return dict(caches=caches, new=(new_k, new_v, new_s), new_rows=new_rows, q=q, table=table_d, lens=lens_d, lens_h=lens,
                 max_len=max_len, ks=ks, vs=vs, out=out, lse=lse, ws=ws, sm=I.sm_scale(w),
-                bpt=K.kvq_bytes_per_token(cache.desc), fp8q=fp8q, qs=qs)
+                bpt=K.kvq_bytes_per_token(cache.desc), fp8q=fp8q, qs=qs, bulk_store=bulk)
 
 
 def run_loop(st, steps, do_store, do_decode, offset=0, fused=False):
@@ -638,6 +648,7 @@ def main():
         "store_then_decode_ms": round(ms_sep, 5),
         "context_tokens_per_s": round(float(st["lens_h"].sum()) / (ms_step * 1e-3), 1),
         "decode_tokens_per_s": round(w.batch / (ms_step * 1e-3), 1),
+        "bulk_store": st["bulk_store"],
     }
     traffic = measured_traffic(w, fp8q=args.fp8q)
     if w.kind == "mla":

@@ -394,7 +394,8 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
           reinterpret_cast<float*>(const_cast<uint8_t*>(a.v_scales) + (int64_t)page * page_scale + head_scale)[t] = vs;
       } else {
         const int64_t base = (int64_t)page * page_code + head_code + (int64_t)(t >> 4) * tile_code_bytes;
-        put_fp8_chunk<FMT>(a.new_k + row, a.new_v + row, tid, t & 15, kscale, vscale, kc, vc, base);
+        put_fp8_chunk<FMT>(a.new_k + row, a.new_v + row, tid, t & 15, make_divisor(kscale), make_divisor(vscale), kc, vc,
+                           base);
       }
     }
   }

@@ -151,7 +151,12 @@ __global__ void __launch_bounds__(256) amax_chan_final_kernel(const unsigned* __
 }
 
 // one thread per (token, kv head, 16-element chunk); the D/16 chunks of a row
-// are consecutive lanes (the KIVI V row amax is reduced across them)
+// are consecutive lanes (the KIVI V row amax is reduced across them). A V
+// lane word holds one element of four consecutive tokens (t16 = 4g..4g+3):
+// when the four tokens of this token's group are the four consecutive list
+// entries around it (a prefill or chunk), their threads write whole words,
+// each thread four elements of all four tokens; otherwise every token writes
+// its own bytes, so the rest of a word is never touched.
 template <int FMT>
 __global__ void __launch_bounds__(256) store_fp8_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const int64_t* __restrict__ slots,
@@ -179,9 +184,22 @@ __global__ void __launch_bounds__(256) store_fp8_kernel(
     return;
   }
   const int si = mode == KVQ_SCALE_HEAD ? h : 0;
-  const float ks = k_scale ? k_scale[si] : 1.0f;
-  const float vs = v_scale ? v_scale[si] : 1.0f;
-  put_fp8_chunk<FMT>(k + row, v + row, c, t16, ks, vs, kc, vc, base);
+  const Divisor ks = make_divisor(k_scale ? k_scale[si] : 1.0f);
+  const Divisor vs = make_divisor(v_scale ? v_scale[si] : 1.0f);
+  const int i = t16 & 3;
+  const int64_t j0 = tok - i;  // list position of the group's first token, if the group is whole
+  bool whole = j0 >= 0 && j0 + 3 < n_tok;
+  if (whole) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) whole = whole && slots[j0 + u] == slot - i + u;
+  }
+  if (!whole) {
+    put_fp8_chunk<FMT>(k + row, v + row, c, t16, ks, vs, kc, vc, base);
+    return;
+  }
+  const uint4* kp = reinterpret_cast<const uint4*>(k + row + 16 * c);
+  *reinterpret_cast<uint4*>(kc + base + 256 * c + 16 * t16) = quant_fp8_16<FMT>(kp[0], kp[1], ks);
+  put_fp8_v_group<FMT>(v + (j0 * hkv + h) * dim, (int64_t)hkv * dim, c, t16 >> 2, i, vs, vc, base);
 }
 
 // one thread per (token, kv head, 16-element block)

@@ -22,6 +22,34 @@
 
 namespace kvq {
 
+// ------------------------------------------------------ binary32 quotient --
+// x / s for many x and one s, correctly rounded, without a division per
+// element. With r = RN(1/s) and q0 = RN(x r), the remainder x - s q0 is exact
+// in one FMA and RN(q0 + (x - s q0) r) = RN(x / s) (Markstein's theorem for
+// a correctly rounded reciprocal) while nothing underflows or overflows:
+// |x| >= 2^-100 and 2^-100 <= |q0| <= 2^100, for s in [2^-60, 2^60]. Past
+// those bounds q0 is kept: it has the quotient's sign and lies below 2^-40
+// or above 2^99 with it, where every FP8 and E2M1 encoder gives the same
+// code (a signed zero or the saturated maximum). Other divisors divide.
+struct Divisor {
+  float s, r;
+  bool fast;
+};
+__device__ __forceinline__ Divisor make_divisor(float s) {
+  Divisor d;
+  d.s = s;
+  d.fast = s >= 0x1p-60f && s <= 0x1p60f;
+  d.r = d.fast ? 1.0f / s : 0.0f;  // IEEE binary32 division
+  return d;
+}
+__device__ __forceinline__ float quotient(float x, const Divisor& d) {
+  if (!d.fast) return x / d.s;
+  const float q0 = x * d.r;
+  const float q1 = __builtin_fmaf(__builtin_fmaf(-d.s, q0, x), d.r, q0);
+  const float aq = __builtin_fabsf(q0);
+  return (__builtin_fabsf(x) >= 0x1p-100f && aq >= 0x1p-100f && aq <= 0x1p100f) ? q1 : q0;
+}
+
 // ------------------------------------------------------------------- FP8 --
 template <int FMT>
 __device__ __forceinline__ uint32_t encode_fp8x4(float a, float b, float c, float d) {
@@ -43,14 +71,14 @@ __device__ __forceinline__ uint32_t encode_fp8x4(float a, float b, float c, floa
 
 // 16 BF16 (two uint4) / s -> 16 FP8 codes (uint4).
 template <int FMT>
-__device__ __forceinline__ uint4 quant_fp8_16(const uint4 lo, const uint4 hi, float s) {
+__device__ __forceinline__ uint4 quant_fp8_16(const uint4 lo, const uint4 hi, const Divisor& s) {
   const uint32_t in[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   uint32_t out[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t w0 = in[2 * i], w1 = in[2 * i + 1];
-    out[i] = encode_fp8x4<FMT>(bf16_bits_to_f32(w0 & 0xffffu) / s, bf16_bits_to_f32(w0 >> 16) / s,
-                               bf16_bits_to_f32(w1 & 0xffffu) / s, bf16_bits_to_f32(w1 >> 16) / s);
+    out[i] = encode_fp8x4<FMT>(quotient(bf16_bits_to_f32(w0 & 0xffffu), s), quotient(bf16_bits_to_f32(w0 >> 16), s),
+                               quotient(bf16_bits_to_f32(w1 & 0xffffu), s), quotient(bf16_bits_to_f32(w1 >> 16), s));
   }
   return make_uint4(out[0], out[1], out[2], out[3]);
 }
@@ -58,8 +86,9 @@ __device__ __forceinline__ uint4 quant_fp8_16(const uint4 lo, const uint4 hi, fl
 // Chunk c (elements 16c..16c+15) of one (token, kv head) row pair. `base`
 // addresses the row's 16-token tile inside its (page, kv head) block.
 template <int FMT>
-__device__ __forceinline__ void put_fp8_chunk(const uint16_t* krow, const uint16_t* vrow, int c, int t16, float ks,
-                                              float vs, uint8_t* kc, uint8_t* vc, int64_t base) {
+__device__ __forceinline__ void put_fp8_chunk(const uint16_t* krow, const uint16_t* vrow, int c, int t16,
+                                              const Divisor& ks, const Divisor& vs, uint8_t* kc, uint8_t* vc,
+                                              int64_t base) {
   const uint4* kp = reinterpret_cast<const uint4*>(krow + 16 * c);
   const uint4* vp = reinterpret_cast<const uint4*>(vrow + 16 * c);
   const uint4 kq = quant_fp8_16<FMT>(kp[0], kp[1], ks);
@@ -71,6 +100,29 @@ __device__ __forceinline__ void put_fp8_chunk(const uint16_t* krow, const uint16
   const uint32_t vw[4] = {vq.x, vq.y, vq.z, vq.w};
 #pragma unroll
   for (int r = 0; r < 16; ++r) vb[16 * r] = (uint8_t)(vw[r >> 2] >> (8 * (r & 3)));
+}
+
+// Store of four tokens that fill one 4-token group of a tile (t16 = 4g..4g+3),
+// whose V codes share lane words: the caller for group member i writes
+// elements 16c + 4i .. +3 of all four V rows, one 4-byte word per element.
+// vrow0 is the first member's V row; the rows are `stride` elements apart.
+template <int FMT>
+__device__ __forceinline__ void put_fp8_v_group(const uint16_t* vrow0, int64_t stride, int c, int g, int i,
+                                                const Divisor& vs, uint8_t* vc, int64_t base) {
+  float x[4][4];  // [token][element]
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    const uint2 w = *reinterpret_cast<const uint2*>(vrow0 + tt * stride + 16 * c + 4 * i);
+    x[tt][0] = bf16_bits_to_f32(w.x & 0xffffu);
+    x[tt][1] = bf16_bits_to_f32(w.x >> 16);
+    x[tt][2] = bf16_bits_to_f32(w.y & 0xffffu);
+    x[tt][3] = bf16_bits_to_f32(w.y >> 16);
+  }
+  uint8_t* vb = vc + base + 1024 * (c >> 2) + 16 * (16 * g + 4 * i) + 4 * (c & 3);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    *reinterpret_cast<uint32_t*>(vb + 16 * k) = encode_fp8x4<FMT>(
+        quotient(x[0][k], vs), quotient(x[1][k], vs), quotient(x[2][k], vs), quotient(x[3][k], vs));
 }
 
 // ------------------------------------------------ FP8, KIVI-style scaling --
@@ -118,6 +170,7 @@ __device__ __forceinline__ float put_fp8_chunk_kivi(const uint16_t* krow, const 
   for (int off = 1; off < chunks; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
   const float amax = bf16_bits_to_f32(m);
   const float vs = amax == 0.f ? 1.0f : amax / MX;  // IEEE binary32 division
+  const Divisor vd = make_divisor(vs);
   float kss[16];
   const float4* kq4 = reinterpret_cast<const float4*>(ks + 16 * c);
 #pragma unroll
@@ -129,7 +182,7 @@ __device__ __forceinline__ float put_fp8_chunk_kivi(const uint16_t* krow, const 
     kss[4 * i + 3] = q.w;
   }
   const uint4 kq = quant_fp8_16_vec<FMT>(kp[0], kp[1], kss);
-  const uint4 vq = quant_fp8_16<FMT>(v0, v1, vs);
+  const uint4 vq = quant_fp8_16<FMT>(v0, v1, vd);
   *reinterpret_cast<uint4*>(kc + base + 256 * c + 16 * t16) = kq;
   uint8_t* vb = vc + base + 1024 * (c >> 2) + 16 * (16 * (t16 >> 2)) + 4 * (c & 3) + (t16 & 3);
   const uint32_t vw[4] = {vq.x, vq.y, vq.z, vq.w};
@@ -228,8 +281,9 @@ __device__ __forceinline__ void put_nvfp4_block(const uint16_t* row, int b, int 
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = __builtin_copysignf(0.0f, x[i]);
   } else {
+    const Divisor dd = make_divisor(sd);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = fminf(fmaxf(x[i] / sd, -6.0f), 6.0f);
+    for (int i = 0; i < 16; ++i) x[i] = fminf(fmaxf(quotient(x[i], dd), -6.0f), 6.0f);
   }
   const uint32_t c0 = encode_e2m1x8(x), c1 = encode_e2m1x8(x + 8);
   // MLA tile layout: the 4-element groups of one token and token quad sit in

@@ -75,6 +75,70 @@ def test_fp8_store_every_code_and_midpoint(dtype):
     _assert_bytes_equal(cache, oc)
 
 
+@pytest.mark.parametrize("dtype", ["e4m3", "e5m2"])
+def test_fp8_store_every_code_and_midpoint_in_word_groups(dtype):
+    """The same values stored in slot order, so V lane words are written whole
+    (four consecutive tokens at a time); the run starts and ends mid-group."""
+    fmt = F.E4M3 if dtype == "e4m3" else F.E5M2
+    vals = _values_fp8(fmt)
+    D, H = 128, 2
+    n_tok = -(-vals.size // (D * H))
+    x = np.zeros(n_tok * H * D)
+    x[: vals.size] = vals
+    k = x.reshape(n_tok, H, D)
+    v = np.random.default_rng(0).permutation(x).reshape(n_tok, H, D)
+    pages = -(-(n_tok + 3) // 16) + 1
+    spec = CacheSpec(dtype, "gqa", H, D, D, 16, pages)
+    slots = 3 + np.arange(n_tok)
+    cache, oc = _store_both(spec, k, v, slots)
+    _assert_bytes_equal(cache, oc)
+
+
+@pytest.mark.parametrize("scale", [2.0 ** -70, 2.0 ** -59, 0.0123, 3.0, 2.0 ** 59, 2.0 ** 70])
+def test_fp8_store_scale_range(scale):
+    """Scales inside and outside the range where the store divides by a
+    reciprocal and one correction; values from 2^-133 to 3e38 so that the
+    quotients reach zero, every code and saturation."""
+    rng = np.random.default_rng(7)
+    D, H, n_tok = 128, 2, 96
+    mag = 2.0 ** rng.uniform(-133, 127.5, (n_tok, H, D))
+    k = np.where(rng.random((n_tok, H, D)) < 0.5, -mag, mag)
+    v = rng.standard_normal((n_tok, H, D)) * scale * 100
+    spec = CacheSpec("e4m3", "gqa", H, D, D, 16, 8)
+    slots = np.concatenate([np.arange(1, 50), 64 + rng.permutation(47)])  # word groups, then single tokens
+    cache, oc = _store_both(spec, k, v, slots, k_scale=scale, v_scale=scale)
+    _assert_bytes_equal(cache, oc)
+
+
+def test_fp8_store_word_groups_and_partial_words():
+    """Runs that fill whole V lane words mixed with ones that do not: a run in
+    reverse order, a group with a gap, a group split over two calls and a
+    skipped slot; words shared with tokens that are not stored keep their
+    bytes."""
+    rng = np.random.default_rng(8)
+    D, H, P = 64, 3, 32
+    spec = CacheSpec("e4m3", "gqa", H, D, D, P, 6)
+    runs = [np.arange(5, 42),                      # starts and ends mid-group
+            np.arange(64, 84)[::-1],               # reverse order: no whole group
+            np.array([96, 97, 99, 100, 101, 102, 103]),  # 96..99 has a gap
+            np.array([128, 129])]                  # first half of a group
+    slots = np.concatenate(runs)
+    slots[20] = -1                                 # a skipped token inside a run
+    n1 = slots.size
+    k = rng.standard_normal((n1 + 2, H, D)) * 4
+    v = rng.standard_normal((n1 + 2, H, D)) * rng.lognormal(0, 0.5, (n1 + 2, 1, 1))
+    cache, oc = _store_both(spec, k[:n1], v[:n1], slots, k_scale=0.02, v_scale=0.01)
+    # the second half of the split group in a second call
+    kb = I.bf16_to_f32(I.bf16_bits(k[n1:].astype(np.float32)))
+    vb = I.bf16_to_f32(I.bf16_bits(v[n1:].astype(np.float32)))
+    s2 = np.array([130, 131])
+    K.kvq_store(cache, _bf16_dev(kb), _bf16_dev(vb), torch.from_numpy(s2).to(DEV),
+                torch.tensor([0.02], device=DEV), torch.tensor([0.01], device=DEV))
+    torch.cuda.synchronize()
+    oc.store(kb, vb, s2, k_scale=0.02, v_scale=0.01)
+    _assert_bytes_equal(cache, oc)
+
+
 @pytest.mark.parametrize("dtype,D,P", [("e4m3", 64, 16), ("e4m3", 128, 32), ("e5m2", 128, 16)])
 def test_fp8_store_random_with_scale(dtype, D, P):
     rng = np.random.default_rng(2)
@@ -142,6 +206,27 @@ def test_nvfp4_store_with_computed_global_scale():
     g = np.float32(g_dev.cpu().numpy()[0])
     assert g == Q.nvfp4_global_scale(np.abs(latb).max())
     slots = rng.permutation(spec.num_pages * 64)[:n_tok]
+    K.kvq_store(cache, _bf16_dev(latb), None, torch.from_numpy(slots.astype(np.int64)).to(DEV), g_dev)
+    torch.cuda.synchronize()
+    oc = OracleCache(spec, fill=0xFF)
+    oc.store(latb, None, slots, k_scale=g)
+    _assert_bytes_equal(cache, oc)
+
+
+@pytest.mark.parametrize("mag", [2.0 ** -56, 2.0 ** -40, 2.0 ** 50, 2.0 ** 100])
+def test_nvfp4_store_extreme_magnitudes(mag):
+    """Latents scaled so that the block divisors E4M3(s) * g fall inside and
+    outside the range where the store divides by a reciprocal."""
+    rng = np.random.default_rng(6)
+    n_tok = 70
+    lat = rng.standard_normal((n_tok, 576)) * mag
+    lat[3, 64:80] *= 2.0 ** -30                             # blocks far below the tensor maximum
+    latb = I.bf16_to_f32(I.bf16_bits(lat.astype(np.float32)))
+    spec = CacheSpec("nvfp4", "mla", 1, 576, 512, 64, 3)
+    cache = K.kvq_alloc_pages("nvfp4", "mla", 1, 576, 512, 64, spec.num_pages, device=DEV, fill=0xFF)
+    g_dev = K.kvq_compute_scale(cache, _bf16_dev(latb))
+    g = np.float32(g_dev.cpu().numpy()[0])
+    slots = np.arange(2, 2 + n_tok)
     K.kvq_store(cache, _bf16_dev(latb), None, torch.from_numpy(slots.astype(np.int64)).to(DEV), g_dev)
     torch.cuda.synchronize()
     oc = OracleCache(spec, fill=0xFF)
