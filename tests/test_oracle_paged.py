@@ -200,3 +200,56 @@ def test_kivi_cache_round_trip_on_grid():
         got = oc.v_token_scales()[page, h, t]
         assert np.array_equal(got, (np.float32(448.0 * vfac[:, h, 0]) / np.float32(448.0)).astype(np.float32))
     assert oc.v_scales.shape == (3, 2, 4 * 32) and spec.token_scale_block_bytes() == 128
+
+
+def _owner_map(spec, fn, n_elem):
+    """Token (t16) owning each byte of one tile of a (page, head) block, from
+    the position function fn. Asserts that no byte (or its two nibbles) is
+    shared by two tokens and that every byte of the tile is used."""
+    t, d = np.meshgrid(np.arange(16), np.arange(n_elem), indexing="ij")
+    byte, _ = fn(spec, t, d)
+    size = int(byte.max()) + 1
+    owner = np.full(size, -1)
+    for tt, bb in zip(t.ravel(), np.asarray(byte).ravel()):
+        assert owner[bb] in (-1, tt), f"byte {bb} holds codes of tokens {owner[bb]} and {tt}"
+        owner[bb] = tt
+    assert np.all(owner >= 0)
+    return owner
+
+
+@pytest.mark.parametrize("spec", SPECS, ids=lambda s: f"{s.dtype}-{s.head_dim}-P{s.page_size}")
+def test_layout_properties_the_header_states(spec):
+    """Properties include/kvq.h states in words (and the decode kernels' loads
+    rely on), checked on the layout functions without their formulas: every
+    byte holds codes of one token only; GQA K puts token t16 of a tile in the
+    t16-th 16-byte lane of every 256-byte group; FP8 V puts one element of
+    four consecutive tokens in each 4-byte word; FP4 V and the MLA latent put
+    four consecutive tokens of one 8- / 4-element group in each 16- / 8-byte
+    unit, token by token."""
+    D = spec.head_dim
+    fp8 = spec.dtype in ("e4m3", "e5m2")
+    if spec.kind == "gqa":
+        k_owner = _owner_map(spec, k_code_pos, D)
+        assert np.array_equal(k_owner, (np.arange(k_owner.size) % 256) // 16)
+        v_owner = _owner_map(spec, v_code_pos, D)
+        if fp8:
+            # byte i of each word: token 4g + i, the word's four bytes one element
+            words = v_owner.reshape(-1, 4)
+            assert np.all(words % 4 == np.arange(4)) and np.all(words // 4 == words[:, :1] // 4)
+            t, d = np.meshgrid(np.arange(16), np.arange(D), indexing="ij")
+            byte, _ = v_code_pos(spec, t, d)
+            word_elems = {}
+            for dd, bb in zip(d.ravel(), np.asarray(byte).ravel()):
+                word_elems.setdefault(bb // 4, set()).add(dd)
+            assert all(len(e) == 1 for e in word_elems.values())
+        else:
+            # each 16-byte lane: tokens 4g..4g+3, one 4-byte word each, one 8-element group
+            lanes = v_owner.reshape(-1, 16)
+            assert np.all(lanes == lanes[:, ::4].repeat(4, axis=1))
+            assert np.all(lanes[:, ::4] % 4 == np.arange(4)) and np.all(lanes[:, ::4] // 4 == lanes[:, :1] // 4)
+    else:
+        owner = _owner_map(spec, k_code_pos, D)
+        # each 8-byte unit: tokens 4g..4g+3, two bytes (one 4-element group) each
+        units = owner.reshape(-1, 8)
+        assert np.all(units == units[:, ::2].repeat(2, axis=1))
+        assert np.all(units[:, ::2] % 4 == np.arange(4)) and np.all(units[:, ::2] // 4 == units[:, :1] // 4)
