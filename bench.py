@@ -481,9 +481,10 @@ def bench_extend(w, args, dev):
     print(json.dumps(res), flush=True)
 
 
-def copy_reference(nbytes=1 << 30, reps=10):
+def copy_reference(nbytes=1 << 30, reps=10, quiet=False):
     """A plain device copy of known size (src -> dst), the reference the HBM
-    traffic counters are scaled by."""
+    traffic counters are scaled by; also reported beside the roofline as the
+    copy rate this GPU reaches (read + write bytes per second)."""
     import torch
     src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
@@ -496,8 +497,13 @@ def copy_reference(nbytes=1 << 30, reps=10):
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / reps
-    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "ms": round(ms, 4),
-                      "GBps_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
+    rec = {"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "ms": round(ms, 4),
+           "GBps_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
+    del src, dst
+    torch.cuda.empty_cache()
+    if not quiet:
+        print(json.dumps(rec), flush=True)
+    return rec
 
 
 def main():
@@ -678,6 +684,8 @@ def main():
                         "decode_without_store": round(kern_only_ms, 5)}
     res["decode_kernel_GBps"] = {"in_step": round(kv_bytes / (kern_ms * 1e-3) / 1e9, 2),
                                  "without_store": round(kv_bytes / (kern_only_ms * 1e-3) / 1e9, 2)}
+    # information only, after the timed region: what a plain 1 GiB device copy reaches here
+    res["device_copy_GBps_read_plus_write"] = copy_reference(quiet=True)["GBps_read_plus_write"]
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, fp8q=args.fp8q)
     print(json.dumps(res), flush=True)
