@@ -81,10 +81,10 @@ typedef enum kvq_status {
 typedef struct kvq_cache_desc {
   int32_t dtype;        /* kvq_dtype */
   int32_t kind;         /* kvq_kind */
-  int32_t num_kv_heads; /* GQA: Hkv >= 1; MLA: must be 1 */
+  int32_t num_kv_heads; /* GQA: 1 <= Hkv <= 4096; MLA: must be 1 */
   int32_t head_dim;     /* GQA: D; MLA: latent + rope dims (Dk) */
   int32_t v_dim;        /* GQA: must equal head_dim; MLA: latent dims (Dv) */
-  int32_t page_size;    /* tokens per page, a multiple of 16 */
+  int32_t page_size;    /* tokens per page, a multiple of 16, at most 65536 */
   int64_t num_pages;    /* physical pages in the pool, >= 1 */
   int32_t scale_mode;   /* kvq_scale_mode; KVQ_SCALE_HEAD and KVQ_SCALE_KIVI are for
                            FP8 GQA only, every other cache uses KVQ_SCALE_TENSOR.
@@ -200,7 +200,9 @@ int kvq_compute_scale(const kvq_cache* cache, const void* x0, int64_t n0, const 
  *         FP4_MX16: both unused (block exponents are computed here from each
  *         16-element block's amax: e = floor(log2 amax) - 2).
  * Inputs must be finite. Two tokens mapped to one slot race.
- * Errors: KVQ_ERR_ARG, KVQ_ERR_HIP. num_tokens == 0 is a no-op. */
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED (more than 2^32 - 256 16-element
+ * pieces in one call: num_tokens x rows x head_dim / 16, rows = num_kv_heads
+ * or 1 for MLA), KVQ_ERR_HIP. num_tokens == 0 is a no-op. */
 int kvq_store(const kvq_cache* cache, const void* k, const void* v,
               const int64_t* slot_mapping, int32_t num_tokens, const float* k_scale,
               const float* v_scale, void* stream);

@@ -22,6 +22,12 @@ constexpr int kMaxDecodeLen = 128 * 1024 * kvq::kTile;  // 128 splits x 1024 til
 constexpr int kGqaTargetWgs = 512;
 constexpr int kMlaTargetWgs = 256;
 constexpr int kMaxTargetWgs = 1 << 20;
+// Descriptor limits: they keep every per-page index of the kernels (int
+// arithmetic over num_kv_heads x page_size x head_dim) inside 32 bits.
+constexpr int kMaxPageSize = 1 << 16;
+constexpr int kMaxKvHeads = 1 << 12;
+// A launch covers at most 2^32 work-items (the dispatch's 32-bit grid size).
+constexpr int64_t kMaxLaunchItems = (int64_t(1) << 32) - 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -35,6 +41,7 @@ int check_desc(const kvq_cache_desc* d) {
   if (d->num_kv_heads < 1 || d->head_dim < 16 || d->v_dim < 1 || d->page_size < 1 || d->num_pages < 1)
     return KVQ_ERR_ARG;
   if (d->page_size % kvq::kTile) return KVQ_ERR_ARG;
+  if (d->page_size > kMaxPageSize || d->num_kv_heads > kMaxKvHeads) return KVQ_ERR_UNSUPPORTED;
   if (d->head_dim % 16) return KVQ_ERR_ARG;
   if (d->scale_mode < KVQ_SCALE_TENSOR || d->scale_mode > KVQ_SCALE_KIVI) return KVQ_ERR_ARG;
   if (d->scale_mode != KVQ_SCALE_TENSOR && !(d->kind == KVQ_GQA && is_fp8(d->dtype))) return KVQ_ERR_UNSUPPORTED;
@@ -359,6 +366,9 @@ int kvq_store(const kvq_cache* c, const void* k, const void* v, const int64_t* s
     if (v) return KVQ_ERR_ARG;
     if (!k_scale) return KVQ_ERR_ARG;  // NVFP4 needs its global scale
   }
+  // one thread per 16 elements of every stored row
+  const int64_t rows = c->desc.kind == KVQ_GQA ? c->desc.num_kv_heads : 1;
+  if ((int64_t)n * rows * (c->desc.head_dim / 16) > kMaxLaunchItems) return KVQ_ERR_UNSUPPORTED;
   Timed timer(0, static_cast<hipStream_t>(stream));
   const hipError_t e = kvq_launch_store(c, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), slots, n,
                                         k_scale, v_scale, static_cast<hipStream_t>(stream));
@@ -415,7 +425,7 @@ int decode_impl(const kvq_cache* c, const void* k_new, const void* v_new, const 
   // the length cap first: it keeps the page count below in range
   if (max_len > kMaxDecodeLen) return KVQ_ERR_UNSUPPORTED;
   const int P = d.page_size;
-  if (page_table_stride < (max_len + P - 1) / P || page_table_stride < 1) return KVQ_ERR_ARG;
+  if (page_table_stride < ((int64_t)max_len + P - 1) / P || page_table_stride < 1) return KVQ_ERR_ARG;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   if (d.kind == KVQ_GQA) {
     if (hq % d.num_kv_heads) return KVQ_ERR_ARG;

@@ -95,6 +95,8 @@ def test_alloc_query_bind_and_layout():
     (dict(n=0), ARG),
     (dict(dv=64), ARG),
     (dict(d=100), ARG),
+    (dict(p=65536 + 16), UNSUP),
+    (dict(hkv=4097), UNSUP),
 ])
 def test_alloc_rejects_bad_descriptors(desc, status):
     lib = _lib()
@@ -142,6 +144,8 @@ def test_store_argument_errors(handles):
     assert lib.kvq_store(h["mla"], P, P, P, 4, P, None, None) == ARG            # MLA has no V input
     assert lib.kvq_store(h["mla"], P, None, P, 4, None, None, None) == ARG      # NVFP4 needs g
     assert lib.kvq_store(None, P, P, P, 4, None, None, None) == ARG
+    # one launch covers at most 2^32 work-items: 2 KV heads x 8 pieces of 16 per token
+    assert lib.kvq_store(h["fp8"], P, P, P, 2**31 - 1, None, None, None) == UNSUP
 
 
 def test_compute_scale_argument_errors(handles):
