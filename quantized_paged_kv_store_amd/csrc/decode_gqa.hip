@@ -50,6 +50,8 @@ constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kPBias = 15.0f;  // p carries a factor 2^15
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kMaxSplitTiles = 1024;  // host keeps tiles_per_split <= this
+// s_waitcnt operand: vector memory count 0, the other counters unconstrained
+constexpr int kWaitVm0 = 0x0f70;
 
 // raw per-lane bytes of one 16-token tile
 template <int FMT, int D>
@@ -364,39 +366,68 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
 
   const int npairs = (t_end - t_begin + 1) >> 1;
 
+  // Append (kvq_decode_append): the split holding position L-1 quantizes the
+  // new token's K/V rows and writes them into the cache before any of its
+  // tile loads; the barrier below orders those stores before this
+  // workgroup's reads of the tile (no other workgroup reads it). The token's
+  // page id and rows are loaded ahead of the page-id staging, so the two
+  // latencies overlap and the appending workgroup starts its tile loads
+  // about when the others do.
+  // FP8 with tensor or head scales: wave 0's 64 lanes share the token, D / 32
+  // elements of K (lanes 0-31) or V (lanes 32-63) each; KIVI and FP4 blocks
+  // need a whole 16-element chunk per lane (lanes 0 .. D/16 - 1).
+  constexpr bool kElems = FMT != KVQ_FP4_MX16 && !KIVI;
+  constexpr int kEpl = D / 32;
+  const int pos = L - 1;
+  const bool app = a.new_k != nullptr && pos / kTile < t_end && pos / kTile >= t_begin &&
+                   tid < (kElems ? 64 : D / 16);
+  int app_page = -1;
+  RowChunk nr;
+  uint2 ne;
+  float nks[KIVI ? 16 : 1];
+  if (app) {
+    app_page = pt[pos / a.page_size];
+    const int64_t row = ((int64_t)b * a.hkv + kvh) * D;
+    if constexpr (kElems) {
+      const uint16_t* src = (tid < 32 ? a.new_k : a.new_v) + row + kEpl * (tid & 31);
+      if constexpr (kEpl == 4)
+        ne = *reinterpret_cast<const uint2*>(src);
+      else
+        ne = make_uint2(*reinterpret_cast<const uint32_t*>(src), 0u);
+    } else {
+      nr = load_row_chunk(a.new_k + row, a.new_v + row, tid);
+      if constexpr (KIVI) load_chan_scales(a.k_scale + (int64_t)kvh * D, tid, nks);
+    }
+  }
   // page ids of this split, staged once in LDS
   __shared__ int sm_pg[kMaxSplitTiles];
   const int fp = t_begin / tpp;
   const int n_pg = (t_end - 1) / tpp - fp + 1;
   for (int i = tid; i < n_pg; i += 256) sm_pg[i] = pt[fp + i];
-  // Append (kvq_decode_append): the split holding position L-1 quantizes the
-  // new token's K/V rows and writes them into the cache before any of its
-  // loads; the barrier below orders those stores before this workgroup's
-  // reads of the tile (no other workgroup reads it).
-  if (a.new_k != nullptr && (L - 1) / kTile < t_end && (L - 1) / kTile >= t_begin && tid < D / 16) {
-    const int pos = L - 1;
-    const int page = pt[pos / a.page_size];
-    if ((unsigned)page < (unsigned)a.num_pages) {
-      const int t = pos % a.page_size;
-      const int64_t row = ((int64_t)b * a.hkv + kvh) * D;
-      uint8_t* kc = const_cast<uint8_t*>(a.k_codes);
-      uint8_t* vc = const_cast<uint8_t*>(a.v_codes);
-      if constexpr (FMT == KVQ_FP4_MX16) {
-        const int64_t cbase = (int64_t)page * page_code + head_code + (int64_t)(t >> 4) * tile_code_bytes;
-        const int64_t sbase = (int64_t)page * page_scale + head_scale + (int64_t)(t >> 4) * tile_scale_bytes;
-        put_mx16_block(a.new_k + row, a.new_v + row, tid, D / 16, D, t & 15, kc, vc, const_cast<uint8_t*>(a.k_scales),
-                       const_cast<uint8_t*>(a.v_scales), cbase, sbase);
-      } else if constexpr (KIVI) {
-        const int64_t base = (int64_t)page * page_code + head_code + (int64_t)(t >> 4) * tile_code_bytes;
-        const float vs = put_fp8_chunk_kivi<FMT>(a.new_k + row, a.new_v + row, tid, D / 16, t & 15,
-                                                 a.k_scale + (int64_t)kvh * D, kc, vc, base);
-        if (tid == 0)
-          reinterpret_cast<float*>(const_cast<uint8_t*>(a.v_scales) + (int64_t)page * page_scale + head_scale)[t] = vs;
-      } else {
-        const int64_t base = (int64_t)page * page_code + head_code + (int64_t)(t >> 4) * tile_code_bytes;
-        put_fp8_chunk<FMT>(a.new_k + row, a.new_v + row, tid, t & 15, make_divisor(kscale), make_divisor(vscale), kc, vc,
-                           base);
-      }
+  // every load above has arrived: otherwise a path that skips the append
+  // joins with the rows still in flight, and the compiler then waits after
+  // the barrier for all memory operations, the append's stores included
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  if (app && (unsigned)app_page < (unsigned)a.num_pages) {
+    const int page = app_page;
+    const int t = pos % a.page_size;
+    uint8_t* kc = const_cast<uint8_t*>(a.k_codes);
+    uint8_t* vc = const_cast<uint8_t*>(a.v_codes);
+    if constexpr (FMT == KVQ_FP4_MX16) {
+      const int64_t cbase = (int64_t)page * page_code + head_code + (int64_t)(t >> 4) * tile_code_bytes;
+      const int64_t sbase = (int64_t)page * page_scale + head_scale + (int64_t)(t >> 4) * tile_scale_bytes;
+      put_mx16_block(nr, tid, D / 16, t & 15, kc, vc, const_cast<uint8_t*>(a.k_scales),
+                     const_cast<uint8_t*>(a.v_scales), cbase, sbase);
+    } else if constexpr (KIVI) {
+      const int64_t base = (int64_t)page * page_code + head_code + (int64_t)(t >> 4) * tile_code_bytes;
+      const float vs = put_fp8_chunk_kivi<FMT>(nr, nks, tid, D / 16, t & 15, kc, vc, base);
+      if (tid == 0)
+        reinterpret_cast<float*>(const_cast<uint8_t*>(a.v_scales) + (int64_t)page * page_scale + head_scale)[t] = vs;
+    } else {
+      const int64_t base = (int64_t)page * page_code + head_code + (int64_t)(t >> 4) * tile_code_bytes;
+      const bool is_v = tid >= 32;
+      put_fp8_elems<FMT, kEpl>(ne, is_v, kEpl * (tid & 31), t & 15, make_divisor(is_v ? vscale : kscale),
+                               is_v ? vc : kc, base);
     }
   }
   __syncthreads();

@@ -223,7 +223,7 @@ __global__ void __launch_bounds__(256) store_mx16_kernel(
   const int64_t row = (tok * hkv + h) * dim;
   const int64_t cbase = (page * hkv + h) * code_block + (int64_t)(t >> 4) * 8 * dim;
   const int64_t sbase = (page * hkv + h) * scale_block + (int64_t)(t >> 4) * dim;
-  put_mx16_block(k + row, v + row, b, nb, dim, t16, kc, vc, ksc, vsc, cbase, sbase);
+  put_mx16_block(k + row, v + row, b, nb, t16, kc, vc, ksc, vsc, cbase, sbase);
 }
 
 // ----------------------------------------------------------------- NVFP4 --

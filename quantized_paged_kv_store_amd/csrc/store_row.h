@@ -83,23 +83,69 @@ __device__ __forceinline__ uint4 quant_fp8_16(const uint4 lo, const uint4 hi, co
   return make_uint4(out[0], out[1], out[2], out[3]);
 }
 
-// Chunk c (elements 16c..16c+15) of one (token, kv head) row pair. `base`
-// addresses the row's 16-token tile inside its (page, kv head) block.
-template <int FMT>
-__device__ __forceinline__ void put_fp8_chunk(const uint16_t* krow, const uint16_t* vrow, int c, int t16,
-                                              const Divisor& ks, const Divisor& vs, uint8_t* kc, uint8_t* vc,
-                                              int64_t base) {
+// The BF16 inputs of chunk c (elements 16c..16c+15) of one (token, kv head)
+// K row and V row, as one lane holds them.
+struct RowChunk {
+  uint4 k0, k1, v0, v1;
+};
+
+__device__ __forceinline__ RowChunk load_row_chunk(const uint16_t* krow, const uint16_t* vrow, int c) {
   const uint4* kp = reinterpret_cast<const uint4*>(krow + 16 * c);
   const uint4* vp = reinterpret_cast<const uint4*>(vrow + 16 * c);
-  const uint4 kq = quant_fp8_16<FMT>(kp[0], kp[1], ks);
-  const uint4 vq = quant_fp8_16<FMT>(vp[0], vp[1], vs);
+  return RowChunk{kp[0], kp[1], vp[0], vp[1]};
+}
+
+// Chunk c (elements 16c..16c+15) of one (token, kv head) row pair, from its
+// loaded inputs. `base` addresses the row's 16-token tile inside its
+// (page, kv head) block.
+template <int FMT>
+__device__ __forceinline__ void put_fp8_chunk(const RowChunk& r, int c, int t16, const Divisor& ks,
+                                              const Divisor& vs, uint8_t* kc, uint8_t* vc, int64_t base) {
+  const uint4 kq = quant_fp8_16<FMT>(r.k0, r.k1, ks);
+  const uint4 vq = quant_fp8_16<FMT>(r.v0, r.v1, vs);
   // K: the 16 elements of chunk c are 16 contiguous bytes
   *reinterpret_cast<uint4*>(kc + base + 256 * c + 16 * t16) = kq;
   // V: element d = 16c + r at 1024*(d/64) + 16*(16*(t16/4) + r) + 4*(c%4) + t16%4
   uint8_t* vb = vc + base + 1024 * (c >> 2) + 16 * (16 * (t16 >> 2)) + 4 * (c & 3) + (t16 & 3);
   const uint32_t vw[4] = {vq.x, vq.y, vq.z, vq.w};
 #pragma unroll
-  for (int r = 0; r < 16; ++r) vb[16 * r] = (uint8_t)(vw[r >> 2] >> (8 * (r & 3)));
+  for (int e = 0; e < 16; ++e) vb[16 * e] = (uint8_t)(vw[e >> 2] >> (8 * (e & 3)));
+}
+
+template <int FMT>
+__device__ __forceinline__ void put_fp8_chunk(const uint16_t* krow, const uint16_t* vrow, int c, int t16,
+                                              const Divisor& ks, const Divisor& vs, uint8_t* kc, uint8_t* vc,
+                                              int64_t base) {
+  put_fp8_chunk<FMT>(load_row_chunk(krow, vrow, c), c, t16, ks, vs, kc, vc, base);
+}
+
+// N = 2 or 4 consecutive elements e0.. (inside one 16-element chunk) of one
+// (token, kv head) K row (is_v false) or V row, from their BF16 bits (element
+// e0 + i in halfword i of w), at the places put_fp8_chunk gives them. Lets a
+// whole wave share one token's store, 64 lanes over K and V, where
+// put_fp8_chunk takes a chunk of both per lane.
+template <int FMT, int N>
+__device__ __forceinline__ void put_fp8_elems(const uint2 w, bool is_v, int e0, int t16, const Divisor& s,
+                                              uint8_t* codes, int64_t base) {
+  static_assert(N == 2 || N == 4, "two or four elements per lane");
+  const float x0 = quotient(bf16_bits_to_f32(w.x & 0xffffu), s), x1 = quotient(bf16_bits_to_f32(w.x >> 16), s);
+  const float x2 = N == 4 ? quotient(bf16_bits_to_f32(w.y & 0xffffu), s) : 0.0f;
+  const float x3 = N == 4 ? quotient(bf16_bits_to_f32(w.y >> 16), s) : 0.0f;
+  const uint32_t q = encode_fp8x4<FMT>(x0, x1, x2, x3);
+  if (!is_v) {
+    // K: the chunk's 16 codes are 16 contiguous bytes
+    uint8_t* kb = codes + base + 256 * (e0 >> 4) + 16 * t16 + (e0 & 15);
+    if constexpr (N == 4)
+      *reinterpret_cast<uint32_t*>(kb) = q;
+    else
+      *reinterpret_cast<uint16_t*>(kb) = (uint16_t)q;
+  } else {
+    // V: element d at 1024*(d/64) + 16*(16*(t16/4) + d%16) + 4*((d/16)%4) + t16%4
+    uint8_t* vb = codes + base + 1024 * (e0 >> 6) + 16 * (16 * (t16 >> 2) + (e0 & 15)) + 4 * ((e0 >> 4) & 3) +
+                  (t16 & 3);
+#pragma unroll
+    for (int i = 0; i < N; ++i) vb[16 * i] = (uint8_t)(q >> (8 * i));
+  }
 }
 
 // Store of four tokens that fill one 4-token group of a tile (t16 = 4g..4g+3),
@@ -154,24 +200,8 @@ __device__ __forceinline__ uint32_t amax16_bits(const uint4 lo, const uint4 hi) 
   return m;
 }
 
-// Chunk c of one (token, kv head) row pair, called by the `chunks` = D/16
-// consecutive lanes of a row together (lane c holds chunk c; the lanes form
-// an aligned group of the wave, all active). ks = the head's D channel
-// scales. Returns the row's V scale (every lane gets it).
-template <int FMT>
-__device__ __forceinline__ float put_fp8_chunk_kivi(const uint16_t* krow, const uint16_t* vrow, int c, int chunks,
-                                                    int t16, const float* ks, uint8_t* kc, uint8_t* vc,
-                                                    int64_t base) {
-  constexpr float MX = (FMT == KVQ_FP8_E4M3) ? 448.0f : 57344.0f;
-  const uint4* kp = reinterpret_cast<const uint4*>(krow + 16 * c);
-  const uint4* vp = reinterpret_cast<const uint4*>(vrow + 16 * c);
-  const uint4 v0 = vp[0], v1 = vp[1];
-  uint32_t m = amax16_bits(v0, v1);
-  for (int off = 1; off < chunks; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-  const float amax = bf16_bits_to_f32(m);
-  const float vs = amax == 0.f ? 1.0f : amax / MX;  // IEEE binary32 division
-  const Divisor vd = make_divisor(vs);
-  float kss[16];
+// The 16 channel scales of chunk c (ks = the head's D channel scales).
+__device__ __forceinline__ void load_chan_scales(const float* ks, int c, float (&kss)[16]) {
   const float4* kq4 = reinterpret_cast<const float4*>(ks + 16 * c);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -181,14 +211,38 @@ __device__ __forceinline__ float put_fp8_chunk_kivi(const uint16_t* krow, const 
     kss[4 * i + 2] = q.z;
     kss[4 * i + 3] = q.w;
   }
-  const uint4 kq = quant_fp8_16_vec<FMT>(kp[0], kp[1], kss);
-  const uint4 vq = quant_fp8_16<FMT>(v0, v1, vd);
+}
+
+// Chunk c of one (token, kv head) row pair, from its loaded inputs and channel
+// scales, called by the `chunks` = D/16 consecutive lanes of a row together
+// (lane c holds chunk c; the lanes form an aligned group of the wave, all
+// active). Returns the row's V scale (every lane gets it).
+template <int FMT>
+__device__ __forceinline__ float put_fp8_chunk_kivi(const RowChunk& r, const float (&kss)[16], int c, int chunks,
+                                                    int t16, uint8_t* kc, uint8_t* vc, int64_t base) {
+  constexpr float MX = (FMT == KVQ_FP8_E4M3) ? 448.0f : 57344.0f;
+  uint32_t m = amax16_bits(r.v0, r.v1);
+  for (int off = 1; off < chunks; off <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+  const float amax = bf16_bits_to_f32(m);
+  const float vs = amax == 0.f ? 1.0f : amax / MX;  // IEEE binary32 division
+  const Divisor vd = make_divisor(vs);
+  const uint4 kq = quant_fp8_16_vec<FMT>(r.k0, r.k1, kss);
+  const uint4 vq = quant_fp8_16<FMT>(r.v0, r.v1, vd);
   *reinterpret_cast<uint4*>(kc + base + 256 * c + 16 * t16) = kq;
   uint8_t* vb = vc + base + 1024 * (c >> 2) + 16 * (16 * (t16 >> 2)) + 4 * (c & 3) + (t16 & 3);
   const uint32_t vw[4] = {vq.x, vq.y, vq.z, vq.w};
 #pragma unroll
-  for (int r = 0; r < 16; ++r) vb[16 * r] = (uint8_t)(vw[r >> 2] >> (8 * (r & 3)));
+  for (int e = 0; e < 16; ++e) vb[16 * e] = (uint8_t)(vw[e >> 2] >> (8 * (e & 3)));
   return vs;
+}
+
+template <int FMT>
+__device__ __forceinline__ float put_fp8_chunk_kivi(const uint16_t* krow, const uint16_t* vrow, int c, int chunks,
+                                                    int t16, const float* ks, uint8_t* kc, uint8_t* vc,
+                                                    int64_t base) {
+  float kss[16];
+  load_chan_scales(ks, c, kss);
+  return put_fp8_chunk_kivi<FMT>(load_row_chunk(krow, vrow, c), kss, c, chunks, t16, kc, vc, base);
 }
 
 // ------------------------------------------------------------- FP4 (E2M1) --
@@ -239,17 +293,15 @@ __device__ __forceinline__ void quant_mx16(const uint4 lo, const uint4 hi, uint3
   sc = (uint8_t)(e + 127);
 }
 
-// Block b (elements 16b..16b+15) of one (token, kv head) row pair; cbase /
-// sbase address the row's 16-token tile of codes / scales.
-__device__ __forceinline__ void put_mx16_block(const uint16_t* krow, const uint16_t* vrow, int b, int nb, int dim,
-                                               int t16, uint8_t* kc, uint8_t* vc, uint8_t* ksc, uint8_t* vsc,
-                                               int64_t cbase, int64_t sbase) {
-  const uint4* kp = reinterpret_cast<const uint4*>(krow + 16 * b);
-  const uint4* vp = reinterpret_cast<const uint4*>(vrow + 16 * b);
+// Block b (elements 16b..16b+15) of one (token, kv head) row pair, from its
+// loaded inputs; cbase / sbase address the row's 16-token tile of codes /
+// scales.
+__device__ __forceinline__ void put_mx16_block(const RowChunk& r, int b, int nb, int t16, uint8_t* kc, uint8_t* vc,
+                                               uint8_t* ksc, uint8_t* vsc, int64_t cbase, int64_t sbase) {
   uint32_t k0, k1, v0, v1;
   uint8_t kse, vse;
-  quant_mx16(kp[0], kp[1], k0, k1, kse);
-  quant_mx16(vp[0], vp[1], v0, v1, vse);
+  quant_mx16(r.k0, r.k1, k0, k1, kse);
+  quant_mx16(r.v0, r.v1, v0, v1, vse);
   const int d0 = 16 * b;
   // K codes: byte 256*(d/32) + 16*t16 + (d%32)/2 -> 8 contiguous bytes
   *reinterpret_cast<uint2*>(kc + cbase + 256 * (d0 >> 5) + 16 * t16 + ((d0 & 31) >> 1)) = make_uint2(k0, k1);
@@ -261,7 +313,12 @@ __device__ __forceinline__ void put_mx16_block(const uint16_t* krow, const uint1
   // scales
   ksc[sbase + 32 * (b >> 1) + 2 * t16 + (b & 1)] = kse;
   vsc[sbase + 4 * (nb * (t16 >> 2) + b) + (t16 & 3)] = vse;
-  (void)dim;
+}
+
+__device__ __forceinline__ void put_mx16_block(const uint16_t* krow, const uint16_t* vrow, int b, int nb, int t16,
+                                               uint8_t* kc, uint8_t* vc, uint8_t* ksc, uint8_t* vsc, int64_t cbase,
+                                               int64_t sbase) {
+  put_mx16_block(load_row_chunk(krow, vrow, b), b, nb, t16, kc, vc, ksc, vsc, cbase, sbase);
 }
 
 // Block b of one MLA latent row (576 elements, 36 blocks); cb / sb address the
