@@ -373,10 +373,10 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
   // page id and rows are loaded ahead of the page-id staging, so the two
   // latencies overlap and the appending workgroup starts its tile loads
   // about when the others do.
-  // FP8 with tensor or head scales: wave 0's 64 lanes share the token, D / 32
-  // elements of K (lanes 0-31) or V (lanes 32-63) each; KIVI and FP4 blocks
-  // need a whole 16-element chunk per lane (lanes 0 .. D/16 - 1).
-  constexpr bool kElems = FMT != KVQ_FP4_MX16 && !KIVI;
+  // FP8: wave 0's 64 lanes share the token, D / 32 elements of K (lanes
+  // 0-31) or V (lanes 32-63) each; FP4 blocks need a whole 16-element chunk
+  // per lane (lanes 0 .. D/16 - 1).
+  constexpr bool kElems = FMT != KVQ_FP4_MX16;
   constexpr int kEpl = D / 32;
   const int pos = L - 1;
   const bool app = a.new_k != nullptr && pos / kTile < t_end && pos / kTile >= t_begin &&
@@ -384,7 +384,7 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
   int app_page = -1;
   RowChunk nr;
   uint2 ne;
-  float nks[KIVI ? 16 : 1];
+  float4 nks;  // KIVI: the K channel scales of this lane's elements
   if (app) {
     app_page = pt[pos / a.page_size];
     const int64_t row = ((int64_t)b * a.hkv + kvh) * D;
@@ -394,9 +394,15 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
         ne = *reinterpret_cast<const uint2*>(src);
       else
         ne = make_uint2(*reinterpret_cast<const uint32_t*>(src), 0u);
+      if constexpr (KIVI) {
+        const float* ks = a.k_scale + (int64_t)kvh * D + kEpl * (tid & 31);
+        if constexpr (kEpl == 4)
+          nks = *reinterpret_cast<const float4*>(ks);
+        else
+          nks = make_float4(ks[0], ks[1], 1.0f, 1.0f);
+      }
     } else {
       nr = load_row_chunk(a.new_k + row, a.new_v + row, tid);
-      if constexpr (KIVI) load_chan_scales(a.k_scale + (int64_t)kvh * D, tid, nks);
     }
   }
   // page ids of this split, staged once in LDS
@@ -419,9 +425,26 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
       put_mx16_block(nr, tid, D / 16, t & 15, kc, vc, const_cast<uint8_t*>(a.k_scales),
                      const_cast<uint8_t*>(a.v_scales), cbase, sbase);
     } else if constexpr (KIVI) {
+      // K: x / its channel scale; V: one scale for the row, fl32(amax / max)
+      // (1.0 for an all-zero row), the maximum taken over lanes 32-63
+      constexpr float MX = (FMT == KVQ_FP8_E4M3) ? 448.0f : 57344.0f;
       const int64_t base = (int64_t)page * page_code + head_code + (int64_t)(t >> 4) * tile_code_bytes;
-      const float vs = put_fp8_chunk_kivi<FMT>(nr, nks, tid, D / 16, t & 15, kc, vc, base);
-      if (tid == 0)
+      const bool is_v = tid >= 32;
+      float x[4];
+      unpack_elems<kEpl>(ne, x);
+      float m = fmaxf(fmaxf(__builtin_fabsf(x[0]), __builtin_fabsf(x[1])),
+                      fmaxf(__builtin_fabsf(x[2]), __builtin_fabsf(x[3])));
+      for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, shfl_xor_f32(m, off));  // within each half
+      const float vs = m == 0.f ? 1.0f : m / MX;  // IEEE binary32 division
+      uint32_t q;
+      if (is_v) {
+        const Divisor vd = make_divisor(vs);
+        q = encode_fp8x4<FMT>(quotient(x[0], vd), quotient(x[1], vd), quotient(x[2], vd), quotient(x[3], vd));
+      } else {
+        q = encode_fp8x4<FMT>(x[0] / nks.x, x[1] / nks.y, x[2] / nks.z, x[3] / nks.w);
+      }
+      place_fp8_elems<kEpl>(q, is_v, kEpl * (tid & 31), t & 15, is_v ? vc : kc, base);
+      if (tid == 32)
         reinterpret_cast<float*>(const_cast<uint8_t*>(a.v_scales) + (int64_t)page * page_scale + head_scale)[t] = vs;
     } else {
       const int64_t base = (int64_t)page * page_code + head_code + (int64_t)(t >> 4) * tile_code_bytes;

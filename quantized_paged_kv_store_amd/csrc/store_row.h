@@ -119,19 +119,16 @@ __device__ __forceinline__ void put_fp8_chunk(const uint16_t* krow, const uint16
   put_fp8_chunk<FMT>(load_row_chunk(krow, vrow, c), c, t16, ks, vs, kc, vc, base);
 }
 
-// N = 2 or 4 consecutive elements e0.. (inside one 16-element chunk) of one
-// (token, kv head) K row (is_v false) or V row, from their BF16 bits (element
-// e0 + i in halfword i of w), at the places put_fp8_chunk gives them. Lets a
-// whole wave share one token's store, 64 lanes over K and V, where
-// put_fp8_chunk takes a chunk of both per lane.
-template <int FMT, int N>
-__device__ __forceinline__ void put_fp8_elems(const uint2 w, bool is_v, int e0, int t16, const Divisor& s,
-                                              uint8_t* codes, int64_t base) {
+// Element-wise form of put_fp8_chunk: N = 2 or 4 consecutive elements e0..
+// (inside one 16-element chunk) of one (token, kv head) K row (is_v false) or
+// V row, so that a whole wave shares one token's store, 64 lanes over K and V,
+// where put_fp8_chunk takes a chunk of both rows per lane.
+// place_fp8_elems writes the N codes held in q's low bytes at the places
+// put_fp8_chunk gives them.
+template <int N>
+__device__ __forceinline__ void place_fp8_elems(const uint32_t q, bool is_v, int e0, int t16, uint8_t* codes,
+                                                int64_t base) {
   static_assert(N == 2 || N == 4, "two or four elements per lane");
-  const float x0 = quotient(bf16_bits_to_f32(w.x & 0xffffu), s), x1 = quotient(bf16_bits_to_f32(w.x >> 16), s);
-  const float x2 = N == 4 ? quotient(bf16_bits_to_f32(w.y & 0xffffu), s) : 0.0f;
-  const float x3 = N == 4 ? quotient(bf16_bits_to_f32(w.y >> 16), s) : 0.0f;
-  const uint32_t q = encode_fp8x4<FMT>(x0, x1, x2, x3);
   if (!is_v) {
     // K: the chunk's 16 codes are 16 contiguous bytes
     uint8_t* kb = codes + base + 256 * (e0 >> 4) + 16 * t16 + (e0 & 15);
@@ -146,6 +143,26 @@ __device__ __forceinline__ void put_fp8_elems(const uint2 w, bool is_v, int e0, 
 #pragma unroll
     for (int i = 0; i < N; ++i) vb[16 * i] = (uint8_t)(q >> (8 * i));
   }
+}
+
+// The N elements' values from their BF16 bits (element e0 + i in halfword i
+// of w), as floats (zero past N).
+template <int N>
+__device__ __forceinline__ void unpack_elems(const uint2 w, float (&x)[4]) {
+  x[0] = bf16_bits_to_f32(w.x & 0xffffu);
+  x[1] = bf16_bits_to_f32(w.x >> 16);
+  x[2] = N == 4 ? bf16_bits_to_f32(w.y & 0xffffu) : 0.0f;
+  x[3] = N == 4 ? bf16_bits_to_f32(w.y >> 16) : 0.0f;
+}
+
+// Codes RNE_sat(x / s) of the N elements, placed.
+template <int FMT, int N>
+__device__ __forceinline__ void put_fp8_elems(const uint2 w, bool is_v, int e0, int t16, const Divisor& s,
+                                              uint8_t* codes, int64_t base) {
+  float x[4];
+  unpack_elems<N>(w, x);
+  place_fp8_elems<N>(encode_fp8x4<FMT>(quotient(x[0], s), quotient(x[1], s), quotient(x[2], s), quotient(x[3], s)),
+                     is_v, e0, t16, codes, base);
 }
 
 // Store of four tokens that fill one 4-token group of a tile (t16 = 4g..4g+3),
