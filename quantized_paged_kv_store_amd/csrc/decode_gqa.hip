@@ -285,9 +285,69 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, hc = lane & 15;
-  const int L = min(max(a.seq_lens[b], 0), a.max_len);  // device data is clamped, never trusted
-  const int ntiles = (L + kTile - 1) / kTile;
   const int t_begin = split * a.tiles_per_split;
+  const int tpp = a.page_size / kTile;
+  const int64_t tile_code_bytes = (FMT == KVQ_FP4_MX16) ? 8 * D : 16 * D;
+  const int64_t tile_scale_bytes = (FMT == KVQ_FP4_MX16) ? D : (KIVI ? 4 * kTile : 0);
+  const int64_t head_code = (int64_t)kvh * a.code_block_bytes;
+  const int64_t head_scale = (int64_t)kvh * a.scale_block_bytes;
+  const int64_t page_code = (int64_t)a.hkv * a.code_block_bytes;
+  const int64_t page_scale = (int64_t)a.hkv * a.scale_block_bytes;
+  const int32_t* pt = a.page_table + (int64_t)b * a.page_table_stride;
+
+  // Tile pairs in flight per wave: two for FP8 at D = 128 (8 KB per wave in
+  // flight), four for the smaller tiles of FP4-MX16 and FP8 at D = 64, which
+  // otherwise leave too few bytes in flight to cover HBM latency. Loads are
+  // issued unconditionally (a missing or out-of-pool tile reads an in-pool
+  // stand-in and is masked afterwards), so the wait before each compute
+  // covers exactly the loads issued earlier.
+  constexpr int kDepth = (FMT == KVQ_FP4_MX16 || D == 64) ? 4 : 2;
+  struct Pair {
+    Tile<FMT, D> t[2];
+    int ok;  // bit s: tile s holds real tokens
+    int tA;
+  };
+  Pair R[kDepth];
+  auto load_pair_tile = [&](Pair& P, int s2, int64_t pg, int64_t sub) {
+    load_tile<FMT, D, KIVI>(P.t[s2], a.k_codes + pg * page_code + head_code + sub * tile_code_bytes,
+                            a.v_codes + pg * page_code + head_code + sub * tile_code_bytes,
+                            a.k_scales + pg * page_scale + head_scale + sub * tile_scale_bytes,
+                            a.v_scales + pg * page_scale + head_scale + sub * tile_scale_bytes, lane);
+  };
+  // Each wave's first tile pair (pair `wave` of the split) is issued before
+  // anything else: its page ids depend on the split alone, not on the
+  // sequence length, so the loads start one memory round trip earlier.
+  // Tiles past the sequence end are masked once the length is known.
+  // The uniform values the prologue needs are read first, with the first
+  // pair's page ids, as scalar loads that return together.
+  const int seq_len = a.seq_lens[b];
+  const int si = a.scale_mode == KVQ_SCALE_HEAD ? kvh : 0;  // per-tensor or per-KV-head FP8 scales
+  const float kscale = (!KIVI && a.k_scale) ? a.k_scale[si] : 1.0f;
+  const float vscale = (!KIVI && a.v_scale) ? a.v_scale[si] : 1.0f;
+  int first_pg[2];
+  {
+    const int tA = t_begin + 2 * __builtin_amdgcn_readfirstlane(wave);
+    // the last tile a page-table row covers (rows hold ceil(max_len / P) ids)
+    const int t_last = max((a.max_len + kTile - 1) / kTile, 1) - 1;
+    R[0].tA = tA;
+    int tile[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      tile[s2] = min(tA + s2, t_last);
+      first_pg[s2] = pt[tile[s2] / tpp];
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int64_t pg = (unsigned)first_pg[s2] < (unsigned)a.num_pages ? first_pg[s2] : 0;
+      load_pair_tile(R[0], s2, pg, tile[s2] - (tile[s2] / tpp) * tpp);
+    }
+    // keeps the compiler from sinking these loads below the length check
+    // (no wait: nothing reads them here)
+    __asm__ volatile("" ::: "memory");
+  }
+
+  const int L = min(max(seq_len, 0), a.max_len);  // device data is clamped, never trusted
+  const int ntiles = (L + kTile - 1) / kTile;
   const int t_end = min(t_begin + a.tiles_per_split, ntiles);
   if (t_begin >= t_end) {
     // an empty sequence has no split to merge: its first split writes 0 / -inf
@@ -302,18 +362,12 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
   }
 
   const int G = a.group;
-  const int tpp = a.page_size / kTile;
-  const int64_t tile_code_bytes = (FMT == KVQ_FP4_MX16) ? 8 * D : 16 * D;
-  const int64_t tile_scale_bytes = (FMT == KVQ_FP4_MX16) ? D : (KIVI ? 4 * kTile : 0);
-  const int64_t head_code = (int64_t)kvh * a.code_block_bytes;
-  const int64_t head_scale = (int64_t)kvh * a.scale_block_bytes;
-  const int64_t page_code = (int64_t)a.hkv * a.code_block_bytes;
-  const int64_t page_scale = (int64_t)a.hkv * a.scale_block_bytes;
-  const int32_t* pt = a.page_table + (int64_t)b * a.page_table_stride;
+  // validity of the first pair's tiles, now that the length is known
+  R[0].ok = 0;
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+    R[0].ok |= (int)(R[0].tA + s2 < t_end && (unsigned)first_pg[s2] < (unsigned)a.num_pages) << s2;
 
-  const int si = a.scale_mode == KVQ_SCALE_HEAD ? kvh : 0;  // per-tensor or per-KV-head FP8 scales
-  const float kscale = (!KIVI && a.k_scale) ? a.k_scale[si] : 1.0f;
-  const float vscale = (!KIVI && a.v_scale) ? a.v_scale[si] : 1.0f;
   float s_log2 = a.sm_scale_log2 * kscale;
 
   // Q^T operand fragments for head hc (zero beyond the group); KIVI: Q * ks
@@ -379,8 +433,10 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
   constexpr bool kElems = FMT != KVQ_FP4_MX16;
   constexpr int kEpl = D / 32;
   const int pos = L - 1;
-  const bool app = a.new_k != nullptr && pos / kTile < t_end && pos / kTile >= t_begin &&
-                   tid < (kElems ? 64 : D / 16);
+  const bool app_split = a.new_k != nullptr && pos / kTile < t_end && pos / kTile >= t_begin;
+  const bool app = app_split && tid < (kElems ? 64 : D / 16);
+  // the wave whose first pair (issued at the start) holds the appended tile
+  const bool app_first = app_split && (pos / kTile - R[0].tA) >> 1 == 0;
   int app_page = -1;
   RowChunk nr;
   uint2 ne;
@@ -455,14 +511,6 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
   }
   __syncthreads();
 
-  // One tile pair in flight: loads are issued unconditionally (a missing or
-  // out-of-pool tile reads an in-pool stand-in and is masked afterwards), so
-  // the wait before each compute covers exactly the loads issued earlier.
-  struct Pair {
-    Tile<FMT, D> t[2];
-    int ok;  // bit s: tile s holds real tokens
-    int tA;
-  };
   auto issue = [&](int pr, Pair& P) {
     const int tA = t_begin + 2 * pr;
     P.tA = tA;
@@ -473,12 +521,7 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
       const int page = __builtin_amdgcn_readfirstlane(sm_pg[tile / tpp - fp]);
       const bool v = (tA + s2 < t_end) && (unsigned)page < (unsigned)a.num_pages;
       ok |= (int)v << s2;
-      const int64_t pg = v ? page : 0;
-      const int64_t sub = tile - (tile / tpp) * tpp;
-      load_tile<FMT, D, KIVI>(P.t[s2], a.k_codes + pg * page_code + head_code + sub * tile_code_bytes,
-                        a.v_codes + pg * page_code + head_code + sub * tile_code_bytes,
-                        a.k_scales + pg * page_scale + head_scale + sub * tile_scale_bytes,
-                        a.v_scales + pg * page_scale + head_scale + sub * tile_scale_bytes, lane);
+      load_pair_tile(P, s2, v ? page : 0, tile - (tile / tpp) * tpp);
     }
     P.ok = ok;
   };
@@ -535,20 +578,18 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
     pv_pair<FMT, D, KIVI>(P.t[0], P.t[1], p, o);
   };
 
-  // Tile pairs in flight per wave: two for FP8 at D = 128 (8 KB per wave in
-  // flight), four for the smaller tiles of FP4-MX16 and FP8 at D = 64, which
-  // otherwise leave too few bytes in flight to cover HBM latency. Every slot
-  // of the unrolled body issues and computes unconditionally (so every wait
-  // count is static); the wave's pair count is rounded up to whole bodies.
-  // Pairs past the split are clamped in-pool stand-ins whose tokens are all
-  // masked: they add exactly nothing to the softmax state.
-  constexpr int kDepth = (FMT == KVQ_FP4_MX16 || D == 64) ? 4 : 2;
+  // Every slot of the unrolled body issues and computes unconditionally (so
+  // every wait count is static); the wave's pair count is rounded up to whole
+  // bodies. Pairs past the split are clamped in-pool stand-ins whose tokens
+  // are all masked: they add exactly nothing to the softmax state.
   int pr = __builtin_amdgcn_readfirstlane(wave);
   if (pr < npairs) {
     const int iters = ((npairs - pr + kWaves - 1) / kWaves + kDepth - 1) / kDepth;
-    Pair R[kDepth];
+    // R[0] holds pair pr, issued at the start (again here if it holds the
+    // appended token, whose stores the barrier above has ordered)
+    if (app_first) issue(pr, R[0]);
 #pragma unroll
-    for (int i = 0; i < kDepth - 1; ++i) issue(pr + i * kWaves, R[i]);
+    for (int i = 1; i < kDepth - 1; ++i) issue(pr + i * kWaves, R[i]);
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
       for (int slot = 0; slot < kDepth; ++slot) {
