@@ -465,7 +465,17 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
   __shared__ int sm_pg[kMaxSplitTiles];
   const int fp = t_begin / tpp;
   const int n_pg = (t_end - 1) / tpp - fp + 1;
-  for (int i = tid; i < n_pg; i += 256) sm_pg[i] = pt[fp + i];
+  {
+    // every thread's loads issued before any is waited on (a split has at
+    // most kMaxSplitTiles pages: up to four per thread)
+    int pg_in[kMaxSplitTiles / 256];
+#pragma unroll
+    for (int j = 0; j < kMaxSplitTiles / 256; ++j)
+      if (tid + 256 * j < n_pg) pg_in[j] = pt[fp + tid + 256 * j];
+#pragma unroll
+    for (int j = 0; j < kMaxSplitTiles / 256; ++j)
+      if (tid + 256 * j < n_pg) sm_pg[tid + 256 * j] = pg_in[j];
+  }
   // every load above has arrived: otherwise a path that skips the append
   // joins with the rows still in flight, and the compiler then waits after
   // the barrier for all memory operations, the append's stores included
