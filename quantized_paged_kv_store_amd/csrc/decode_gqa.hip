@@ -435,7 +435,8 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
   const int pos = L - 1;
   const bool app_split = a.new_k != nullptr && pos / kTile < t_end && pos / kTile >= t_begin;
   const bool app = app_split && tid < (kElems ? 64 : D / 16);
-  // the wave whose first pair (issued at the start) holds the appended tile
+  // this wave's first pair (issued at the start) holds the appended tile, so
+  // it is read again after the barrier
   const bool app_first = app_split && (pos / kTile - R[0].tA) >> 1 == 0;
   int app_page = -1;
   RowChunk nr;
