@@ -435,8 +435,7 @@ __global__ void __launch_bounds__(256, 2) decode_gqa_kernel(const GqaDecodeArgs 
   const int pos = L - 1;
   const bool app_split = a.new_k != nullptr && pos / kTile < t_end && pos / kTile >= t_begin;
   const bool app = app_split && tid < (kElems ? 64 : D / 16);
-  // this wave's first pair (issued at the start) holds the appended tile, so
-  // it is read again after the barrier
+  // the wave whose first pair (issued at the start) holds the appended tile
   const bool app_first = app_split && (pos / kTile - R[0].tA) >> 1 == 0;
   int app_page = -1;
   RowChunk nr;
