@@ -266,8 +266,8 @@ int kvq_decode_noalloc(const kvq_cache* cache, const void* q, int32_t batch, int
  * kvq_decode with the same arguments: the quantization is the store's and
  * the codes written are bit-identical ([P4] quantize_and_store, then decode
  * over the quantized cache). The context split that holds position L-1
- * quantizes and writes that token before it reads its tiles, which saves the
- * separate store launch of a decode step.
+ * quantizes and writes that token before it reads the tile that holds it,
+ * which saves the separate store launch of a decode step.
  *   k_new, v_new: [dev] BF16, GQA [batch][num_kv_heads][head_dim] each;
  *                 MLA: k_new = latent rows [batch][head_dim], v_new must be NULL.
  * All other arguments, the workspace and the errors are kvq_decode's; a NULL
