@@ -44,6 +44,21 @@ def test_append_gqa(dtype, D, G, P):
     _check(a, b, f"append {dtype} D{D} G{G} P{P}", [0, 1, 4, 9])
 
 
+@pytest.mark.parametrize("dtype,D,G,P,target", [("e4m3", 128, 4, 48, 100), ("mx16", 128, 8, 80, 90),
+                                                ("e5m2", 64, 2, 48, 140)])
+def test_append_gqa_pages_of_several_tiles(dtype, D, G, P, target):
+    """Pages of 3 and 5 tiles and splits that start inside a page: the
+    appended token's tile is found by division, and a wave whose first tile
+    pair (loaded before the length is known) holds it reads that pair again
+    after the append."""
+    w = I.Workload(f"append-{dtype}-{P}", dtype, "gqa", len(LENS), 2 * G, 2, D, D, P, max(LENS), 0, 1, "llama",
+                   seed=23)
+    a = Case(w, lens=LENS).run_gpu(split_target=target)
+    b = Case(w, lens=LENS, data=a.data).run_gpu(append=True, split_target=target)
+    torch.cuda.synchronize()
+    _check(a, b, f"append {dtype} D{D} G{G} P{P} target {target}", [0, 1, 4, 7, 9])
+
+
 @pytest.mark.parametrize("hq,P", [(128, 64), (64, 16), (16, 64)])
 def test_append_mla(hq, P):
     w = I.Workload(f"append-mla-{hq}", "nvfp4", "mla", len(LENS), hq, 1, 576, 512, P, max(LENS), 0, 1, "mla",

@@ -50,6 +50,21 @@ def test_ragged_lengths(dtype, D, G, P):
     assert np.all(got[0] == 0) and np.all(np.isneginf(c.lse.cpu().numpy()[0]))
 
 
+@pytest.mark.parametrize("dtype,D,G,P,target", [
+    ("e4m3", 128, 4, 48, 90), ("mx16", 128, 8, 80, 64), ("e5m2", 64, 2, 48, 0), ("e4m3", 128, 16, 80, 200),
+])
+def test_pages_of_several_tiles_with_unaligned_splits(dtype, D, G, P, target):
+    """Pages of 3 and 5 tiles (page sizes 48 and 80, not powers of two), with
+    split targets that start splits inside a page: the page and tile-in-page
+    of every load (the first pair's before the length is known, the rest
+    from the staged page ids) come from divisions by the tiles per page."""
+    hkv = 2
+    w = I.Workload(f"pages-{dtype}-{P}", dtype, "gqa", len(RAGGED), G * hkv, hkv, D, D, P, max(RAGGED), 0, 1,
+                   "llama", seed=17)
+    c = Case(w, lens=RAGGED).run_gpu(split_target=target)
+    _check(c, list(range(len(RAGGED))), f"{dtype} D{D} G{G} P{P} target {target}")
+
+
 class _TinyBlocksCase(Case):
     """K and V rows of every fifth token scaled by 2^-130 (input generation
     only; both sides see the same BF16 rows, many of them BF16 subnormals):
