@@ -255,7 +255,8 @@ def test_llama3_8b_decode_sampled():
     print(f"llama3_8b: max-abs {mab:.2e} rel-L2 {r:.2e}; quantization error vs BF16 attention rel-L2 {q_err:.3e}")
 
 
-@pytest.mark.parametrize("hq,P", [(128, 64), (64, 16), (128, 32), (16, 64), (96, 16), (40, 32), (1, 64)])
+@pytest.mark.parametrize("hq,P", [(128, 64), (64, 16), (128, 32), (16, 64), (96, 16), (40, 32), (1, 64), (128, 48),
+                                  (64, 96)])
 def test_mla_ragged_lengths(hq, P):
     lens = [0, 1, 17, 64, 100, 1000, 2500]
     w = I.Workload(f"mla-ragged-{hq}", "nvfp4", "mla", len(lens), hq, 1, 576, 512, P, max(lens), 0, 1, "mla", seed=9)
