@@ -139,7 +139,8 @@ def test_fp8_store_word_groups_and_partial_words():
     _assert_bytes_equal(cache, oc)
 
 
-@pytest.mark.parametrize("dtype,D,P", [("e4m3", 64, 16), ("e4m3", 128, 32), ("e5m2", 128, 16)])
+@pytest.mark.parametrize("dtype,D,P", [("e4m3", 64, 16), ("e4m3", 128, 32), ("e5m2", 128, 16), ("e4m3", 128, 48),
+                                       ("e5m2", 64, 80)])
 def test_fp8_store_random_with_scale(dtype, D, P):
     rng = np.random.default_rng(2)
     H, n_tok = 3, 200
@@ -175,7 +176,8 @@ def _mx_blocks(rng):
     return np.array(blocks)
 
 
-def test_mx16_store_bruteforce_blocks():
+@pytest.mark.parametrize("P", [16, 48])
+def test_mx16_store_bruteforce_blocks(P):
     rng = np.random.default_rng(3)
     blocks = _mx_blocks(rng)
     D, H = 128, 2
@@ -185,9 +187,9 @@ def test_mx16_store_bruteforce_blocks():
     x[: len(blocks)] = blocks
     k = x.reshape(n_tok, H, D)
     v = x[rng.permutation(len(x))].reshape(n_tok, H, D)
-    pages = -(-n_tok // 16) + 1
-    spec = CacheSpec("mx16", "gqa", H, D, D, 16, pages)
-    slots = rng.permutation(pages * 16)[:n_tok]
+    pages = -(-n_tok // P) + 1
+    spec = CacheSpec("mx16", "gqa", H, D, D, P, pages)
+    slots = rng.permutation(pages * P)[:n_tok]
     cache, oc = _store_both(spec, k, v, slots)
     _assert_bytes_equal(cache, oc)
 
