@@ -44,6 +44,8 @@ def _oracle(inp, s_k, s_v, sm, rows=None):
     (1, 16, [70, 129], [129, 5]),
     (1, 32, [40, 0], [300, 513]),      # G = 1: 256 chunk tokens per tile, so these span 2 and 3 tiles
     (2, 64, [64, 640], [200, 1]),
+    (4, 48, [100, 0, 257], [33, 16, 17]),   # workspace pages that are not a power of two in size
+    (16, 80, [300, 65], [64, 9]),
 ])
 def test_extend_matches_oracle(G, P, prefix, chunk):
     hkv, D = 2, 128
