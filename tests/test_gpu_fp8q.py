@@ -106,6 +106,7 @@ def _check(c, out, lse, qs_host, ids, what):
     ("e5m2", 64, 1, 64, True, "stale"),
     ("e4m3", 128, 4, 16, False, "stale"),
     ("e4m3", 128, 2, 16, False, "none"),
+    ("e4m3", 128, 4, 48, True, "cal"),
 ])
 def test_fp8q_decode_matches_oracle(dtype, D, G, P, per_head, how):
     c = Case(_workload(dtype, LENS, G=G, D=D, P=P, per_head=per_head), lens=LENS).run_gpu(decode=False)
@@ -202,7 +203,7 @@ def _mla_check(c, out, lse, qs_host, ids, what):
 
 
 @pytest.mark.parametrize("hq,P,how", [(128, 64, "cal"), (128, 16, "none"), (64, 32, "cal"), (40, 64, "stale"),
-                                      (16, 16, "cal"), (1, 64, "cal")])
+                                      (16, 16, "cal"), (1, 64, "cal"), (128, 48, "cal")])
 def test_mla_fp8q_matches_oracle(hq, P, how):
     lens = [0, 1, 17, 64, 100, 1000, 2500]
     c = Case(_mla_workload(lens, hq, P), lens=lens).run_gpu(decode=False)

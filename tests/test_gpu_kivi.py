@@ -45,7 +45,7 @@ LENS = [0, 1, 15, 16, 17, 300, 2048, 5000]
 
 
 @pytest.mark.parametrize("dtype,D,G,P", [("e4m3", 128, 4, 16), ("e5m2", 128, 8, 32), ("e4m3", 64, 3, 16),
-                                         ("e4m3", 128, 16, 64)])
+                                         ("e4m3", 128, 16, 64), ("e4m3", 128, 4, 48)])
 def test_kivi_store_bytes_and_decode(dtype, D, G, P):
     c = Case(_workload(dtype, LENS, G=G, hkv=2, D=D, P=P), lens=LENS).run_gpu()
     ks, vs = c.gpu_scales()
