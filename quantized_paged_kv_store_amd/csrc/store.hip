@@ -150,6 +150,23 @@ __global__ void __launch_bounds__(256) amax_chan_final_kernel(const unsigned* __
   out[i] = (amax == 0.f) ? 1.0f : amax / fmt_div;  // IEEE binary32 division
 }
 
+// Page and position of a cache slot (slot / page_size, slot % page_size):
+// a shift and a mask when the page size is a power of two (a kernel argument,
+// so the branch is uniform), else a 64-bit division. slot >= 0.
+__device__ __forceinline__ void slot_place(int64_t slot, int page_size, int64_t& page, int& t) {
+  if ((page_size & (page_size - 1)) == 0) {
+    page = slot >> __builtin_ctz(page_size);
+    t = (int)(slot & (page_size - 1));
+  } else {
+    page = slot / page_size;
+    t = (int)(slot - page * page_size);
+  }
+}
+
+// The store kernels launch one thread per (token, [kv head,] 16-element piece)
+// and the C ABI keeps such a launch below 2^32 threads, so the thread's split
+// into token, head and piece runs in 32-bit arithmetic.
+
 // one thread per (token, kv head, 16-element chunk); the D/16 chunks of a row
 // are consecutive lanes (the KIVI V row amax is reduced across them). A V
 // lane word holds one element of four consecutive tokens (t16 = 4g..4g+3):
@@ -164,16 +181,17 @@ __global__ void __launch_bounds__(256) store_fp8_kernel(
     const float* __restrict__ v_scale, int mode, uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
     int64_t block_bytes, uint8_t* __restrict__ vts, int64_t vts_block) {
   const int chunks = dim / 16;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)n_tok * hkv * chunks) return;
-  const int c = (int)(gid % chunks);
-  const int64_t th = gid / chunks;
-  const int h = (int)(th % hkv);
-  const int64_t tok = th / hkv;
+  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (uint32_t)n_tok * (uint32_t)hkv * (uint32_t)chunks) return;
+  const int c = (int)(gid % (uint32_t)chunks);
+  const uint32_t th = gid / (uint32_t)chunks;
+  const int h = (int)(th % (uint32_t)hkv);
+  const int64_t tok = th / (uint32_t)hkv;
   const int64_t slot = slots[tok];
   if (slot < 0 || slot >= capacity) return;
-  const int64_t page = slot / page_size;
-  const int t = (int)(slot % page_size);
+  int64_t page;
+  int t;
+  slot_place(slot, page_size, page, t);
   const int t16 = t & 15;
   const int64_t row = (tok * hkv + h) * dim;
   const int64_t base = (page * hkv + h) * block_bytes + (int64_t)(t >> 4) * 16 * dim;
@@ -209,16 +227,17 @@ __global__ void __launch_bounds__(256) store_mx16_kernel(
     uint8_t* __restrict__ vc, uint8_t* __restrict__ ksc, uint8_t* __restrict__ vsc, int64_t code_block,
     int64_t scale_block) {
   const int nb = dim / 16;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)n_tok * hkv * nb) return;
-  const int b = (int)(gid % nb);
-  const int64_t th = gid / nb;
-  const int h = (int)(th % hkv);
-  const int64_t tok = th / hkv;
+  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (uint32_t)n_tok * (uint32_t)hkv * (uint32_t)nb) return;
+  const int b = (int)(gid % (uint32_t)nb);
+  const uint32_t th = gid / (uint32_t)nb;
+  const int h = (int)(th % (uint32_t)hkv);
+  const int64_t tok = th / (uint32_t)hkv;
   const int64_t slot = slots[tok];
   if (slot < 0 || slot >= capacity) return;
-  const int64_t page = slot / page_size;
-  const int t = (int)(slot % page_size);
+  int64_t page;
+  int t;
+  slot_place(slot, page_size, page, t);
   const int t16 = t & 15;
   const int64_t row = (tok * hkv + h) * dim;
   const int64_t cbase = (page * hkv + h) * code_block + (int64_t)(t >> 4) * 8 * dim;
@@ -233,16 +252,17 @@ __global__ void __launch_bounds__(256) store_nvfp4_kernel(
     int page_size, int64_t capacity, const float* __restrict__ g_scale, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales) {
   const int nb = dim / 16;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)n_tok * nb) return;
-  const int b = (int)(gid % nb);
-  const int64_t tok = gid / nb;
+  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (uint32_t)n_tok * (uint32_t)nb) return;
+  const int b = (int)(gid % (uint32_t)nb);
+  const int64_t tok = gid / (uint32_t)nb;
   const int64_t slot = slots[tok];
   if (slot < 0 || slot >= capacity) return;
-  const int page = (int)(slot / page_size);
-  const int t = (int)(slot % page_size);
-  uint8_t* cb = codes + (int64_t)page * page_size * (dim / 2) + (int64_t)(t >> 4) * 16 * (dim / 2);
-  uint8_t* sb = scales + (int64_t)page * page_size * nb + (int64_t)(t >> 4) * 16 * nb;
+  int64_t page;
+  int t;
+  slot_place(slot, page_size, page, t);
+  uint8_t* cb = codes + page * page_size * (dim / 2) + (int64_t)(t >> 4) * 16 * (dim / 2);
+  uint8_t* sb = scales + page * page_size * nb + (int64_t)(t >> 4) * 16 * nb;
   put_nvfp4_block(k + tok * dim, b, t & 15, g_scale[0], cb, sb);
 }
 
