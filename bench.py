@@ -509,8 +509,10 @@ def copy_reference(nbytes=1 << 30, reps=10, quiet=False):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 1,000 for a decode step: a serving loop's steady state; 100 for "
+                         "--dequant-prev and --extend)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps first (default steps / 10)")
     ap.add_argument("--workload", default="llama3_8b")
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -532,6 +534,10 @@ def main():
                     help="FP8 GQA and NVFP4 MLA workloads: FP8-domain attention (query rounded to E4M3, QK on "
                          "FP8 MFMA; MLA keys as E4M3 codes of the latent / 8g)")
     args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 100 if (args.dequant_prev or args.extend) else 1000
+    if args.warmup is None:
+        args.warmup = max(args.steps // 10, 1)
     if args.copy_ref:
         copy_reference()
         return
