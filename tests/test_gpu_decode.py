@@ -65,6 +65,17 @@ def test_pages_of_several_tiles_with_unaligned_splits(dtype, D, G, P, target):
     _check(c, list(range(len(RAGGED))), f"{dtype} D{D} G{G} P{P} target {target}")
 
 
+@pytest.mark.parametrize("dtype,hkv,G", [("e4m3", 32, 1), ("mx16", 16, 2)])
+def test_many_kv_heads(dtype, hkv, G):
+    """Many KV heads per page (32 and 16: 32 of them make a 64 KB FP8 page of 16
+    tokens), including multi-head attention (G = 1)."""
+    lens = [0, 5, 300, 2049]
+    w = I.Workload(f"heads-{dtype}-{hkv}", dtype, "gqa", len(lens), G * hkv, hkv, 128, 128, 16, max(lens), 0, 1,
+                   "llama", seed=19)
+    c = Case(w, lens=lens).run_gpu()
+    _check(c, list(range(len(lens))), f"{dtype} Hkv{hkv} G{G}")
+
+
 class _TinyBlocksCase(Case):
     """K and V rows of every fifth token scaled by 2^-130 (input generation
     only; both sides see the same BF16 rows, many of them BF16 subnormals):
