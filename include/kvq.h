@@ -207,7 +207,10 @@ int kvq_store(const kvq_cache* cache, const void* k, const void* v,
               const int64_t* slot_mapping, int32_t num_tokens, const float* k_scale,
               const float* v_scale, void* stream);
 
-/* Bytes of device workspace kvq_decode needs for this batch shape. */
+/* Bytes of device workspace kvq_decode needs for this batch shape: 0 when
+ * one context split covers every sequence (no partials to merge), and 0 for
+ * arguments the decode itself rejects (a null handle, negative sizes, MLA
+ * with more than 128 query heads), which the decode call then reports. */
 size_t kvq_decode_workspace_bytes(const kvq_cache* cache, int32_t batch, int32_t num_q_heads,
                                   int32_t max_seq_len);
 
